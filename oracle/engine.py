@@ -1,0 +1,223 @@
+"""The whole tier, step by step, in the order the pages give (FreeToken PR
+#499, "Why this works for sparse attention" and "Design"):
+
+    write path:  ensure_write_pages -> store (pool + write-through mirror + slab)
+    decode path: select (indexer top-k) -> compact -> ensure -> fetch -> attention
+
+Rows of a call are grouped by request: rows of request b are
+``row_start[b] .. row_start[b+1]-1``.
+
+Content modes.  With ``materialize=True`` the mirror and the pool are real
+byte rows, written by the store and copied by the fetch.  With
+``materialize=False`` (the full-size workloads) only the slab and the
+per-page written-token counts are kept; the bytes of a page are rebuilt on
+demand by ``row_builder(page)`` -- the same ``write_tokens`` arithmetic
+applied to the page's tokens -- and a resident slot reads its page's mirror
+row, which is what the write-through mirror guarantees (PR #499 "Design":
+every GPU slot is drop-clean).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import attend
+from .layout import RowLayout
+from .lru import LRUState
+from .select import compact_request, select_row
+from .store import read_kv, slab_entry, write_tokens
+
+ERR_NOT_RESIDENT = 4      # store to a page that is not resident (pool not written)
+
+
+class CapacityError(ValueError):
+    pass
+
+
+class OracleTier:
+    def __init__(self, *, num_layers, num_q_heads, num_kv_heads, head_dim, page_size,
+                 fp8, num_logical_pages, num_slots, materialize=True, row_builder=None):
+        self.L, self.Hq, self.Hkv, self.d = num_layers, num_q_heads, num_kv_heads, head_dim
+        self.ps, self.N, self.S = page_size, int(num_logical_pages), int(num_slots)
+        self.lay = RowLayout(num_layers, num_kv_heads, page_size, head_dim, fp8)
+        self.materialize = materialize
+        self.row_builder = row_builder
+        self.mirror = {}                      # page -> uint8 row
+        self.pool = (np.zeros((self.S, self.lay.row_bytes), dtype=np.uint8)
+                     if materialize else None)
+        self.slab = np.zeros((self.L, self.N, self.Hkv, self.d), dtype=np.float32)
+        self._partial_sums = {}               # (layer, page) -> fp64 key sum of a partly written page
+        self.written = np.zeros(self.N, dtype=np.int64)   # tokens written per page (layer 0)
+        self.lru = LRUState(self.N, self.S)
+        self.drops = 0
+        self.bytes_fetched = 0
+        self.bytes_mirrored = 0
+        self.max_sel_pages = None
+        self.max_certificate = 0.0
+
+    # ------------------------------------------------------------ config --
+    def set_select_width(self, max_bs, block_topk, max_sel_pages=0):
+        """PR #525 commit summary: the whole batch selection must fit the
+        physical pool by construction."""
+        C = max_sel_pages if max_sel_pages > 0 else 2 * block_topk + 8
+        if max_bs * C > self.S:
+            raise CapacityError(f"max_bs*max_sel_pages={max_bs * C} > num_slots={self.S}")
+        self.max_sel_pages = C
+        return C
+
+    def reset_residency(self):
+        self.lru.reset()
+        self.drops = self.bytes_fetched = self.bytes_mirrored = 0
+
+    # ------------------------------------------------------------ rows ----
+    def mirror_row(self, page: int) -> np.ndarray:
+        if self.materialize:
+            if page not in self.mirror:
+                self.mirror[page] = np.zeros(self.lay.row_bytes, dtype=np.uint8)
+            return self.mirror[page]
+        return self.row_builder(page)
+
+    def pool_row(self, slot: int) -> np.ndarray:
+        if self.materialize:
+            return self.pool[slot]
+        page = int(self.lru.slot_to_page[slot])
+        return self.row_builder(page)
+
+    # ------------------------------------------------------------ write ---
+    def ensure_write_pages(self, runs, block_table, old_len):
+        """runs: list of (req, start, length).  Every page a run touches is made
+        resident; a page whose first position is >= the request's old length
+        has no content yet and is allocated without a fetch."""
+        needed, nofetch = [], []
+        for req, start, length in runs:
+            if length <= 0:
+                continue
+            for lp in range(start // self.ps, (start + length - 1) // self.ps + 1):
+                needed.append(int(block_table[req][lp]))
+                nofetch.append(lp * self.ps >= old_len[req])
+        out, misses = self.lru.ensure(np.array(needed, dtype=np.int64), np.array(nofetch, dtype=bool))
+        self.fetch(misses)
+        return out, misses
+
+    def store(self, layer, runs, k, v, block_table):
+        """k, v float32 [n_tok][Hkv][d], tokens of the runs concatenated in order.
+        The pages must be resident (ensure_write_pages first); a page that is
+        not is still written to the mirror and the slab, and flagged."""
+        off = 0
+        for req, start, length in runs:
+            pos = start
+            while pos < start + length:
+                lp = pos // self.ps
+                a = pos - lp * self.ps
+                n = min(self.ps - a, start + length - pos)
+                page = int(block_table[req][lp])
+                kk = k[off:off + n]
+                vv = v[off:off + n]
+                slot = int(self.lru.page_to_slot[page])
+                if slot < 0:
+                    self.lru.error_word |= ERR_NOT_RESIDENT
+                if self.materialize:
+                    write_tokens(self.mirror_row(page), self.lay, layer, a, kk, vv)
+                    if slot >= 0:
+                        write_tokens(self.pool[slot], self.lay, layer, a, kk, vv)
+                # slab: mean of all written keys of the page
+                key = (layer, page)
+                prev = self._partial_sums.pop(key, None) if a > 0 else None
+                s = kk.astype(np.float64).sum(axis=0) + (0.0 if prev is None else prev)
+                cnt = a + n
+                if cnt < self.ps:
+                    self._partial_sums[key] = s
+                self.slab[layer, page] = slab_entry_from_sum(s, cnt)
+                if layer == 0:
+                    self.written[page] = cnt
+                tok_bytes = self.lay.layer_bytes // self.ps
+                self.bytes_mirrored += (n + (self.ps - cnt if a == 0 else 0)) * tok_bytes
+                pos += n
+                off += n
+
+    # ------------------------------------------------------------ decode --
+    def select(self, layer, q, row_start, row_pos, block_table, n_pages, topk, bias=None):
+        """q float32 [rows][Hq][d] -> (sel_local int32 [rows][topk], needed int32 [B][C])."""
+        B = len(n_pages)
+        rows = q.shape[0]
+        sel = np.full((rows, topk), -1, dtype=np.int32)
+        for b in range(B):
+            for r in range(row_start[b], row_start[b + 1]):
+                pos = None if row_pos is None else int(row_pos[r])
+                sel[r], cert = select_row(q[r], self.slab[layer], block_table[b], int(n_pages[b]),
+                                          topk, self.Hkv, bias, pos, self.ps)
+                self.max_certificate = max(self.max_certificate, cert)
+        C = self.max_sel_pages
+        needed = np.full((B, C), -1, dtype=np.int32)
+        for b in range(B):
+            needed[b], drops = compact_request(sel[row_start[b]:row_start[b + 1]], block_table[b], C)
+            self.drops += drops
+        return sel, needed
+
+    def ensure(self, needed, no_fetch=None):
+        return self.lru.ensure(np.asarray(needed).reshape(-1), no_fetch)
+
+    def fetch(self, misses):
+        """Copy the mirror row of each missed page into its slot, all layers and
+        all banks at once."""
+        for slot, page in np.asarray(misses).reshape(-1, 2):
+            if self.materialize:
+                self.pool[slot][:] = self.mirror_row(int(page))
+            self.bytes_fetched += self.lay.row_bytes
+
+    def gather_kv(self, layer, b, sel_row, block_table, ctx_len, row_pos=None):
+        """Dequantised K, V [Hkv][T][d] of the selected resident pages' visible tokens."""
+        ks, vs = [], []
+        limit = int(ctx_len[b]) if row_pos is None else min(int(ctx_len[b]), int(row_pos) + 1)
+        for i in sel_row:
+            if i < 0:
+                continue
+            page = int(block_table[b][i])
+            slot = int(self.lru.page_to_slot[page])
+            if slot < 0:
+                continue
+            n = min(self.ps, limit - int(i) * self.ps)
+            if n <= 0:
+                continue
+            k, v = read_kv(self.pool_row(slot), self.lay, layer)
+            ks.append(k[:, :n])
+            vs.append(v[:, :n])
+        if not ks:
+            z = np.zeros((self.Hkv, 0, self.d))
+            return z, z
+        return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
+
+    def attention_row(self, layer, q_row, b, sel_row, block_table, ctx_len, row_pos=None):
+        k, v = self.gather_kv(layer, b, sel_row, block_table, ctx_len, row_pos)
+        return attend(q_row.astype(np.float64), k, v)
+
+    def attention(self, layer, q, row_start, row_pos, ctx_len, sel, block_table):
+        out = np.zeros(q.shape, dtype=np.float64)
+        for b in range(len(row_start) - 1):
+            for r in range(row_start[b], row_start[b + 1]):
+                pos = None if row_pos is None else row_pos[r]
+                out[r] = self.attention_row(layer, q[r], b, sel[r], block_table, ctx_len, pos)
+        return out
+
+    def decode_layer(self, layer, q, row_start, block_table, n_pages, ctx_len, topk,
+                     bias=None, row_pos=None, with_attention=True):
+        sel, needed = self.select(layer, q, row_start, row_pos, block_table, n_pages, topk, bias)
+        out_slots, misses = self.ensure(needed)
+        self.fetch(misses)
+        out = (self.attention(layer, q, row_start, row_pos, ctx_len, sel, block_table)
+               if with_attention else None)
+        return dict(sel=sel, needed=needed, out_slots=out_slots, misses=misses, out=out)
+
+    def counters(self):
+        c = dict(self.lru.counters)
+        c.update(drops=self.drops, bytes_fetched=self.bytes_fetched,
+                 bytes_mirrored=self.bytes_mirrored, error_word=self.lru.error_word)
+        return c
+
+
+def slab_entry_from_sum(s: np.ndarray, n: int) -> np.ndarray:
+    """bf16(fp32(sum) / n) -- the mean of n written keys given their exact sum."""
+    from .codecs import bf16_round
+    return bf16_round(s.astype(np.float32) / np.float32(n))
+
+
+__all__ = ["OracleTier", "CapacityError", "slab_entry", "slab_entry_from_sum"]

@@ -1,0 +1,141 @@
+"""End-to-end pins of the oracle chain on small workloads.
+
+* budget >= context: the chain's sparse output equals dense attention over
+  every token of the context, computed straight from the generated keys and
+  values quantised by the store (FreeToken PR #499: only the selection
+  changes what is read);
+* the pool row of every resident page equals the mirror row after every
+  layer (drop-clean slots), the decode path never writes the mirror, each
+  fetch moves exactly the missed pages and nothing is fetched twice per call;
+* forced drops are counted, never silent.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from oracle import run
+from oracle.attention import dense_reference
+from oracle.engine import CapacityError
+from oracle.store import quantize_tokens
+from oracle.codecs import e4m3_decode
+from workload import gen, get_workload
+
+
+def _check_drop_clean(tier):
+    for s in range(tier.S):
+        p = int(tier.lru.slot_to_page[s])
+        if p >= 0:
+            assert np.array_equal(tier.pool[s], tier.mirror_row(p)), (s, p)
+
+
+def test_c1_chain_drop_clean_and_no_writeback():
+    wl = get_workload("c1")
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    _check_drop_clean(tier)
+    snapshot = {p: r.copy() for p, r in tier.mirror.items()}
+    fetched = []
+
+    def on_layer(s, layer, rec):
+        _check_drop_clean(tier)
+        m = rec["misses"]
+        assert len({int(p) for p in m[:, 1]}) == len(m)   # nothing fetched twice
+        fetched.append(len(m))
+
+    b0 = tier.bytes_fetched
+    run.decode(wl, tier, on_layer=on_layer, attention=True)
+    assert tier.bytes_fetched - b0 == sum(fetched) * tier.lay.row_bytes
+    for p, r in tier.mirror.items():
+        assert np.array_equal(r, snapshot[p])
+    assert tier.counters()["drops"] == 0 and tier.counters()["error_word"] == 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_sparse_equals_dense_when_budget_covers_context(fmt):
+    base = get_workload("c1")
+    wl = replace(base, kv_format=fmt, contexts=(256,), topk=16, num_slots=48, steps=2)
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    tr = run.decode(wl, tier, attention=True)
+    q = gen.decode_queries(wl)
+    k = gen.kv_tokens(wl, gen.KIND_K, 0, 0, 0, 256)
+    v = gen.kv_tokens(wl, gen.KIND_V, 0, 0, 0, 256)
+    if fmt == "fp8":
+        kc, ks = quantize_tokens(k)
+        vc, vs = quantize_tokens(v)
+        k = e4m3_decode(kc).astype(np.float64) * ks[:, None, None]
+        v = e4m3_decode(vc).astype(np.float64) * vs[:, None, None]
+    for s in range(2):
+        assert tr[s][0]["sel"][0].tolist() == list(range(16))
+        ref = dense_reference(q[s, 0, 0].astype(np.float64), k.transpose(1, 0, 2).astype(np.float64),
+                              v.transpose(1, 0, 2).astype(np.float64))
+        assert np.allclose(tr[s][0]["out"][0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_partial_last_page_masked_by_context_length():
+    wl = replace(get_workload("c1"), contexts=(250,), topk=16, num_slots=48, steps=1)
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    tr = run.decode(wl, tier, attention=True)
+    q = gen.decode_queries(wl)
+    k = gen.kv_tokens(wl, gen.KIND_K, 0, 0, 0, 250).transpose(1, 0, 2).astype(np.float64)
+    v = gen.kv_tokens(wl, gen.KIND_V, 0, 0, 0, 250).transpose(1, 0, 2).astype(np.float64)
+    ref = dense_reference(q[0, 0, 0].astype(np.float64), k, v)
+    assert np.allclose(tr[0][0]["out"][0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_forced_drops_counted():
+    wl = replace(get_workload("c1"), steps=2)
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    bt, npg = gen.block_tables(wl)
+    tier.set_select_width(1, wl.topk, 10)       # cap below top-k
+    q = gen.decode_queries(wl)
+    sel, needed = tier.select(0, q[0, 0], np.array([0, 1]), None, bt, npg, wl.topk)
+    assert tier.drops == wl.topk - 10
+    assert needed[0].tolist() == bt[0][sel[0][:10]].tolist()
+
+
+def test_capacity_by_construction():
+    wl = get_workload("c4")
+    tier = run.make_tier(replace(wl, num_slots=200), materialize=False)
+    with pytest.raises(CapacityError):
+        tier.set_select_width(4, 32)            # 4 * 72 = 288 > 200
+
+
+def test_roundtrip_store_evict_fetch_exact():
+    wl = replace(get_workload("c3s"), steps=3)
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    ref = {p: r.copy() for p, r in tier.mirror.items()}
+    run.decode(wl, tier)                                   # thrashes: evicts and refetches
+    assert tier.lru.counters["evictions"] > 0 and tier.bytes_fetched > 0
+    _check_drop_clean(tier)
+    for p, r in tier.mirror.items():
+        assert np.array_equal(r, ref[p])
+
+
+def test_lazy_rows_equal_materialized_rows():
+    wl = get_workload("c4s")
+    a = run.make_tier(wl, materialize=True)
+    b = run.make_tier(wl, materialize=False)
+    run.setup(wl, a)
+    run.setup(wl, b)
+    assert np.array_equal(a.slab, b.slab)
+    for p in [0, 5, 100, 250, wl.num_logical_pages - 1]:
+        assert np.array_equal(a.mirror_row(p), b.mirror_row(p))
+
+
+def test_prefill_chain_small():
+    wl = get_workload("c5s")
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    recs = run.prefill(wl, tier, attention_rows=[0, 1, 63, 64, 511])
+    n0 = wl.contexts[0] // wl.page_size
+    for rec in recs:
+        sel = rec["sel"]
+        # row 0 (position = cached length) sees pages 0..n0
+        assert sel[0].max() <= n0
+        assert np.all(rec["out_slots"][rec["needed"][0] >= 0] >= 0)
+    assert tier.counters()["error_word"] == 0

@@ -1,0 +1,100 @@
+"""Pins for the oracle's store path (quantisation, row layout, slab mean)."""
+import numpy as np
+
+from oracle.codecs import e4m3_decode
+from oracle.layout import RowLayout
+from oracle.store import quantize_tokens, read_kv, slab_entry, write_tokens
+from workload import gen, get_workload
+
+
+def _grid_tokens(n, H=4, d=128, seed=0):
+    rng = np.random.default_rng(seed)
+    return (np.clip(np.rint(rng.standard_normal((n, H, d)) * 16), -64, 64) / 16).astype(np.float32)
+
+
+def test_fp8_relative_error_bound():
+    """Dequantised values are within half an e4m3 ulp: 2^-4 relative in the
+    normal range, 2^-10 * scale absolute in the subnormal range."""
+    x = _grid_tokens(64)
+    codes, scale = quantize_tokens(x)
+    xr = e4m3_decode(codes).astype(np.float64) * scale[:, None, None]
+    err = np.abs(xr - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scale[:, None, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
+def test_amax_element_maps_to_448():
+    x = _grid_tokens(64, seed=1)
+    codes, scale = quantize_tokens(x)
+    flat = np.abs(x.reshape(64, -1))
+    arg = flat.argmax(axis=1)
+    c = codes.reshape(64, -1)[np.arange(64), arg] & 0x7F
+    assert np.all(c == 0x7E)
+
+
+def test_zero_token_scale_one():
+    x = np.zeros((2, 4, 128), dtype=np.float32)
+    codes, scale = quantize_tokens(x)
+    assert np.all(scale == 1.0) and np.all(codes == 0)
+
+
+def test_scale_is_fp32_division():
+    x = _grid_tokens(8, seed=2)
+    _, scale = quantize_tokens(x)
+    amax = np.abs(x.reshape(8, -1)).max(axis=1)
+    # the scale times 448 recovers amax to within one fp32 ulp
+    assert np.all(np.abs(scale.astype(np.float64) * 448 - amax) <= np.spacing(amax.astype(np.float32)))
+
+
+def test_row_layout_sizes_match_survey_shapes():
+    lay = RowLayout(12, 4, 64, 128, True)
+    assert lay.layer_bytes == 66048 and lay.row_bytes == 792576
+    assert RowLayout(1, 1, 16, 128, False).row_bytes == 8192
+
+
+def test_write_read_roundtrip_positions():
+    """bf16 rows store values verbatim: every (head, token, dim) lands where
+    read_kv finds it."""
+    lay = RowLayout(2, 2, 8, 128, False)
+    row = np.zeros(lay.row_bytes, dtype=np.uint8)
+    k = (np.arange(8 * 2 * 128).reshape(8, 2, 128) % 251 - 125).astype(np.float32)
+    v = -k
+    write_tokens(row, lay, 1, 0, k, v)
+    kr, vr = read_kv(row, lay, 1)
+    assert np.array_equal(kr.transpose(1, 0, 2), k) and np.array_equal(vr.transpose(1, 0, 2), v)
+    k0, _ = read_kv(row, lay, 0)
+    assert not np.any(k0)
+
+
+def test_fresh_page_write_zero_fills_tail():
+    lay = RowLayout(1, 4, 64, 128, True)
+    row = np.full(lay.row_bytes, 0xAB, dtype=np.uint8)
+    x = _grid_tokens(10, seed=3)
+    write_tokens(row, lay, 0, 0, x, x)
+    k, _ = read_kv(row, lay, 0)
+    assert not np.any(k[:, 10:])
+    # an append after offset 0 does not touch other positions
+    row2 = row.copy()
+    write_tokens(row2, lay, 0, 10, x[:3], x[:3])
+    k2, _ = read_kv(row2, lay, 0)
+    assert np.array_equal(k2[:, :10], k[:, :10]) and not np.any(k2[:, 13:])
+
+
+def test_slab_is_bf16_of_numpy_mean():
+    x = _grid_tokens(64, seed=4)
+    ref = x.astype(np.float64).mean(axis=0)      # exact on the 2^-4 grid
+    got = slab_entry(x)
+    # bf16 of the mean: relative error <= 2^-9
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-12)
+    # the mean of a page of 64 grid keys is a multiple of 2^-10
+    assert np.all(np.mod(got.astype(np.float64) * 1024, 1) == 0)
+
+
+def test_generator_values_on_grid_and_bf16_exact():
+    wl = get_workload("c2")
+    k = gen.kv_page(wl, gen.KIND_K, 3, 0, 17)
+    assert k.shape == (64, 4, 128)
+    assert np.all(np.mod(k * 16, 1) == 0) and np.abs(k).max() <= 4
+    gen.to_bf16_bits(k)
+    q = gen.prefill_queries(get_workload("c5"), 0, 5, 70)
+    assert q.shape == (70, 32, 128) and np.all(np.mod(q * 32, 1) == 0)
