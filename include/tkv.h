@@ -1,0 +1,258 @@
+/*
+ * tkv.h -- C ABI of the tiered KV-cache sparse decode library (gfx950).
+ *
+ * The method (FreeToken PR #499, "feat(kvcache): host-RAM KV tier for
+ * sparse-attention models", sections "What", "Why this works for sparse
+ * attention" and "Design"): the full KV cache lives in a pinned host mirror
+ * (the backing store); the GPU pool is an LRU cache of physical slots over
+ * the logical page space.  Each attention step first runs the indexer (top-k
+ * page selection over a compressed key slab kept on the GPU), compacts the
+ * selection (cap max_sel_pages = 2*block_topk + 8, with a drop counter),
+ * makes the selected pages resident with a device-side LRU, copies the missed
+ * pages host->device in one fused copy that moves K+V (codes and scales) of a
+ * page for every layer, translates logical page ids to slots, and runs sparse
+ * paged attention over the selected pages only.  Every store of new K/V is
+ * quantised and written through to the mirror, so eviction is a pure rebind.
+ *
+ * Conventions
+ *  - All device pointers are caller-owned device memory (the library never
+ *    allocates device memory).  The pinned host mirror is owned by the ctx.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    calls except tkv_create/tkv_attach_device/tkv_read_counters/
+ *    tkv_debug_read_state are asynchronous, launch a fixed number of kernels
+ *    whose shapes depend only on the arguments' sizes, never synchronise and
+ *    never allocate, so they can be captured in a HIP graph.
+ *  - Return value: TKV_OK (0) or a negative TKV_E_* code; tkv_last_error()
+ *    returns a thread-local message naming the offending argument or knob.
+ *  - Anomalies found on the device (page id out of range, a selection that
+ *    does not fit the pool, a store to a non-resident page) set bits of a
+ *    sticky error word returned by tkv_read_counters.  Pages cut by the
+ *    selection cap are not errors: they are counted in `drops`.
+ *  - One ctx is used from one stream at a time; calls on one ctx that
+ *    overlap on different streams race.
+ *
+ * Page row layout (identical in a pool slot and a mirror row; one row holds
+ * one logical page for ALL layers): for layer l at l*layer_bytes,
+ *   fp8  : K codes u8[Hkv][page][d] | V codes u8[Hkv][page][d] |
+ *          K scales f32[page] | V scales f32[page]
+ *   bf16 : K bf16[Hkv][page][d] | V bf16[Hkv][page][d]
+ * fp8 is OCP E4M3FN; one fp32 scale per token per tensor over all Hkv*d
+ * values: scale = amax/448 (1 if amax == 0), code = e4m3(x / scale), round
+ * to nearest even, saturating.
+ *
+ * Slab: bf16 [L][num_logical_pages][Hkv][d], the mean of each page's written
+ * keys rounded once to bf16.
+ */
+#ifndef TKV_H
+#define TKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TKV_OK 0
+#define TKV_E_INVALID_ARG (-1)
+#define TKV_E_UNSUPPORTED_FORMAT (-2)
+#define TKV_E_CAPACITY (-3)
+#define TKV_E_OOM (-4)
+#define TKV_E_HIP (-5)
+#define TKV_E_STATE (-6)
+
+/* kv_format */
+#define TKV_KV_BF16 0
+#define TKV_KV_FP8_E4M3_PER_TOKEN 1
+#define TKV_KV_NVFP4_BLOCK 2 /* recognised and refused: per-block scales the mirror cannot hold */
+
+/* device error word bits */
+#define TKV_ERR_PAGE_RANGE 1   /* a needed/selected page id outside [-1, num_logical_pages) */
+#define TKV_ERR_CAPACITY 2     /* an ensure needed more distinct pages than slots: call ignored */
+#define TKV_ERR_NOT_RESIDENT 4 /* store to a page with no slot: mirror and slab written, pool not */
+#define TKV_ERR_BAD_MISS 8     /* fetch list entry outside the pool or the page space: skipped */
+
+typedef struct tkv_config {
+  int32_t num_layers;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;     /* num_q_heads / num_kv_heads must be 8; head_dim 128 */
+  int32_t head_dim;
+  int32_t page_size;        /* 16 or 64 tokens */
+  int32_t kv_format;        /* TKV_KV_* */
+  int64_t num_logical_pages;/* mirror rows (cf. --kv-host-pages + --num-pages) */
+  int32_t num_slots;        /* GPU pool slots (cf. --num-pages) */
+  int32_t max_batch;        /* requests per call */
+  int32_t max_rows;         /* query rows per call (decode: requests; prefill: chunk tokens) */
+  int32_t max_topk;         /* pages selected per row */
+  int32_t max_pages_per_req;/* block-table width */
+  int32_t max_width;        /* entries of one ensure call (>= max_batch*max_sel_pages and write-ensures) */
+} tkv_config;
+
+typedef struct tkv_sizes {
+  size_t pool_bytes;      /* num_slots * row_bytes */
+  size_t slab_bytes;      /* bf16 slab */
+  size_t state_bytes;     /* residency state, counters and the slab's fp32 running sums */
+  size_t workspace_bytes; /* per-call scratch for the largest call the config allows */
+  size_t mirror_bytes;    /* pinned host mirror (allocated by tkv_create) */
+  size_t row_bytes;       /* bytes of one page row (all layers) */
+  size_t layer_bytes;     /* bytes of one layer of a row */
+} tkv_sizes;
+
+typedef struct tkv_device_buffers {
+  void* pool;      /* >= pool_bytes, 256-byte aligned */
+  void* slab;      /* >= slab_bytes */
+  void* state;     /* >= state_bytes */
+  void* workspace; /* >= workspace_bytes */
+} tkv_device_buffers;
+
+typedef struct tkv_counters {
+  int64_t ensure_calls, hits, misses, fresh_allocs, evictions, drops, bytes_fetched, bytes_mirrored;
+  int64_t clock;
+  int32_t error_word;
+  int32_t reserved;
+} tkv_counters;
+
+typedef struct tkv_ctx tkv_ctx;
+
+/* Sizes of every buffer the config needs.  TKV_E_UNSUPPORTED_FORMAT for a
+ * kv_format whose scales the mirror cannot hold (the message names
+ * kv_format); TKV_E_INVALID_ARG for shapes the kernels do not support. */
+int tkv_required_bytes(const tkv_config* cfg, tkv_sizes* out);
+
+/* Validates the config and allocates the pinned, device-mapped host mirror
+ * (zero-filled).  *out is owned by the caller until tkv_destroy. */
+int tkv_create(const tkv_config* cfg, tkv_ctx** out);
+
+/* Binds caller-allocated device buffers and initialises them on `stream`
+ * (empty pool, zero slab, zero counters).  Synchronises `stream`. */
+int tkv_attach_device(tkv_ctx* ctx, const tkv_device_buffers* bufs, void* stream);
+
+/* FreeToken PR #525 commit summary (set_select_width takes max_bs): the
+ * whole batch's selection must fit the pool by construction.  Sets the
+ * compaction width C = max_sel_pages (0 -> 2*block_topk + 8, PR #499
+ * "Design").  TKV_E_CAPACITY if max_bs*C > num_slots or > max_width. */
+int tkv_set_select_width(tkv_ctx* ctx, int32_t max_bs, int32_t block_topk, int32_t max_sel_pages);
+
+/* Empties the pool (every page non-resident, clock 0) and zeroes the
+ * counters and error word.  Slab and mirror contents are kept. */
+int tkv_reset_residency(tkv_ctx* ctx, void* stream);
+
+/* Indexer + compact_selected_pages (PR #499 "Why this works for sparse
+ * attention", "Design").  Rows of request b are row_start[b] ..
+ * row_start[b+1]-1 (device int32[B+1]).  For each row: qg[g] = bf16(sum of
+ * the group's bf16 query heads), score of local page i = sum_g qg[g] .
+ * slab[layer][block_table[b][i]][g] + page_bias[logical] (fp32), top-k by
+ * score with ties to the lower page index, written ascending to
+ * sel_local[row][0..topk) and padded with -1.  A row with row_pos != NULL
+ * sees page i only if page_size*i <= row_pos[row].  Per request: union of
+ * its rows' selections, ascending, unique, the first C logical ids written
+ * to needed[b][0..C) (-1 padded), the rest counted as drops.
+ *   q          bf16 [rows][Hq][d]           row_pos   int32 [rows] or NULL
+ *   block_table int32 [B][max_pages]        n_pages   int32 [B]
+ *   page_bias  f32 [num_logical_pages] or NULL
+ *   sel_local  int32 [rows][topk] (out)     needed    int32 [B][C] (out) */
+int tkv_select_pages(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t rows,
+                     const int32_t* row_start, const int32_t* row_pos,
+                     const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                     int32_t B, const float* page_bias, int32_t topk, int32_t* sel_local,
+                     int32_t* needed, void* stream);
+
+/* Device-side LRU (PR #499 "What", "Design": fixed-shape, graph-safe, the
+ * pool is an LRU cache over logical pages, eviction is a rebind).  One clock
+ * tick per call; hits are restamped; misses in first-occurrence order take
+ * the slots not hit by this call in ascending (stamp, slot) order.  A miss
+ * whose first occurrence has no_fetch[j] != 0 is bound without a fetch.
+ *   needed    int32 [width] logical ids, -1 = padding
+ *   no_fetch  uint8 [width] or NULL
+ *   out_slots int32 [width] (out): slot of needed[j] after the call, or -1
+ *   miss      int32 [width][2] (out): (slot, page) rows to fetch
+ *   miss_count int32 [1] (out)
+ * A call needing more distinct pages than slots changes nothing and sets
+ * TKV_ERR_CAPACITY. */
+int tkv_lru_ensure(tkv_ctx* ctx, const int32_t* needed, int32_t width, const uint8_t* no_fetch,
+                   int32_t* out_slots, int32_t* miss, int32_t* miss_count, void* stream);
+
+/* Fused host->device page copy (PR #499 "Design": one launch copies K+V of
+ * a page across all layers; PR #525 commit summary: with the scale banks):
+ * pool row miss[i][0] := mirror row miss[i][1] for i < *miss_count, all
+ * layers, codes and scales.  `width` bounds *miss_count (fixed launch shape). */
+int tkv_fetch_pages(tkv_ctx* ctx, const int32_t* miss, const int32_t* miss_count, int32_t width,
+                    void* stream);
+
+/* Sparse paged attention over the selected pages (PR #499 "Design": after
+ * ensure the block table is translated logical->physical; the page ids are
+ * translated here through the LRU's page->slot map).  For row r of request b
+ * and query head h (KV head h/8): softmax over the tokens 64*i+j of the
+ * selected resident pages i with position < ctx_len[b] (and <= row_pos[r]
+ * when row_pos != NULL) of (q_h . k)/sqrt(d), times v; k and v dequantised.
+ * Empty selection -> zeros.  out bf16 [rows][Hq][d], round to nearest even.
+ * Rows of request b are row_start[b] .. row_start[b+1]-1 (device int32[B+1]);
+ * block_table int32 [B][max_pages]; ctx_len int32 [B]; sel_local as
+ * written by tkv_select_pages.  With rows > max_batch (prefill chunks) topk
+ * must be <= 64. */
+int tkv_sparse_paged_attn(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t rows,
+                          const int32_t* row_start, const int32_t* row_pos,
+                          const int32_t* ctx_len, int32_t B, const int32_t* sel_local,
+                          const int32_t* block_table, int32_t max_pages, int32_t topk,
+                          uint16_t* out, void* stream);
+
+/* One decode step of one layer for B requests with one query row each:
+ * select + compact + ensure in one launch, then fetch, then attention.
+ * Same semantics as tkv_select_pages -> tkv_lru_ensure(needed, B*C) ->
+ * tkv_fetch_pages -> tkv_sparse_paged_attn.  out_slots int32 [B*C],
+ * miss int32 [B*C][2], miss_count int32 [1]. */
+int tkv_decode_layer(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
+                     const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                     const int32_t* ctx_len, const float* page_bias, int32_t topk,
+                     int32_t* sel_local, int32_t* needed, int32_t* out_slots, int32_t* miss,
+                     int32_t* miss_count, uint16_t* out, void* stream);
+
+/* ensure_write_pages (PR #499 "Design": one fixed-shape launch of stride
+ * samples plus one boundary sample per request run): run r writes tokens
+ * run_start[r] .. run_start[r]+run_len[r]-1 of request run_req[r].  Every
+ * page the runs touch is made resident (one ensure call); a page whose
+ * first position is >= old_len[req] has no content yet and is bound without
+ * a fetch; other missed pages are fetched.  run_len[r] <= max_run_len. */
+int tkv_ensure_write_pages(tkv_ctx* ctx, int32_t n_runs, const int32_t* run_req,
+                           const int32_t* run_start, const int32_t* run_len, int32_t max_run_len,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* old_len,
+                           void* stream);
+
+/* store_kv with the write-through mirror (PR #499 "Design"; PR #525 commit
+ * summary, mirror_store_quant: the mirror takes the codes and scales read
+ * after quantisation).  k, v bf16 [n_tok][Hkv][d]: the tokens of run r are
+ * at rows run_tok_off[r] ..; they are quantised (fp8) or copied (bf16) into
+ * the page's slot and its mirror row; a write that begins a page zero-fills
+ * the page's later positions; the slab entry of each touched page becomes
+ * the mean of all its written keys.  Runs of one call must not share pages.
+ * Pages must be resident (tkv_ensure_write_pages). */
+int tkv_store_kv_mirror(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const uint16_t* v,
+                        int32_t n_runs, const int32_t* run_req, const int32_t* run_start,
+                        const int32_t* run_len, const int32_t* run_tok_off, int32_t max_run_len,
+                        const int32_t* block_table, int32_t max_pages, void* stream);
+
+/* Copies the counters to the host.  Synchronises `stream`. */
+int tkv_read_counters(tkv_ctx* ctx, tkv_counters* out, void* stream);
+
+/* Test hooks.  Copy the LRU state to host arrays (page_to_slot
+ * [num_logical_pages], slot_to_page [num_slots], stamp [num_slots]);
+ * synchronises `stream`. */
+int tkv_debug_read_state(tkv_ctx* ctx, int32_t* page_to_slot, int32_t* slot_to_page,
+                         int64_t* stamp, int64_t* clock, void* stream);
+/* fp32 -> e4m3 codes with the store's encoder; device pointers. */
+int tkv_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+/* e4m3 codes -> fp32 with the attention kernel's decoder; device pointers. */
+int tkv_debug_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream);
+
+/* Host pointer to the pinned mirror (read-only view for tests). */
+const void* tkv_mirror_host_ptr(const tkv_ctx* ctx);
+
+/* Frees the mirror and the ctx.  Device buffers stay with the caller. */
+void tkv_destroy(tkv_ctx* ctx);
+
+const char* tkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TKV_H */

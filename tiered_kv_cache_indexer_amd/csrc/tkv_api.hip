@@ -1,0 +1,467 @@
+// C ABI of the tiered KV-cache library: validation, buffer layout, launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/tkv.h"
+#include "tkv_dev.h"
+#include "tkv_launch.h"
+
+#define SEL_CHUNK_HOST 64
+
+struct tkv_ctx {
+  tkv_config cfg;
+  size_t row_bytes, layer_bytes, code_bytes;
+  size_t mirror_bytes;
+  uint8_t* mirror_host = nullptr;
+  uint8_t* mirror_dev = nullptr;
+  bool attached = false;
+  DevCtx dev{};
+  int C = 0;            // compaction width (set_select_width)
+};
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+static int hip_fail(hipError_t e, const char* what) {
+  return fail(TKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHECK(expr, what)                 \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t row, layer, code;
+  size_t pool, slab, mirror;
+  // state offsets
+  size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
+  // workspace offsets
+  size_t ws_scores, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_total;
+};
+
+static int validate(const tkv_config* c) {
+  if (!c) return fail(TKV_E_INVALID_ARG, "config is NULL");
+  if (c->kv_format == TKV_KV_NVFP4_BLOCK)
+    return fail(TKV_E_UNSUPPORTED_FORMAT,
+                "kv_format=nvfp4: per-block scales are not held by the host mirror rows; "
+                "use kv_format=fp8_e4m3_per_token or bf16");
+  if (c->kv_format != TKV_KV_BF16 && c->kv_format != TKV_KV_FP8_E4M3_PER_TOKEN)
+    return fail(TKV_E_UNSUPPORTED_FORMAT, "kv_format=%d is not a known KV format", c->kv_format);
+  if (c->num_layers < 1) return fail(TKV_E_INVALID_ARG, "num_layers=%d must be >= 1", c->num_layers);
+  if (c->head_dim != 128) return fail(TKV_E_INVALID_ARG, "head_dim=%d: only 128 is supported", c->head_dim);
+  if (c->num_kv_heads < 1 || c->num_q_heads != 8 * c->num_kv_heads)
+    return fail(TKV_E_INVALID_ARG, "num_q_heads=%d, num_kv_heads=%d: the GQA group must be 8",
+                c->num_q_heads, c->num_kv_heads);
+  const int e8 = c->num_kv_heads * c->head_dim / 8;
+  if (e8 != 16 && e8 != 32 && e8 != 64 && e8 != 128)
+    return fail(TKV_E_INVALID_ARG, "num_kv_heads=%d: 1, 2, 4 or 8 KV heads are supported", c->num_kv_heads);
+  if (c->page_size != 16 && c->page_size != 64)
+    return fail(TKV_E_INVALID_ARG, "page_size=%d: 16 or 64 tokens are supported", c->page_size);
+  if (c->num_logical_pages < 1 || c->num_logical_pages > 0x7FFFFFFF)
+    return fail(TKV_E_INVALID_ARG, "num_logical_pages=%lld out of range", (long long)c->num_logical_pages);
+  if (c->num_slots < 1) return fail(TKV_E_INVALID_ARG, "num_slots=%d must be >= 1", c->num_slots);
+  if (c->max_batch < 1 || c->max_rows < c->max_batch)
+    return fail(TKV_E_INVALID_ARG, "max_batch=%d, max_rows=%d: need 1 <= max_batch <= max_rows",
+                c->max_batch, c->max_rows);
+  if (c->max_topk < 1 || c->max_topk > 1024)
+    return fail(TKV_E_INVALID_ARG, "max_topk=%d out of [1, 1024]", c->max_topk);
+  if (c->max_pages_per_req < 1 || c->max_pages_per_req > 16384)
+    return fail(TKV_E_INVALID_ARG, "max_pages_per_req=%d out of [1, 16384]", c->max_pages_per_req);
+  if (c->max_width < 1 || c->max_width > 65535)
+    return fail(TKV_E_INVALID_ARG, "max_width=%d out of [1, 65535]", c->max_width);
+  return TKV_OK;
+}
+
+static Layout make_layout(const tkv_config* c) {
+  Layout L{};
+  const size_t H = c->num_kv_heads, PS = c->page_size, D = c->head_dim, N = c->num_logical_pages,
+               S = c->num_slots, NL = c->num_layers;
+  const bool fp8 = c->kv_format == TKV_KV_FP8_E4M3_PER_TOKEN;
+  L.code = H * PS * D * (fp8 ? 1 : 2);
+  L.layer = 2 * L.code + (fp8 ? 8 * PS : 0);
+  L.row = NL * L.layer;
+  L.pool = S * L.row;
+  L.mirror = N * L.row;
+  L.slab = NL * N * H * D * 2;
+  size_t o = 0;
+  L.st_hdr = o; o = align256(o + sizeof(StateHdr));
+  L.st_p2s = o; o = align256(o + N * 4);
+  L.st_mark = o; o = align256(o + N * 4);
+  L.st_s2p = o; o = align256(o + S * 4);
+  L.st_stamp = o; o = align256(o + S * 8);
+  L.st_order = o; o = align256(o + 2 * S * 4);
+  L.st_touched = o; o = align256(o + S * 4);
+  L.st_acc = o; o = align256(o + NL * N * H * D * 4);
+  L.st_total = o;
+  const size_t W = c->max_width, R = c->max_rows, P = c->max_pages_per_req;
+  o = 0;
+  L.ws_scores = o; o = align256(o + R * P * 4);
+  L.ws_row_done = o; o = align256(o + R * 4);
+  L.ws_glob = o; o = align256(o + 16);
+  L.ws_slot_of_j = o; o = align256(o + W * 4);
+  L.ws_miss_j = o; o = align256(o + W * 4);
+  L.ws_victims = o; o = align256(o + W * 4);
+  L.ws_wneeded = o; o = align256(o + W * 4);
+  L.ws_wnofetch = o; o = align256(o + W);
+  L.ws_wmiss = o; o = align256(o + W * 8);
+  L.ws_wmiss_count = o; o = align256(o + 4);
+  L.ws_part = o; o = align256(o + (size_t)c->max_batch * c->num_q_heads * c->max_topk * (D + 2) * 4);
+  L.ws_attn_done = o; o = align256(o + (size_t)c->max_batch * H * 4);
+  L.ws_iota = o; o = align256(o + (R + 1) * 4);
+  L.ws_total = o;
+  return L;
+}
+
+extern "C" {
+
+const char* tkv_last_error(void) { return g_err.c_str(); }
+
+int tkv_required_bytes(const tkv_config* cfg, tkv_sizes* out) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!out) return fail(TKV_E_INVALID_ARG, "out is NULL");
+  Layout L = make_layout(cfg);
+  out->pool_bytes = L.pool;
+  out->slab_bytes = L.slab;
+  out->state_bytes = L.st_total;
+  out->workspace_bytes = L.ws_total;
+  out->mirror_bytes = L.mirror;
+  out->row_bytes = L.row;
+  out->layer_bytes = L.layer;
+  return TKV_OK;
+}
+
+int tkv_create(const tkv_config* cfg, tkv_ctx** out) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!out) return fail(TKV_E_INVALID_ARG, "out is NULL");
+  Layout L = make_layout(cfg);
+  tkv_ctx* c = new tkv_ctx();
+  c->cfg = *cfg;
+  c->row_bytes = L.row;
+  c->layer_bytes = L.layer;
+  c->code_bytes = L.code;
+  c->mirror_bytes = L.mirror;
+  void* h = nullptr;
+  hipError_t e = hipHostMalloc(&h, L.mirror, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess || !h) {
+    delete c;
+    return fail(TKV_E_OOM, "pinned host mirror of %zu bytes (num_logical_pages=%lld): %s", L.mirror,
+                (long long)cfg->num_logical_pages, hipGetErrorString(e));
+  }
+  memset(h, 0, L.mirror);
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    hipHostFree(h);
+    delete c;
+    return hip_fail(e, "hipHostGetDevicePointer(mirror)");
+  }
+  c->mirror_host = (uint8_t*)h;
+  c->mirror_dev = (uint8_t*)d;
+  *out = c;
+  return TKV_OK;
+}
+
+void tkv_destroy(tkv_ctx* c) {
+  if (!c) return;
+  if (c->mirror_host) hipHostFree(c->mirror_host);
+  delete c;
+}
+
+const void* tkv_mirror_host_ptr(const tkv_ctx* c) { return c ? c->mirror_host : nullptr; }
+
+static bool aligned256(const void* p) { return ((uintptr_t)p & 255) == 0; }
+
+int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
+  if (!c || !b) return fail(TKV_E_INVALID_ARG, "ctx or buffers is NULL");
+  if (!b->pool || !b->slab || !b->state || !b->workspace)
+    return fail(TKV_E_INVALID_ARG, "a device buffer is NULL (pool, slab, state, workspace)");
+  if (!aligned256(b->pool) || !aligned256(b->slab) || !aligned256(b->state) || !aligned256(b->workspace))
+    return fail(TKV_E_INVALID_ARG, "device buffers must be 256-byte aligned");
+  Layout L = make_layout(&c->cfg);
+  const tkv_config& f = c->cfg;
+  DevCtx& d = c->dev;
+  d = DevCtx{};
+  d.L = f.num_layers; d.Hq = f.num_q_heads; d.Hkv = f.num_kv_heads; d.D = f.head_dim;
+  d.PS = f.page_size; d.fp8 = f.kv_format == TKV_KV_FP8_E4M3_PER_TOKEN;
+  d.N = f.num_logical_pages; d.S = f.num_slots;
+  d.row_bytes = (int64_t)L.row; d.layer_bytes = (int64_t)L.layer; d.code_bytes = (int64_t)L.code;
+  d.pool = (uint8_t*)b->pool;
+  d.mirror = c->mirror_dev;
+  d.slab = (uint16_t*)b->slab;
+  uint8_t* st = (uint8_t*)b->state;
+  d.hdr = (StateHdr*)(st + L.st_hdr);
+  d.page_to_slot = (int32_t*)(st + L.st_p2s);
+  d.page_mark = (int32_t*)(st + L.st_mark);
+  d.slot_to_page = (int32_t*)(st + L.st_s2p);
+  d.stamp = (int64_t*)(st + L.st_stamp);
+  d.order = (int32_t*)(st + L.st_order);
+  d.touched = (int32_t*)(st + L.st_touched);
+  d.slab_acc = (float*)(st + L.st_acc);
+  uint8_t* ws = (uint8_t*)b->workspace;
+  d.scores = (float*)(ws + L.ws_scores);
+  d.row_done = (int32_t*)(ws + L.ws_row_done);
+  d.glob_done = (int32_t*)(ws + L.ws_glob);
+  d.slot_of_j = (int32_t*)(ws + L.ws_slot_of_j);
+  d.miss_j = (int32_t*)(ws + L.ws_miss_j);
+  d.victims = (int32_t*)(ws + L.ws_victims);
+  d.wneeded = (int32_t*)(ws + L.ws_wneeded);
+  d.wnofetch = (uint8_t*)(ws + L.ws_wnofetch);
+  d.wmiss = (int32_t*)(ws + L.ws_wmiss);
+  d.wmiss_count = (int32_t*)(ws + L.ws_wmiss_count);
+  d.attn_part = (float*)(ws + L.ws_part);
+  d.attn_done = (int32_t*)(ws + L.ws_attn_done);
+  d.iota = (int32_t*)(ws + L.ws_iota);
+  d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
+  d.max_batch = f.max_batch; d.max_width = f.max_width;
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(launch_reset(d, 1, s), "initialise device state");
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  c->attached = true;
+  return TKV_OK;
+}
+
+int tkv_set_select_width(tkv_ctx* c, int32_t max_bs, int32_t block_topk, int32_t max_sel_pages) {
+  if (!c) return fail(TKV_E_INVALID_ARG, "ctx is NULL");
+  if (max_bs < 1 || max_bs > c->cfg.max_batch)
+    return fail(TKV_E_INVALID_ARG, "max_bs=%d out of [1, max_batch=%d]", max_bs, c->cfg.max_batch);
+  if (block_topk < 1 || block_topk > c->cfg.max_topk)
+    return fail(TKV_E_INVALID_ARG, "block_topk=%d out of [1, max_topk=%d]", block_topk, c->cfg.max_topk);
+  const int C = max_sel_pages > 0 ? max_sel_pages : 2 * block_topk + 8;
+  if ((int64_t)max_bs * C > c->cfg.num_slots)
+    return fail(TKV_E_CAPACITY, "max_bs*max_sel_pages=%d*%d=%lld > num_slots=%d: the batch selection "
+                "must fit the pool", max_bs, C, (long long)max_bs * C, c->cfg.num_slots);
+  if ((int64_t)max_bs * C > c->cfg.max_width)
+    return fail(TKV_E_CAPACITY, "max_bs*max_sel_pages=%lld > max_width=%d", (long long)max_bs * C,
+                c->cfg.max_width);
+  c->C = C;
+  return TKV_OK;
+}
+
+static int need_attached(tkv_ctx* c) {
+  if (!c) return fail(TKV_E_INVALID_ARG, "ctx is NULL");
+  if (!c->attached) return fail(TKV_E_STATE, "device buffers not attached (tkv_attach_device)");
+  return TKV_OK;
+}
+
+int tkv_reset_residency(tkv_ctx* c, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  HIPCHECK(launch_reset(c->dev, 0, (hipStream_t)stream), "reset residency");
+  return TKV_OK;
+}
+
+static int check_rows(tkv_ctx* c, int layer, int rows, int B, int max_pages, int topk) {
+  const tkv_config& f = c->cfg;
+  if (layer < 0 || layer >= f.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of [0, %d)", layer, f.num_layers);
+  if (rows < 1 || rows > f.max_rows) return fail(TKV_E_INVALID_ARG, "rows=%d out of [1, max_rows=%d]", rows, f.max_rows);
+  if (B < 1 || B > f.max_batch) return fail(TKV_E_INVALID_ARG, "B=%d out of [1, max_batch=%d]", B, f.max_batch);
+  if (max_pages < 1 || max_pages > f.max_pages_per_req)
+    return fail(TKV_E_INVALID_ARG, "max_pages=%d out of [1, max_pages_per_req=%d]", max_pages, f.max_pages_per_req);
+  if (topk < 1 || topk > f.max_topk) return fail(TKV_E_INVALID_ARG, "topk=%d out of [1, max_topk=%d]", topk, f.max_topk);
+  return TKV_OK;
+}
+
+static SelArgs make_sel(tkv_ctx* c, int layer, const uint16_t* q, int rows, const int32_t* row_start,
+                        const int32_t* row_pos, const int32_t* bt, int max_pages, const int32_t* n_pages,
+                        int B, const float* bias, int topk, int32_t* sel, int32_t* needed) {
+  SelArgs a{};
+  a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
+  a.bt = bt; a.max_pages = max_pages; a.n_pages = n_pages; a.B = B; a.bias = bias; a.topk = topk;
+  a.sel_local = sel; a.needed = needed; a.C = c->C;
+  a.n_chunks = (max_pages + SEL_CHUNK_HOST - 1) / SEL_CHUNK_HOST;
+  return a;
+}
+
+int tkv_select_pages(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows, const int32_t* row_start,
+                     const int32_t* row_pos, const int32_t* block_table, int32_t max_pages,
+                     const int32_t* n_pages, int32_t B, const float* page_bias, int32_t topk,
+                     int32_t* sel_local, int32_t* needed, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if ((rc = check_rows(c, layer, rows, B, max_pages, topk))) return rc;
+  if (!c->C) return fail(TKV_E_STATE, "select width not set (tkv_set_select_width)");
+  if (!q || !row_start || !block_table || !n_pages || !sel_local || !needed)
+    return fail(TKV_E_INVALID_ARG, "a required pointer is NULL (q, row_start, block_table, n_pages, sel_local, needed)");
+  SelArgs a = make_sel(c, layer, q, rows, row_start, row_pos, block_table, max_pages, n_pages, B,
+                       page_bias, topk, sel_local, needed);
+  a.do_ensure = 0;
+  HIPCHECK(launch_select_scan(c->dev, a, (hipStream_t)stream), "select_pages launch");
+  return TKV_OK;
+}
+
+int tkv_lru_ensure(tkv_ctx* c, const int32_t* needed, int32_t width, const uint8_t* no_fetch,
+                   int32_t* out_slots, int32_t* miss, int32_t* miss_count, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (width < 1 || width > c->cfg.max_width)
+    return fail(TKV_E_INVALID_ARG, "width=%d out of [1, max_width=%d]", width, c->cfg.max_width);
+  if (!needed || !miss || !miss_count)
+    return fail(TKV_E_INVALID_ARG, "needed, miss and miss_count must not be NULL");
+  HIPCHECK(launch_ensure(c->dev, needed, width, no_fetch, out_slots, miss, miss_count, (hipStream_t)stream),
+           "lru_ensure launch");
+  return TKV_OK;
+}
+
+int tkv_fetch_pages(tkv_ctx* c, const int32_t* miss, const int32_t* miss_count, int32_t width, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (width < 1 || !miss || !miss_count) return fail(TKV_E_INVALID_ARG, "miss, miss_count or width invalid");
+  HIPCHECK(launch_fetch(c->dev, miss, miss_count, width, (hipStream_t)stream), "fetch_pages launch");
+  return TKV_OK;
+}
+
+int tkv_sparse_paged_attn(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
+                          const int32_t* row_start, const int32_t* row_pos, const int32_t* ctx_len,
+                          int32_t B, const int32_t* sel_local, const int32_t* block_table,
+                          int32_t max_pages, int32_t topk, uint16_t* out, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if ((rc = check_rows(c, layer, rows, B, max_pages, topk))) return rc;
+  if (!q || !row_start || !ctx_len || !sel_local || !block_table || !out)
+    return fail(TKV_E_INVALID_ARG, "a required pointer is NULL (q, row_start, ctx_len, sel_local, block_table, out)");
+  if (rows > c->cfg.max_batch && topk > 64)
+    return fail(TKV_E_INVALID_ARG, "topk=%d > 64 with rows=%d > max_batch: such rows are not split", topk, rows);
+  AttnArgs a{};
+  a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
+  a.ctx_len = ctx_len; a.sel = sel_local; a.bt = block_table; a.max_pages = max_pages; a.topk = topk;
+  a.B = B; a.out = out;
+  HIPCHECK(launch_attn(c->dev, a, (hipStream_t)stream), "sparse_paged_attn launch");
+  return TKV_OK;
+}
+
+int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* n_pages, const int32_t* ctx_len,
+                     const float* page_bias, int32_t topk, int32_t* sel_local, int32_t* needed,
+                     int32_t* out_slots, int32_t* miss, int32_t* miss_count, uint16_t* out, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if ((rc = check_rows(c, layer, B, B, max_pages, topk))) return rc;
+  if (!c->C) return fail(TKV_E_STATE, "select width not set (tkv_set_select_width)");
+  if (!q || !block_table || !n_pages || !ctx_len || !sel_local || !needed || !miss || !miss_count || !out)
+    return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
+  if ((int64_t)B * c->C > c->cfg.max_width || (int64_t)B * c->C > c->cfg.num_slots)
+    return fail(TKV_E_CAPACITY, "B*max_sel_pages=%lld exceeds num_slots or max_width", (long long)B * c->C);
+  hipStream_t s = (hipStream_t)stream;
+  SelArgs a = make_sel(c, layer, q, B, c->dev.iota, nullptr, block_table, max_pages, n_pages, B,
+                       page_bias, topk, sel_local, needed);
+  a.do_ensure = 1;
+  a.out_slots = out_slots;
+  a.miss = miss;
+  a.miss_count = miss_count;
+  HIPCHECK(launch_select_scan(c->dev, a, s), "decode select+ensure launch");
+  HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
+  AttnArgs t{};
+  t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
+  t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
+  t.B = B; t.out = out;
+  HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");
+  return TKV_OK;
+}
+
+int tkv_ensure_write_pages(tkv_ctx* c, int32_t n_runs, const int32_t* run_req, const int32_t* run_start,
+                           const int32_t* run_len, int32_t max_run_len, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* old_len, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (n_runs < 1 || max_run_len < 1) return fail(TKV_E_INVALID_ARG, "n_runs=%d, max_run_len=%d must be >= 1", n_runs, max_run_len);
+  if (!run_req || !run_start || !run_len || !block_table || !old_len)
+    return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
+  if (max_pages < 1 || max_pages > c->cfg.max_pages_per_req) return fail(TKV_E_INVALID_ARG, "max_pages out of range");
+  const int spr = (max_run_len + c->cfg.page_size - 1) / c->cfg.page_size + 1;
+  if ((int64_t)n_runs * spr > c->cfg.max_width)
+    return fail(TKV_E_CAPACITY, "n_runs*(max_run_len/page_size+1)=%lld samples > max_width=%d",
+                (long long)n_runs * spr, c->cfg.max_width);
+  HIPCHECK(launch_write_ensure(c->dev, n_runs, run_req, run_start, run_len, spr, block_table, max_pages,
+                               old_len, (hipStream_t)stream), "ensure_write_pages launch");
+  return TKV_OK;
+}
+
+int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,
+                        const int32_t* run_req, const int32_t* run_start, const int32_t* run_len,
+                        const int32_t* run_tok_off, int32_t max_run_len, const int32_t* block_table,
+                        int32_t max_pages, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
+  if (n_runs < 1 || max_run_len < 1) return fail(TKV_E_INVALID_ARG, "n_runs=%d, max_run_len=%d must be >= 1", n_runs, max_run_len);
+  if (!k || !v || !run_req || !run_start || !run_len || !run_tok_off || !block_table)
+    return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
+  if (max_pages < 1 || max_pages > c->cfg.max_pages_per_req) return fail(TKV_E_INVALID_ARG, "max_pages out of range");
+  StoreArgs a{};
+  a.layer = layer; a.k = k; a.v = v; a.n_runs = n_runs; a.run_req = run_req; a.run_start = run_start;
+  a.run_len = run_len; a.run_tok_off = run_tok_off; a.bt = block_table; a.max_pages = max_pages;
+  HIPCHECK(launch_store(c->dev, a, max_run_len, (hipStream_t)stream), "store_kv_mirror launch");
+  return TKV_OK;
+}
+
+int tkv_read_counters(tkv_ctx* c, tkv_counters* out, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (!out) return fail(TKV_E_INVALID_ARG, "out is NULL");
+  StateHdr h;
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(hipMemcpyAsync(&h, c->dev.hdr, sizeof h, hipMemcpyDeviceToHost, s), "read counters");
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  out->ensure_calls = h.counters[CNT_ENSURE];
+  out->hits = h.counters[CNT_HITS];
+  out->misses = h.counters[CNT_MISSES];
+  out->fresh_allocs = h.counters[CNT_FRESH];
+  out->evictions = h.counters[CNT_EVICT];
+  out->drops = h.counters[CNT_DROPS];
+  out->bytes_fetched = h.counters[CNT_BYTES_FETCHED];
+  out->bytes_mirrored = h.counters[CNT_BYTES_MIRRORED];
+  out->clock = h.clock;
+  out->error_word = h.error_word;
+  out->reserved = 0;
+  return TKV_OK;
+}
+
+int tkv_debug_read_state(tkv_ctx* c, int32_t* page_to_slot, int32_t* slot_to_page, int64_t* stamp,
+                         int64_t* clock, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const DevCtx& d = c->dev;
+  if (page_to_slot) HIPCHECK(hipMemcpyAsync(page_to_slot, d.page_to_slot, (size_t)d.N * 4, hipMemcpyDeviceToHost, s), "read page_to_slot");
+  if (slot_to_page) HIPCHECK(hipMemcpyAsync(slot_to_page, d.slot_to_page, (size_t)d.S * 4, hipMemcpyDeviceToHost, s), "read slot_to_page");
+  if (stamp) HIPCHECK(hipMemcpyAsync(stamp, d.stamp, (size_t)d.S * 8, hipMemcpyDeviceToHost, s), "read stamp");
+  StateHdr h;
+  HIPCHECK(hipMemcpyAsync(&h, d.hdr, sizeof h, hipMemcpyDeviceToHost, s), "read clock");
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (clock) *clock = h.clock;
+  return TKV_OK;
+}
+
+int tkv_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (!in || !out || n < 0) return fail(TKV_E_INVALID_ARG, "bad arguments");
+  HIPCHECK(launch_e4m3_encode(in, out, n, (hipStream_t)stream), "e4m3 encode launch");
+  return TKV_OK;
+}
+
+int tkv_debug_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream) {
+  if (!in || !out || n < 0) return fail(TKV_E_INVALID_ARG, "bad arguments");
+  HIPCHECK(launch_e4m3_decode(in, out, n, (hipStream_t)stream), "e4m3 decode launch");
+  return TKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Device-side definitions shared by the tiered KV-cache kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TKV_BLOCK 256
+#define TKV_WAVE 64
+
+// device error word bits (mirror the TKV_ERR_* values of the public header)
+#define DERR_PAGE_RANGE 1
+#define DERR_CAPACITY 2
+#define DERR_NOT_RESIDENT 4
+#define DERR_BAD_MISS 8
+
+enum { CNT_ENSURE = 0, CNT_HITS, CNT_MISSES, CNT_FRESH, CNT_EVICT, CNT_DROPS, CNT_BYTES_FETCHED,
+       CNT_BYTES_MIRRORED, CNT_N };
+
+struct StateHdr {
+  int64_t clock;
+  int64_t counters[CNT_N];
+  int32_t error_word;
+  int32_t parity;      // which half of `order` is current
+  int32_t pad[2];
+};
+
+// Everything a kernel needs to find the tier's memory.  Passed by value.
+struct DevCtx {
+  int L, Hq, Hkv, D, PS, fp8;
+  int64_t N;      // logical pages
+  int S;          // slots
+  int64_t row_bytes, layer_bytes, code_bytes;
+  uint8_t* pool;
+  uint8_t* mirror;          // device-visible address of the pinned host mirror
+  uint16_t* slab;           // bf16 [L][N][Hkv][D]
+  float* slab_acc;          // fp32 [L][N][Hkv][D] running key sums
+  // residency state
+  StateHdr* hdr;
+  int32_t* page_to_slot;    // [N]
+  int32_t* page_mark;       // [N], INT32_MAX when idle (first-occurrence scratch)
+  int32_t* slot_to_page;    // [S]
+  int64_t* stamp;           // [S]
+  int32_t* order;           // [2][S] slots in ascending (stamp, slot)
+  int32_t* touched;         // [S]
+  // workspace
+  float* scores;            // [max_rows][max_pages]
+  int32_t* row_done;        // [max_rows] last-block counters (kept at zero between calls)
+  int32_t* glob_done;       // [4]
+  int32_t* slot_of_j;       // [max_width]
+  int32_t* miss_j;          // [max_width]
+  int32_t* victims;         // [max_width]
+  int32_t* wneeded;         // [max_width]
+  uint8_t* wnofetch;        // [max_width]
+  int32_t* wmiss;           // [max_width][2]
+  int32_t* wmiss_count;     // [1]
+  float* attn_part;         // [max_batch][Hq][max_topk][D+2]
+  int32_t* attn_done;       // [max_batch][Hkv]
+  int32_t* iota;            // [max_rows + 1] = 0, 1, 2, ... (row_start of one-row-per-request calls)
+  int max_rows, max_pages, max_topk, max_batch, max_width;
+};
+
+// ------------------------------------------------------------- call arguments --
+struct SelArgs {
+  int layer;
+  const uint16_t* q;
+  int rows;
+  const int32_t* row_start;
+  const int32_t* row_pos;
+  const int32_t* bt;
+  int max_pages;
+  const int32_t* n_pages;
+  int B;
+  const float* bias;
+  int topk;
+  int32_t* sel_local;
+  int32_t* needed;
+  int C;
+  int n_chunks;
+  int do_ensure;
+  int32_t* out_slots;
+  int32_t* miss;
+  int32_t* miss_count;
+};
+
+struct StoreArgs {
+  int layer;
+  const uint16_t* k;
+  const uint16_t* v;
+  int n_runs;
+  const int32_t* run_req;
+  const int32_t* run_start;
+  const int32_t* run_len;
+  const int32_t* run_tok_off;
+  const int32_t* bt;
+  int max_pages;
+};
+
+struct AttnArgs {
+  int layer;
+  const uint16_t* q;
+  int rows;
+  const int32_t* row_start;
+  const int32_t* row_pos;
+  const int32_t* ctx_len;
+  const int32_t* sel;
+  const int32_t* bt;
+  int max_pages;
+  int topk;
+  int B;
+  uint16_t* out;
+  int splits;
+  int pages_per_split;
+};
+
+// ------------------------------------------------------------------ numbers --
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> bfloat16, round to nearest, ties to even
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// binary32 -> OCP E4M3FN, round to nearest, ties to even, saturating to +-448.
+// Normal results: the IEEE exponent/mantissa field rounded to 3 mantissa bits
+// and rebiased (127 -> 7); subnormal results: round(|x| * 2^9) to an integer.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;   // >= 448 (and inf): saturate
+  if (a >= 0x3C800000u) {                      // >= 2^-6: normal
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    return sign | (r - (120u << 3));
+  }
+  float m = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE to integer 0..8
+  return sign | (uint32_t)m;
+}
+
+// e4m3 byte pair decode through the hardware converter (gfx950: OCP E4M3FN)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2 e4m3x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false); }
+__device__ __forceinline__ f32x2 e4m3x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true); }
+
+// orderable key: larger float -> larger unsigned (+0 canonical)
+__device__ __forceinline__ uint32_t f32_order(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------------ block ops --
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim == 256).
+// Returns the exclusive prefix; *total gets the block sum.  Uses sm[0..4].
+__device__ __forceinline__ int block_excl_scan(int v, int* total, int* sm) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v);
+  __syncthreads();
+  if (lane == 63) sm[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < TKV_BLOCK / 64; ++i) {
+    int s = sm[i];
+    if (i < w) base += s;
+    tot += s;
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* sm) {
+  int tot;
+  (void)block_excl_scan(v, &tot, sm);
+  return tot;
+}
+
+__device__ __forceinline__ int ld_acquire_i32(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void set_error(StateHdr* h, int bits) {
+  atomicOr(&h->error_word, bits);
+}
+
+// Last-block election: every block calls it once after publishing its
+// results; returns true in exactly one block (the last to arrive), after
+// which that block sees every other block's writes.  The counter is reset.
+__device__ __forceinline__ bool last_block_arrive(int32_t* counter, int expected, int* sm_flag) {
+  __threadfence();  // every thread: its global writes are visible device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (old == expected - 1);
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sm_flag = last;
+  }
+  __syncthreads();
+  bool last = *sm_flag != 0;
+  if (last) __threadfence();
+  return last;
+}

@@ -1,0 +1,198 @@
+// Fused host->device page copy, write-ensure sampling, state initialisation
+// and the codec test kernels (gfx950).
+//
+// FreeToken PR #499, "Design": one launch copies K+V of a page for every
+// layer; PR #525 commit summary: the copy also carries the scale banks.  With
+// page-major rows (a row holds one page for all layers, scales included) one
+// miss is one contiguous mirror row -> one contiguous pool slot.
+//
+// The miss count lives on the device, so the launch is fixed-shape: a grid of
+// FETCH_GRID workgroups walks (miss, 16 KiB chunk) work items up to
+// *miss_count.  Each thread moves four 16-byte vectors per item, all four
+// loads issued before the stores, reading the pinned mirror over the host
+// link with non-temporal loads (the bytes are used once from host memory).
+#include "tkv_dev.h"
+#include "tkv_launch.h"
+
+#define FETCH_GRID 1024
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define FETCH_VEC_PER_THREAD 4
+#define FETCH_CHUNK (TKV_BLOCK * 16 * FETCH_VEC_PER_THREAD)
+
+__global__ __launch_bounds__(TKV_BLOCK) void k_fetch(DevCtx c, const int32_t* miss,
+                                                     const int32_t* miss_count, int width) {
+  int m = *miss_count;
+  if (m > width) m = width;
+  const int64_t row = c.row_bytes;
+  const int cpr = (int)((row + FETCH_CHUNK - 1) / FETCH_CHUNK);
+  const int64_t items = (int64_t)m * cpr;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && m > 0)
+    c.hdr->counters[CNT_BYTES_FETCHED] += (int64_t)m * row;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int mi = (int)(it / cpr), ch = (int)(it - (int64_t)mi * cpr);
+    const int slot = miss[2 * mi], page = miss[2 * mi + 1];
+    if (slot < 0 || slot >= c.S || page < 0 || (int64_t)page >= c.N) {
+      if (threadIdx.x == 0) set_error(c.hdr, DERR_BAD_MISS);
+      continue;
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * row);
+    u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * row);
+    const int64_t nvec = row / 16;
+    const int64_t v0 = (int64_t)ch * (FETCH_CHUNK / 16) + threadIdx.x;
+    u32x4 buf[FETCH_VEC_PER_THREAD];
+#pragma unroll
+    for (int u = 0; u < FETCH_VEC_PER_THREAD; ++u) {
+      const int64_t v = v0 + (int64_t)u * TKV_BLOCK;
+      if (v < nvec) buf[u] = __builtin_nontemporal_load(src + v);
+    }
+#pragma unroll
+    for (int u = 0; u < FETCH_VEC_PER_THREAD; ++u) {
+      const int64_t v = v0 + (int64_t)u * TKV_BLOCK;
+      if (v < nvec) dst[v] = buf[u];
+    }
+  }
+}
+
+hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(k_fetch, dim3(FETCH_GRID), dim3(TKV_BLOCK), 0, st, c, miss, miss_count, width);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- write-ensure ----
+// Stride samples start, start+PS, ... plus one boundary sample start+len-1
+// per run: every page the run touches is sampled at least once, in page order.
+__global__ void k_write_samples(DevCtx c, int n_runs, const int32_t* run_req, const int32_t* run_start,
+                                const int32_t* run_len, int spr, const int32_t* bt, int max_pages,
+                                const int32_t* old_len) {
+  const int W = n_runs * spr;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < W; j += gridDim.x * blockDim.x) {
+    const int r = j / spr, k = j - r * spr;
+    const int req = run_req[r], start = run_start[r], len = run_len[r];
+    int pos = -1;
+    if (len > 0) {
+      if (k < spr - 1) {
+        if (k * c.PS < len) pos = start + k * c.PS;
+      } else {
+        pos = start + len - 1;
+      }
+    }
+    int needed = -1;
+    uint8_t nf = 0;
+    if (pos >= 0) {
+      const int lp = pos / c.PS;
+      if (lp < max_pages) {
+        needed = bt[(size_t)req * max_pages + lp];
+        nf = (lp * c.PS >= old_len[req]) ? 1 : 0;
+      } else {
+        needed = -2;  // flagged by the ensure as out of range
+      }
+    }
+    c.wneeded[j] = needed;
+    c.wnofetch[j] = nf;
+  }
+}
+
+hipError_t launch_write_ensure(const DevCtx& c, int n_runs, const int32_t* run_req,
+                               const int32_t* run_start, const int32_t* run_len, int spr,
+                               const int32_t* bt, int max_pages, const int32_t* old_len,
+                               hipStream_t st) {
+  const int W = n_runs * spr;
+  hipLaunchKernelGGL(k_write_samples, dim3((W + 255) / 256), dim3(256), 0, st, c, n_runs, run_req,
+                     run_start, run_len, spr, bt, max_pages, old_len);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_ensure(c, c.wneeded, W, c.wnofetch, nullptr, c.wmiss, c.wmiss_count, st);
+  if (e != hipSuccess) return e;
+  return launch_fetch(c, c.wmiss, c.wmiss_count, W, st);
+}
+
+// ---------------------------------------------------------- initialisation --
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void k_fill_u8(uint8_t* p, int64_t n, uint8_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+__global__ void k_iota_i32(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = (int32_t)i;
+}
+__global__ void k_reset_hdr(StateHdr* h) {
+  if (threadIdx.x == 0) {
+    h->clock = 0;
+    for (int i = 0; i < CNT_N; ++i) h->counters[i] = 0;
+    h->error_word = 0;
+    h->parity = 0;
+    h->pad[0] = h->pad[1] = 0;
+  }
+}
+
+static hipError_t fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int g = (int)((n + 255) / 256);
+  if (g > 4096) g = 4096;
+  hipLaunchKernelGGL(k_fill_i32, dim3(g), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_bytes(void* p, int64_t n, uint8_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int g = (int)((n + 255) / 256);
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(k_fill_u8, dim3(g), dim3(256), 0, st, (uint8_t*)p, n, v);
+  return hipGetLastError();
+}
+
+// Empty pool, zero counters.  With full=1 also clear slab, running sums and
+// the chain counters (first attach).
+hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st) {
+  hipError_t e;
+  if ((e = fill_i32(c.page_to_slot, c.N, -1, st)) != hipSuccess) return e;
+  if ((e = fill_i32(c.page_mark, c.N, 0x7FFFFFFF, st)) != hipSuccess) return e;
+  if ((e = fill_i32(c.slot_to_page, c.S, -1, st)) != hipSuccess) return e;
+  if ((e = launch_fill_bytes(c.stamp, (int64_t)c.S * 8, 0, st)) != hipSuccess) return e;
+  if ((e = fill_i32(c.touched, c.S, 0, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_iota_i32, dim3((c.S + 255) / 256), dim3(256), 0, st, c.order, (int64_t)c.S);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_reset_hdr, dim3(1), dim3(64), 0, st, c.hdr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (full) {
+    const int64_t E = (int64_t)c.L * c.N * c.Hkv * c.D;
+    if ((e = launch_fill_bytes(c.slab, E * 2, 0, st)) != hipSuccess) return e;
+    if ((e = launch_fill_bytes(c.slab_acc, E * 4, 0, st)) != hipSuccess) return e;
+    if ((e = fill_i32(c.row_done, c.max_rows, 0, st)) != hipSuccess) return e;
+    if ((e = fill_i32(c.glob_done, 4, 0, st)) != hipSuccess) return e;
+    if ((e = fill_i32(c.attn_done, (int64_t)c.max_batch * c.Hkv, 0, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_iota_i32, dim3((c.max_rows + 256) / 256), dim3(256), 0, st, c.iota, (int64_t)c.max_rows + 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------- codec hooks ----
+__global__ void k_e4m3_encode(const float* in, uint8_t* out, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = (uint8_t)f32_to_e4m3(in[i]);
+}
+__global__ void k_e4m3_decode(const uint8_t* in, float* out, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    f32x2 v = e4m3x2_lo((uint32_t)in[i]);
+    out[i] = v.x;
+  }
+}
+
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int g = (int)((n + 255) / 256);
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(k_e4m3_encode, dim3(g), dim3(256), 0, st, in, out, n);
+  return hipGetLastError();
+}
+hipError_t launch_e4m3_decode(const uint8_t* in, float* out, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int g = (int)((n + 255) / 256);
+  if (g > 8192) g = 8192;
+  hipLaunchKernelGGL(k_e4m3_decode, dim3(g), dim3(256), 0, st, in, out, n);
+  return hipGetLastError();
+}

@@ -1,0 +1,209 @@
+// Device-side LRU ensure, run by one 256-thread workgroup.
+//
+// FreeToken PR #499 ("What", "Design"): the GPU pool is an LRU cache of
+// physical slots over the logical page space; the ensure is device-side and
+// fixed-shape; the mirror is write-through, so evicting a page only rebinds
+// its slot.  Policy (one clock tick per call): distinct needed pages in
+// first-occurrence order; resident pages are hits and get the new stamp; the
+// misses, in first-occurrence order, take the slots not hit by this call in
+// ascending (stamp, slot) order.
+//
+// The (stamp, slot) order is kept incrementally in `order[parity]`: slots not
+// touched by a call keep their relative order and every touched slot gets the
+// newest stamp, so the next order is "untouched slots in old order, then the
+// touched slots by index".  Victims are the first M untouched entries.  Each
+// step is a block-wide scan over the needed list or over the slots, so a call
+// costs O(width + slots) with no sort.
+#pragma once
+#include "tkv_dev.h"
+
+struct EnsureOut {
+  int32_t* out_slots;   // [W] or null
+  int32_t* miss;        // [W][2]
+  int32_t* miss_count;  // [1]
+};
+
+__device__ __forceinline__ bool page_ok(const DevCtx& c, int p) { return p >= 0 && (int64_t)p < c.N; }
+
+__device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
+                                 const uint8_t* no_fetch, EnsureOut o, int* sm_scan) {
+  const int tid = threadIdx.x;
+  const int32_t INTMAX = 0x7FFFFFFF;
+
+  // A: first occurrence of every valid page id (atomicMin of the index)
+  int bad = 0;
+  for (int j = tid; j < W; j += TKV_BLOCK) {
+    int p = needed[j];
+    if (p == -1) continue;
+    if (!page_ok(c, p)) { bad = 1; continue; }
+    atomicMin(&c.page_mark[p], j);
+  }
+  if (bad) set_error(c.hdr, DERR_PAGE_RANGE);
+  __syncthreads();
+
+  // B: distinct pages; the capacity check precedes any state change
+  int local = 0;
+  for (int j = tid; j < W; j += TKV_BLOCK) {
+    int p = needed[j];
+    if (page_ok(c, p) && ld_acquire_i32(&c.page_mark[p]) == j) ++local;
+  }
+  const int distinct = block_sum(local, sm_scan);
+  const int par = c.hdr->parity;
+  const int64_t clock_new = c.hdr->clock + 1;
+
+  if (distinct > c.S) {
+    for (int j = tid; j < W; j += TKV_BLOCK) {
+      int p = needed[j];
+      if (page_ok(c, p)) c.page_mark[p] = INTMAX;
+      if (o.out_slots) o.out_slots[j] = -1;
+    }
+    if (tid == 0) {
+      set_error(c.hdr, DERR_CAPACITY);
+      *o.miss_count = 0;
+    }
+    return;
+  }
+
+  // C: hits are restamped; misses are ranked in first-occurrence order
+  int n_hits = 0;
+  int M = 0;
+  for (int base = 0; base < W; base += TKV_BLOCK) {
+    int j = base + tid;
+    int is_miss = 0;
+    if (j < W) {
+      int p = needed[j];
+      if (page_ok(c, p) && ld_acquire_i32(&c.page_mark[p]) == j) {
+        int s = c.page_to_slot[p];
+        if (s >= 0) {
+          c.touched[s] = 1;
+          c.stamp[s] = clock_new;
+          c.slot_of_j[j] = s;
+          ++n_hits;
+        } else {
+          is_miss = 1;
+        }
+      }
+    }
+    int tot;
+    int ex = block_excl_scan(is_miss, &tot, sm_scan);
+    if (is_miss) c.miss_j[M + ex] = j;
+    M += tot;
+  }
+  __syncthreads();
+
+  // D: victims = the first M slots of the (stamp, slot) order not hit here
+  {
+    int got = 0;
+    const int32_t* ord = c.order + (size_t)par * c.S;
+    for (int base = 0; base < c.S && got < M; base += TKV_BLOCK) {
+      int i = base + tid;
+      int cand = 0, s = 0;
+      if (i < c.S) {
+        s = ord[i];
+        cand = c.touched[s] ? 0 : 1;
+      }
+      int tot;
+      int ex = block_excl_scan(cand, &tot, sm_scan);
+      if (cand && got + ex < M) c.victims[got + ex] = s;
+      got += tot;
+    }
+  }
+  __syncthreads();
+
+  // E: bind each miss to its victim (an evicted page just loses its slot)
+  int n_evict = 0;
+  for (int m = tid; m < M; m += TKV_BLOCK) {
+    int j = c.miss_j[m];
+    int p = needed[j];
+    int s = c.victims[m];
+    int old = c.slot_to_page[s];
+    if (old >= 0) {
+      c.page_to_slot[old] = -1;
+      ++n_evict;
+    }
+    c.page_to_slot[p] = s;
+    c.slot_to_page[s] = p;
+    c.stamp[s] = clock_new;
+    c.touched[s] = 1;
+    c.slot_of_j[j] = s;
+  }
+  __syncthreads();
+
+  // fetch list: misses not marked no_fetch, in first-occurrence order
+  int MF = 0;
+  for (int base = 0; base < M; base += TKV_BLOCK) {
+    int m = base + tid;
+    int f = 0, j = 0;
+    if (m < M) {
+      j = c.miss_j[m];
+      f = (no_fetch && no_fetch[j]) ? 0 : 1;
+    }
+    int tot;
+    int ex = block_excl_scan(f, &tot, sm_scan);
+    if (f) {
+      o.miss[2 * (MF + ex)] = c.slot_of_j[j];
+      o.miss[2 * (MF + ex) + 1] = needed[j];
+    }
+    MF += tot;
+  }
+
+  // F: out_slots (a duplicate reads its first occurrence's slot)
+  for (int j = tid; j < W; j += TKV_BLOCK) {
+    int p = needed[j];
+    int s = -1;
+    if (page_ok(c, p)) s = c.slot_of_j[ld_acquire_i32(&c.page_mark[p])];
+    if (o.out_slots) o.out_slots[j] = s;
+  }
+  __syncthreads();
+  // G: release the first-occurrence marks
+  for (int j = tid; j < W; j += TKV_BLOCK) {
+    int p = needed[j];
+    if (page_ok(c, p)) c.page_mark[p] = INTMAX;
+  }
+
+  // H: next order = untouched slots in old order, then touched slots by index
+  {
+    const int32_t* ord = c.order + (size_t)par * c.S;
+    int32_t* nxt = c.order + (size_t)(1 - par) * c.S;
+    int run = 0;
+    for (int base = 0; base < c.S; base += TKV_BLOCK) {
+      int i = base + tid;
+      int u = 0, s = 0;
+      if (i < c.S) {
+        s = ord[i];
+        u = c.touched[s] ? 0 : 1;
+      }
+      int tot;
+      int ex = block_excl_scan(u, &tot, sm_scan);
+      if (u) nxt[run + ex] = s;
+      run += tot;
+    }
+    __syncthreads();
+    for (int base = 0; base < c.S; base += TKV_BLOCK) {
+      int s = base + tid;
+      int t = (s < c.S) ? c.touched[s] : 0;
+      int tot;
+      int ex = block_excl_scan(t, &tot, sm_scan);
+      if (t) {
+        nxt[run + ex] = s;
+        c.touched[s] = 0;
+      }
+      run += tot;
+    }
+  }
+
+  // I: clock, parity, counters
+  int hits = block_sum(n_hits, sm_scan);
+  int ev = block_sum(n_evict, sm_scan);
+  if (tid == 0) {
+    StateHdr* h = c.hdr;
+    h->clock = clock_new;
+    h->parity = 1 - par;
+    h->counters[CNT_ENSURE] += 1;
+    h->counters[CNT_HITS] += hits;
+    h->counters[CNT_MISSES] += MF;
+    h->counters[CNT_FRESH] += M - MF;
+    h->counters[CNT_EVICT] += ev;
+    *o.miss_count = MF;
+  }
+}

@@ -1,0 +1,292 @@
+// Indexer top-k page selection and compact_selected_pages (gfx950).
+//
+// FreeToken PR #499, "Why this works for sparse attention": each attention
+// step first scores the pages on a compressed key slab that stays on the GPU
+// and keeps the top-k; "Design": compact_selected_pages caps the selection
+// at max_sel_pages = 2*block_topk + 8 and counts what it drops.
+//
+// Decode launch: grid (chunks, rows), 256 threads.  Each workgroup scores
+// CHUNK pages of one row: a wave reads one page's slab row (Hkv*d bf16 =
+// 1 KiB at d=128, Hkv=4) with one 16-byte load per lane, multiplies by the
+// per-group query sum held in registers and reduces across the lanes.  The
+// last workgroup of a row (atomic counter) selects the row's top-k by radix
+// select over the scores; the last row of the call compacts every request
+// and, for the fused decode step, runs the LRU ensure in the same launch.
+//
+// The slab values are bf16 on a 2^-10 grid and the query sums bf16 on a
+// 2^-5 grid, so every product is exact in fp32 and so is every partial sum
+// while sum |q*slab| < 2^9: the scores -- and hence the selections -- do not
+// depend on the summation order.
+#include "tkv_dev.h"
+#include "tkv_launch.h"
+#include "tkv_lru_dev.h"
+
+#define SEL_CHUNK 64
+
+
+
+__device__ __forceinline__ int request_of_row(const int32_t* row_start, int B, int r) {
+  int b = 0;
+  while (b + 1 < B && row_start[b + 1] <= r) ++b;
+  return b;
+}
+
+__device__ __forceinline__ int visible_pages(const SelArgs& a, int PS, int b, int r) {
+  int n = a.n_pages[b];
+  n = n < a.max_pages ? n : a.max_pages;   // never past the block-table row
+  if (n < 0) n = 0;
+  if (a.row_pos) {
+    int pos = a.row_pos[r];
+    int v = pos < 0 ? 0 : pos / PS + 1;
+    n = v < n ? v : n;
+  }
+  return n;
+}
+
+// Top-k of scores[0..visible) (ties -> lower index), ascending, -1 padded.
+__device__ void row_topk_block(const float* scores, int visible, int k, int32_t* out,
+                               uint32_t* keys, int* hist, int* sm_scan, int* sm_misc) {
+  const int tid = threadIdx.x;
+  if (visible <= k) {
+    for (int j = tid; j < k; j += TKV_BLOCK) out[j] = j < visible ? j : -1;
+    return;
+  }
+  for (int i = tid; i < visible; i += TKV_BLOCK) keys[i] = f32_order(scores[i]);
+  uint32_t prefix = 0, mask = 0;
+  int kk = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < visible; i += TKV_BLOCK) {
+      uint32_t key = keys[i];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    // suffix sums from the top digit down: thread t owns digit 255 - t
+    int v = hist[255 - tid];
+    int tot;
+    int ex = block_excl_scan(v, &tot, sm_scan);
+    int incl = ex + v;                           // keys with digit >= 255 - tid
+    if (incl >= kk && ex < kk) {
+      sm_misc[0] = 255 - tid;
+      sm_misc[1] = ex;                           // keys with a strictly larger digit
+    }
+    __syncthreads();
+    uint32_t d = (uint32_t)sm_misc[0];
+    kk -= sm_misc[1];
+    prefix |= d << shift;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;                      // the k-th largest key; kk ties to take
+  const int E = (visible + TKV_BLOCK - 1) / TKV_BLOCK;
+  const int i0 = tid * E, i1 = min(visible, i0 + E);
+  int ties = 0;
+  for (int i = i0; i < i1; ++i) ties += keys[i] == T;
+  int tot;
+  int tie_base = block_excl_scan(ties, &tot, sm_scan);
+  int nsel = 0;
+  {
+    int tr = tie_base;
+    for (int i = i0; i < i1; ++i) {
+      uint32_t key = keys[i];
+      if (key > T) ++nsel;
+      else if (key == T) { if (tr < kk) ++nsel; ++tr; }
+    }
+  }
+  int out_base = block_excl_scan(nsel, &tot, sm_scan);
+  {
+    int tr = tie_base, pos = out_base;
+    for (int i = i0; i < i1; ++i) {
+      uint32_t key = keys[i];
+      bool s = false;
+      if (key > T) s = true;
+      else if (key == T) { s = tr < kk; ++tr; }
+      if (s) out[pos++] = i;
+    }
+  }
+}
+
+// Union of request b's rows, ascending, unique; first C kept, rest counted.
+__device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t* bm, int* sm_scan) {
+  const int tid = threadIdx.x;
+  const int words = (a.max_pages + 31) >> 5;
+  for (int w = tid; w < words; w += TKV_BLOCK) bm[w] = 0;
+  __syncthreads();
+  const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
+  const int total = (r1 - r0) * a.topk;
+  for (int idx = tid; idx < total; idx += TKV_BLOCK) {
+    int i = a.sel_local[(size_t)r0 * a.topk + idx];
+    if (i >= 0 && i < a.max_pages) atomicOr(&bm[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  const int WPT = (words + TKV_BLOCK - 1) / TKV_BLOCK;
+  const int w0 = tid * WPT, w1 = min(words, w0 + WPT);
+  int cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  int u;
+  int pos = block_excl_scan(cnt, &u, sm_scan);
+  int32_t* nd = a.needed + (size_t)b * a.C;
+  const int32_t* btb = a.bt + (size_t)b * a.max_pages;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bm[w];
+    while (bits) {
+      int bit = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < a.C) nd[pos] = btb[(w << 5) + bit];
+      ++pos;
+    }
+  }
+  for (int p = u + tid; p < a.C; p += TKV_BLOCK) nd[p] = -1;
+  if (tid == 0 && u > a.C) c.hdr->counters[CNT_DROPS] += u - a.C;
+  __syncthreads();
+}
+
+// Shared tail: row top-k for row r, then (last row) compaction and ensure.
+__device__ void select_tail(const DevCtx& c, const SelArgs& a, int r, int visible, uint32_t* dyn,
+                            int* hist, int* sm_scan, int* sm_misc) {
+  row_topk_block(c.scores + (size_t)r * c.max_pages, visible, a.topk,
+                 a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
+  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+  for (int b = 0; b < a.B; ++b) compact_block(c, a, b, dyn, sm_scan);
+  if (a.do_ensure) {
+    EnsureOut o{a.out_slots, a.miss, a.miss_count};
+    lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan);
+  }
+}
+
+template <int E8>
+__global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ int hist[256];
+  __shared__ int sm_scan[8];
+  __shared__ int sm_misc[8];
+  __shared__ int sm_b;
+  __shared__ float sm_qg[E8 * 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y, chunk = blockIdx.x;
+  if (tid == 0) sm_b = request_of_row(a.row_start, a.B, r);
+  const int G = c.Hq / c.Hkv;
+  constexpr int E = E8 * 8;  // Hkv * D
+  // per-group query sum: exact (fp64) sum of the group's bf16 heads -> fp32 -> bf16
+  for (int e = tid; e < E; e += TKV_BLOCK) {
+    const int g = e / c.D, dd = e - g * c.D;
+    double acc = 0.0;
+    for (int h = 0; h < G; ++h) acc += (double)bf16_to_f32(a.q[((size_t)r * c.Hq + g * G + h) * c.D + dd]);
+    sm_qg[e] = bf16_to_f32(f32_to_bf16((float)acc));
+  }
+  __syncthreads();
+  const int b = sm_b;
+  const int visible = visible_pages(a, c.PS, b, r);
+
+  constexpr int PPW = E8 >= 64 ? 1 : 64 / E8;       // pages per wave pass
+  constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;        // 16-byte segments per lane
+  constexpr int LANES = E8 >= 64 ? 64 : E8;          // lanes per page
+  constexpr int PASSES = SEL_CHUNK / 4 / PPW;        // wave passes per chunk
+  const int sub = lane / LANES;
+  const int seg0 = lane % LANES;
+  float qg[SPL][8];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qg[s][t] = sm_qg[(seg0 + s * 64) * 8 + t];
+
+  const int p_begin = chunk * SEL_CHUNK;
+  const int p_end = min(visible, p_begin + SEL_CHUNK);
+  const int32_t* btb = a.bt + (size_t)b * a.max_pages;
+  const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
+  float* sc = c.scores + (size_t)r * c.max_pages;
+
+  // all loads of this lane first (memory-level parallelism), then the math
+  int logical[PASSES];
+#pragma unroll
+  for (int it = 0; it < PASSES; ++it) {
+    const int p = p_begin + (it * 4 + wave) * PPW + sub;
+    int lg = -1;
+    if (p < p_end) lg = btb[p];
+    logical[it] = ((int64_t)lg >= 0 && (int64_t)lg < c.N) ? lg : -1;
+  }
+  uint4 v[PASSES][SPL];
+#pragma unroll
+  for (int it = 0; it < PASSES; ++it) {
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      if (logical[it] >= 0) v[it][s] = reinterpret_cast<const uint4*>(slab_l + (size_t)logical[it] * E)[seg0 + s * 64];
+      else v[it][s] = make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < PASSES; ++it) {
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      const uint32_t w[4] = {v[it][s].x, v[it][s].y, v[it][s].z, v[it][s].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        part += qg[s][2 * t] * __uint_as_float(w[t] << 16);
+        part += qg[s][2 * t + 1] * __uint_as_float(w[t] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int o = LANES / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    const int p = p_begin + (it * 4 + wave) * PPW + sub;
+    if (p < p_end && seg0 == 0) {
+      float key = part;
+      if (logical[it] < 0) key = -INFINITY;
+      else if (a.bias) key = key + a.bias[logical[it]];
+      sc[p] = key;
+    }
+  }
+  if (!last_block_arrive(&c.row_done[r], a.n_chunks, &sm_misc[4])) return;
+  select_tail(c, a, r, visible, dyn, hist, sm_scan, sm_misc);
+}
+
+// Tail-only launch: scores already in the workspace (prefill scoring kernel).
+__global__ __launch_bounds__(TKV_BLOCK) void k_select_rows(DevCtx c, SelArgs a) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ int hist[256];
+  __shared__ int sm_scan[8];
+  __shared__ int sm_misc[8];
+  __shared__ int sm_b;
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0) sm_b = request_of_row(a.row_start, a.B, r);
+  __syncthreads();
+  select_tail(c, a, r, visible_pages(a, c.PS, sm_b, r), dyn, hist, sm_scan, sm_misc);
+}
+
+__global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* needed, int W,
+                                                      const uint8_t* no_fetch, EnsureOut o) {
+  __shared__ int sm_scan[8];
+  lru_ensure_block(c, needed, W, no_fetch, o, sm_scan);
+}
+
+// ------------------------------------------------------------------ launchers --
+size_t select_dyn_lds(const DevCtx& c) {
+  size_t keys = (size_t)c.max_pages * 4;
+  size_t bm = (size_t)((c.max_pages + 31) / 32) * 4;
+  return keys > bm ? keys : bm;
+}
+
+hipError_t launch_select_scan(const DevCtx& c, const SelArgs& a, hipStream_t st) {
+  dim3 grid(a.n_chunks, a.rows);
+  size_t lds = select_dyn_lds(c);
+  const int E8 = c.Hkv * c.D / 8;
+  if (E8 == 64) hipLaunchKernelGGL(k_select_scan<64>, grid, dim3(TKV_BLOCK), lds, st, c, a);
+  else if (E8 == 16) hipLaunchKernelGGL(k_select_scan<16>, grid, dim3(TKV_BLOCK), lds, st, c, a);
+  else if (E8 == 32) hipLaunchKernelGGL(k_select_scan<32>, grid, dim3(TKV_BLOCK), lds, st, c, a);
+  else if (E8 == 128) hipLaunchKernelGGL(k_select_scan<128>, grid, dim3(TKV_BLOCK), lds, st, c, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_select_rows(const DevCtx& c, const SelArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_select_rows, dim3(a.rows), dim3(TKV_BLOCK), select_dyn_lds(c), st, c, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ensure(const DevCtx& c, const int32_t* needed, int W, const uint8_t* no_fetch,
+                         int32_t* out_slots, int32_t* miss, int32_t* miss_count, hipStream_t st) {
+  EnsureOut o{out_slots, miss, miss_count};
+  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(TKV_BLOCK), 0, st, c, needed, W, no_fetch, o);
+  return hipGetLastError();
+}

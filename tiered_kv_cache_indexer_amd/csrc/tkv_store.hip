@@ -1,0 +1,186 @@
+// store_kv with the write-through mirror (gfx950).
+//
+// FreeToken PR #499, "Design": every store_kv is mirrored to the pinned host
+// bank over the unified address space, so a GPU slot is always drop-clean.
+// PR #525 commit summary (mirror_store_quant): the mirror takes the e4m3
+// codes and fp32 scales AFTER quantisation -- the pool is the source of truth.
+//
+// One workgroup per (run, page of the run).  A wave quantises one token at a
+// time: each lane holds 8 of the token's Hkv*d bf16 values (one 16-byte
+// load), the wave reduces |x| to the token's amax, scale = amax/448 (1 if
+// amax is 0), code = e4m3(x / scale) with a correctly rounded fp32 division.
+// The same 8 code bytes go to the pool slot (HBM) and to the mirror row
+// (posted writes over the host link).  The workgroup also sums the page's
+// keys for the indexer slab: slab = bf16(running sum / tokens written).
+#include "tkv_dev.h"
+#include "tkv_launch.h"
+
+
+
+template <int E8, bool FP8>
+__global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
+  constexpr int E = E8 * 8;
+  constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;
+  __shared__ float ksum_w[4][E];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x, j = blockIdx.y;
+  const int PS = c.PS, D = c.D;
+  const int req = a.run_req[r], start = a.run_start[r], len = a.run_len[r];
+  if (len <= 0) return;
+  const int lp = start / PS + j;
+  const int t0 = max(start, lp * PS), t1 = min(start + len, (lp + 1) * PS);
+  if (t0 >= t1) return;
+  if (lp >= a.max_pages) {
+    if (tid == 0) set_error(c.hdr, DERR_PAGE_RANGE);
+    return;
+  }
+  const int off = t0 - lp * PS, n = t1 - t0;
+  const int page = a.bt[(size_t)req * a.max_pages + lp];
+  if (page < 0 || (int64_t)page >= c.N) {
+    if (tid == 0) set_error(c.hdr, DERR_PAGE_RANGE);
+    return;
+  }
+  const int slot = c.page_to_slot[page];
+  if (slot < 0 && tid == 0) set_error(c.hdr, DERR_NOT_RESIDENT);
+  uint8_t* mir = c.mirror + (size_t)page * c.row_bytes + (size_t)a.layer * c.layer_bytes;
+  uint8_t* pol = slot >= 0 ? c.pool + (size_t)slot * c.row_bytes + (size_t)a.layer * c.layer_bytes : nullptr;
+  const size_t cb = (size_t)c.code_bytes;
+  const int tok0 = a.run_tok_off[r] + (t0 - start);
+
+  float ksum[SPL][8];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ksum[s][t] = 0.f;
+
+  for (int tt = wave; tt < n; tt += 4) {
+    const int pos = off + tt;  // position within the page
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = (kv == 0 ? a.k : a.v) + (size_t)(tok0 + tt) * E;
+      float x[SPL][8];
+      bool act[SPL];
+      float amax = 0.f;
+#pragma unroll
+      for (int s = 0; s < SPL; ++s) {
+        const int seg = lane + s * 64;
+        act[s] = seg < E8;
+        uint4 w = act[s] ? reinterpret_cast<const uint4*>(src)[seg] : make_uint4(0, 0, 0, 0);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          x[s][2 * t] = __uint_as_float(ww[t] << 16);
+          x[s][2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(x[s][t]));
+        if (kv == 0)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) ksum[s][t] += x[s][t];
+      }
+      uint8_t* mblk = mir + kv * cb;
+      uint8_t* pblk = pol ? pol + kv * cb : nullptr;
+      if (FP8) {
+        amax = wave_max(amax);
+        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          if (!act[s]) continue;
+          const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) lo |= f32_to_e4m3(x[s][t] / scale) << (8 * t);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) hi |= f32_to_e4m3(x[s][4 + t] / scale) << (8 * t);
+          const size_t o = ((size_t)h * PS + pos) * D + dd;
+          const uint2 val = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(mblk + o) = val;
+          if (pblk) *reinterpret_cast<uint2*>(pblk + o) = val;
+        }
+        if (lane == 0) {
+          const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
+          *reinterpret_cast<float*>(mir + so) = scale;
+          if (pol) *reinterpret_cast<float*>(pol + so) = scale;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          if (!act[s]) continue;
+          const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
+          const uint4 w = reinterpret_cast<const uint4*>(src)[lane + s * 64];
+          const size_t o = (((size_t)h * PS + pos) * D + dd) * 2;
+          *reinterpret_cast<uint4*>(mblk + o) = w;
+          if (pblk) *reinterpret_cast<uint4*>(pblk + o) = w;
+        }
+      }
+    }
+  }
+
+  // a write that begins the page clears the page's later positions
+  if (off == 0 && n < PS) {
+    const int elt = FP8 ? 1 : 2;
+    const int H = c.Hkv;
+    const int tail = (PS - n) * D * elt;  // bytes per head
+    for (int kv = 0; kv < 2; ++kv)
+      for (int h = 0; h < H; ++h) {
+        const size_t base = (size_t)kv * cb + ((size_t)h * PS + n) * D * elt;
+        for (int i = tid * 4; i < tail; i += TKV_BLOCK * 4) {
+          *reinterpret_cast<uint32_t*>(mir + base + i) = 0u;
+          if (pol) *reinterpret_cast<uint32_t*>(pol + base + i) = 0u;
+        }
+      }
+    if (FP8) {
+      for (int i = n + tid; i < PS; i += TKV_BLOCK) {
+        reinterpret_cast<float*>(mir + 2 * cb)[i] = 0.f;
+        reinterpret_cast<float*>(mir + 2 * cb + PS * 4)[i] = 0.f;
+        if (pol) {
+          reinterpret_cast<float*>(pol + 2 * cb)[i] = 0.f;
+          reinterpret_cast<float*>(pol + 2 * cb + PS * 4)[i] = 0.f;
+        }
+      }
+    }
+  }
+
+  // slab: mean of every key written to this page so far
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) {
+    const int seg = lane + s * 64;
+    if (seg < E8)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ksum_w[wave][seg * 8 + t] = ksum[s][t];
+  }
+  __syncthreads();
+  const size_t sbase = ((size_t)a.layer * c.N + page) * E;
+  const int cnt = off + n;
+  for (int e = tid; e < E; e += TKV_BLOCK) {
+    float sum = (ksum_w[0][e] + ksum_w[1][e]) + (ksum_w[2][e] + ksum_w[3][e]);
+    if (off > 0) sum += c.slab_acc[sbase + e];
+    c.slab_acc[sbase + e] = sum;
+    c.slab[sbase + e] = f32_to_bf16(sum / (float)cnt);
+  }
+  if (tid == 0) {
+    const int64_t tok_bytes = c.layer_bytes / PS;
+    const int64_t nb = (int64_t)(n + (off == 0 ? PS - n : 0)) * tok_bytes;
+    atomicAdd((unsigned long long*)&c.hdr->counters[CNT_BYTES_MIRRORED], (unsigned long long)nb);
+  }
+}
+
+hipError_t launch_store(const DevCtx& c, const StoreArgs& a, int max_run_len, hipStream_t st) {
+  const int ppr = (max_run_len + c.PS - 1) / c.PS + 1;
+  dim3 grid(a.n_runs, ppr);
+  const int E8 = c.Hkv * c.D / 8;
+  if (c.fp8) {
+    if (E8 == 64) hipLaunchKernelGGL((k_store<64, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (E8 == 64) hipLaunchKernelGGL((k_store<64, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
