@@ -44,6 +44,7 @@ class OracleTier:
         self.mirror = {}                      # page -> uint8 row
         self.pool = (np.zeros((self.S, self.lay.row_bytes), dtype=np.uint8)
                      if materialize else None)
+        self._lazy_pool = {}                  # slot -> (page, row copied by the fetch)
         self.slab = np.zeros((self.L, self.N, self.Hkv, self.d), dtype=np.float32)
         self._partial_sums = {}               # (layer, page) -> fp64 key sum of a partly written page
         self.written = np.zeros(self.N, dtype=np.int64)   # tokens written per page (layer 0)
@@ -66,6 +67,7 @@ class OracleTier:
 
     def reset_residency(self):
         self.lru.reset()
+        self._lazy_pool.clear()
         self.drops = self.bytes_fetched = self.bytes_mirrored = 0
 
     # ------------------------------------------------------------ rows ----
@@ -80,6 +82,9 @@ class OracleTier:
         if self.materialize:
             return self.pool[slot]
         page = int(self.lru.slot_to_page[slot])
+        held = self._lazy_pool.get(slot)
+        if held is not None and held[0] == page:
+            return held[1]
         return self.row_builder(page)
 
     # ------------------------------------------------------------ write ---
@@ -162,6 +167,8 @@ class OracleTier:
         for slot, page in np.asarray(misses).reshape(-1, 2):
             if self.materialize:
                 self.pool[slot][:] = self.mirror_row(int(page))
+            else:
+                self._lazy_pool[int(slot)] = (int(page), self.mirror_row(int(page)).copy())
             self.bytes_fetched += self.lay.row_bytes
 
     def gather_kv(self, layer, b, sel_row, block_table, ctx_len, row_pos=None):
