@@ -53,7 +53,7 @@ struct Layout {
   // state offsets
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
-  size_t ws_scores, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
+  size_t ws_scores, ws_sel_slots, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
       ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_total;
 };
 
@@ -113,7 +113,8 @@ static Layout make_layout(const tkv_config* c) {
   L.st_total = o;
   const size_t W = c->max_width, R = c->max_rows, P = c->max_pages_per_req;
   o = 0;
-  L.ws_scores = o; o = align256(o + R * P * 4);
+  L.ws_scores = o; o = align256(o + R * ((P + 63) / 64) * 64 * 8);
+  L.ws_sel_slots = o; o = align256(o + R * (size_t)c->max_topk * 4);
   L.ws_row_done = o; o = align256(o + R * 4);
   L.ws_glob = o; o = align256(o + 16);
   L.ws_slot_of_j = o; o = align256(o + W * 4);
@@ -123,7 +124,7 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_wnofetch = o; o = align256(o + W);
   L.ws_wmiss = o; o = align256(o + W * 8);
   L.ws_wmiss_count = o; o = align256(o + 4);
-  L.ws_part = o; o = align256(o + (size_t)c->max_batch * c->num_q_heads * c->max_topk * (D + 2) * 4);
+  L.ws_part = o; o = align256(o + (size_t)c->max_batch * c->num_q_heads * c->max_topk * (D + 4) * 4);
   L.ws_attn_done = o; o = align256(o + (size_t)c->max_batch * H * 4);
   L.ws_iota = o; o = align256(o + (R + 1) * 4);
   L.ws_total = o;
@@ -219,6 +220,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.slab_acc = (float*)(st + L.st_acc);
   uint8_t* ws = (uint8_t*)b->workspace;
   d.scores = (float*)(ws + L.ws_scores);
+  d.sel_slots = (int32_t*)(ws + L.ws_sel_slots);
   d.row_done = (int32_t*)(ws + L.ws_row_done);
   d.glob_done = (int32_t*)(ws + L.ws_glob);
   d.slot_of_j = (int32_t*)(ws + L.ws_slot_of_j);
@@ -357,7 +359,7 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
   if (rc) return rc;
   if ((rc = check_rows(c, layer, B, B, max_pages, topk))) return rc;
   if (!c->C) return fail(TKV_E_STATE, "select width not set (tkv_set_select_width)");
-  if (!q || !block_table || !n_pages || !ctx_len || !sel_local || !needed || !miss || !miss_count || !out)
+  if (!q || !block_table || !n_pages || !ctx_len || !sel_local || !needed || !out_slots || !miss || !miss_count || !out)
     return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
   if ((int64_t)B * c->C > c->cfg.max_width || (int64_t)B * c->C > c->cfg.num_slots)
     return fail(TKV_E_CAPACITY, "B*max_sel_pages=%lld exceeds num_slots or max_width", (long long)B * c->C);
@@ -368,12 +370,14 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
   a.out_slots = out_slots;
   a.miss = miss;
   a.miss_count = miss_count;
+  a.sel_slots = c->dev.sel_slots;
   HIPCHECK(launch_select_scan(c->dev, a, s), "decode select+ensure launch");
   HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
   AttnArgs t{};
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
   t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
   t.B = B; t.out = out;
+  t.slots = c->dev.sel_slots;
   HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");
   return TKV_OK;
 }

@@ -69,7 +69,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
   for (int jj = tid; jj < np && jj < ATT_MAXP; jj += TKV_BLOCK) {
     const int i = a.sel[(size_t)r * a.topk + j0 + jj];
     int slot = -1, nt = 0;
-    if (i >= 0 && i < a.max_pages) {
+    if (a.slots) {
+      const int s = a.slots[(size_t)r * a.topk + j0 + jj];
+      if (i >= 0 && s >= 0 && s < c.S) {
+        slot = s;
+        nt = min(PS, limit - i * PS);
+      }
+    } else if (i >= 0 && i < a.max_pages) {
       const int page = a.bt[(size_t)b * a.max_pages + i];
       if (page >= 0 && (int64_t)page < c.N) slot = c.page_to_slot[page];
       nt = min(PS, limit - i * PS);
@@ -245,8 +251,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
     }
     return;
   }
-  // partial record: [r][h][split] -> o[D], m, l
-  const int REC = D + 2;
+  // partial record: [r][h][split] -> o[D], m, l (16-byte aligned records)
+  constexpr int REC = D + 4;
   if (half == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -256,27 +262,49 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
     }
   }
   if (!last_block_arrive(&c.attn_done[r * c.Hkv + g], a.splits, &sflag[0])) return;
-  // merge splits: thread = (head, 4 d values)
+  // merge the splits: thread = (head, 4 d values); every load of a pass is
+  // independent so the whole pass is one memory round trip
   {
     const int h = tid / 32, d0 = (tid % 32) * 4;
     const float* base = c.attn_part + ((size_t)r * c.Hq + g * G + h) * a.splits * REC;
+    const int S = a.splits;
     float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, base[(size_t)s * REC + D]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float mv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mv[u] = (s0 + u < S) ? base[(size_t)(s0 + u) * REC + D] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) M = fmaxf(M, mv[u]);
+    }
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     if (M != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float* rec = base + (size_t)s * REC;
-        const float m = rec[D];
-        if (m == -INFINITY) continue;
-        const float w = exp2f(m - M);
-        L += rec[D + 1] * w;
-        o0 += rec[d0] * w; o1 += rec[d0 + 1] * w; o2 += rec[d0 + 2] * w; o3 += rec[d0 + 3] * w;
+      for (int s0 = 0; s0 < S; s0 += 16) {
+        float4 ov[16];
+        float2 ml[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (s0 + u < S) {
+            const float* rec = base + (size_t)(s0 + u) * REC;
+            ov[u] = *reinterpret_cast<const float4*>(rec + d0);
+            ml[u] = *reinterpret_cast<const float2*>(rec + D);
+          } else {
+            ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            ml[u] = make_float2(-INFINITY, 0.f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float w = (ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
+          L += ml[u].y * w;
+          o.x += ov[u].x * w; o.y += ov[u].y * w; o.z += ov[u].z * w; o.w += ov[u].w * w;
+        }
       }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t* op = a.out + ((size_t)r * c.Hq + g * G + h) * D + d0;
-    op[0] = f32_to_bf16(o0 * inv); op[1] = f32_to_bf16(o1 * inv);
-    op[2] = f32_to_bf16(o2 * inv); op[3] = f32_to_bf16(o3 * inv);
+    op[0] = f32_to_bf16(o.x * inv); op[1] = f32_to_bf16(o.y * inv);
+    op[2] = f32_to_bf16(o.z * inv); op[3] = f32_to_bf16(o.w * inv);
   }
 }
 

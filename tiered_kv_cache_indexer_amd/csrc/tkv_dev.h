@@ -43,7 +43,8 @@ struct DevCtx {
   int32_t* order;           // [2][S] slots in ascending (stamp, slot)
   int32_t* touched;         // [S]
   // workspace
-  float* scores;            // [max_rows][max_pages]
+  float* scores;            // [max_rows][max_pages rounded to 64] x 8 bytes: float scores or 64-bit keys
+  int32_t* sel_slots;       // [max_rows][max_topk] slots of the selected pages (fused decode)
   int32_t* row_done;        // [max_rows] last-block counters (kept at zero between calls)
   int32_t* glob_done;       // [4]
   int32_t* slot_of_j;       // [max_width]
@@ -80,6 +81,7 @@ struct SelArgs {
   int32_t* out_slots;
   int32_t* miss;
   int32_t* miss_count;
+  int32_t* sel_slots;   // fused path: translated slots of sel_local (or null)
 };
 
 struct StoreArgs {
@@ -108,6 +110,7 @@ struct AttnArgs {
   int topk;
   int B;
   uint16_t* out;
+  const int32_t* slots;  // optional: slots of sel (skips the page->slot translation)
   int splits;
   int pages_per_split;
 };
@@ -150,6 +153,71 @@ __device__ __forceinline__ uint32_t f32_order(float f) {
   if (f == 0.0f) f = 0.0f;
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------ wave sorting --
+// 64-bit selection keys: (orderable score << 32) | ~index -- a larger key is a
+// higher score, and among equal scores the lower index.  0 = no page.
+__device__ __forceinline__ uint64_t sel_key(float score, int idx) {
+  return ((uint64_t)f32_order(score) << 32) | (uint64_t)(~(uint32_t)idx);
+}
+__device__ __forceinline__ int sel_key_index(uint64_t k) { return (int)(~(uint32_t)k); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Bitonic sort of one key per lane across a wave, descending (lane 0 = max).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0;
+      const bool keep_max = (lower == desc);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
+// Top 64 of two descending lists, descending.
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t a, uint64_t b) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t br = shfl_u64(b, 63 - lane);
+  uint64_t v = a > br ? a : br;   // bitonic, holds the top 64
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, stride);
+    const bool lower = (lane & stride) == 0;
+    v = lower ? (v > o ? v : o) : (v < o ? v : o);
+  }
+  return v;
+}
+
+// Bitonic sort of one int per lane, ascending.
+__device__ __forceinline__ int wave_sort_asc_i32(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int o = __shfl_xor(v, stride, 64);
+      const bool lower = (lane & stride) == 0;
+      const bool asc = (lane & size) == 0;
+      const bool keep_min = (lower == asc);
+      v = keep_min ? min(v, o) : max(v, o);
+    }
+  }
+  return v;
 }
 
 // ------------------------------------------------------------------ block ops --
@@ -212,17 +280,24 @@ __device__ __forceinline__ void set_error(StateHdr* h, int bits) {
 // Last-block election: every block calls it once after publishing its
 // results; returns true in exactly one block (the last to arrive), after
 // which that block sees every other block's writes.  The counter is reset.
+// Each wave first drains its own memory operations (so its stores have
+// reached L2), then one thread per block makes the block's writes visible
+// device-wide (agent-scope release: L2 writeback) before counting in, and the
+// last block's thread 0 acquires (L1/L2 invalidate) for the whole block --
+// one fence per block instead of one per thread.
 __device__ __forceinline__ bool last_block_arrive(int32_t* counter, int expected, int* sm_flag) {
-  __threadfence();  // every thread: its global writes are visible device-wide
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (old == expected - 1);
-    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old == expected - 1);
+    if (last) {
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
     *sm_flag = last;
   }
   __syncthreads();
-  bool last = *sm_flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *sm_flag != 0;
 }

@@ -107,6 +107,37 @@ __device__ void row_topk_block(const float* scores, int visible, int k, int32_t*
   }
 }
 
+// Row top-k for k <= 64 (wave bitonic): each wave folds a share of the
+// row's sorted 64-key lists into its running top-64 list, the four wave lists
+// are merged through LDS, and wave 0 writes the first k indices ascending.
+// `load_list(c)` returns chunk c's sorted list in this lane.
+template <typename LoadList>
+__device__ void row_topk64_block(int n_lists, int k, int32_t* out, uint64_t* lds64, LoadList load_list) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int BATCH = 8;   // lists loaded per wave before merging (loads in flight together)
+  uint64_t run = 0;
+  for (int base = wave; base < n_lists; base += 4 * BATCH) {
+    uint64_t v[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int c = base + 4 * u;
+      v[u] = c < n_lists ? load_list(c) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) run = (base == wave && u == 0) ? v[u] : wave_merge_desc(run, v[u]);
+  }
+  lds64[wave * 64 + lane] = run;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) run = wave_merge_desc(run, lds64[w * 64 + lane]);
+    int idx = (lane < k && run != 0) ? sel_key_index(run) : 0x7FFFFFFF;
+    idx = wave_sort_asc_i32(idx);
+    if (lane < k) out[lane] = idx == 0x7FFFFFFF ? -1 : idx;
+  }
+  __syncthreads();
+}
+
 // Union of request b's rows, ascending, unique; first C kept, rest counted.
 __device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t* bm, int* sm_scan) {
   const int tid = threadIdx.x;
@@ -142,22 +173,45 @@ __device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t
   __syncthreads();
 }
 
-// Shared tail: row top-k for row r, then (last row) compaction and ensure.
-__device__ void select_tail(const DevCtx& c, const SelArgs& a, int r, int visible, uint32_t* dyn,
-                            int* hist, int* sm_scan, int* sm_misc) {
-  row_topk_block(c.scores + (size_t)r * c.max_pages, visible, a.topk,
-                 a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
-  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+// After the ensure: translated slots of every row's selection (fused decode).
+// A request with one row whose selection fits the compaction width has
+// needed[b][j] = block_table[b][sel[j]], so its slots are the ensure's
+// out_slots[b*C + j]; other requests translate through the page->slot map.
+__device__ void write_sel_slots(const DevCtx& c, const SelArgs& a) {
+  for (int b = 0; b < a.B; ++b) {
+    const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
+    const bool direct = (r1 - r0 == 1) && (a.topk <= a.C);
+    const int32_t* btb = a.bt + (size_t)b * a.max_pages;
+    for (int idx = threadIdx.x; idx < (r1 - r0) * a.topk; idx += TKV_BLOCK) {
+      const int i = a.sel_local[(size_t)r0 * a.topk + idx];
+      int slot = -1;
+      if (i >= 0 && i < a.max_pages) {
+        if (direct) {
+          slot = a.out_slots[(size_t)b * a.C + idx];
+        } else {
+          const int p = btb[i];
+          if (p >= 0 && (int64_t)p < c.N) slot = c.page_to_slot[p];
+        }
+      }
+      a.sel_slots[(size_t)r0 * a.topk + idx] = slot;
+    }
+  }
+}
+
+// Shared tail once every row's selection is written: compaction and ensure.
+__device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan) {
   for (int b = 0; b < a.B; ++b) compact_block(c, a, b, dyn, sm_scan);
   if (a.do_ensure) {
     EnsureOut o{a.out_slots, a.miss, a.miss_count};
     lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan);
+    __syncthreads();
+    if (a.sel_slots) write_sel_slots(c, a);
   }
 }
 
 template <int E8>
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) {
-  extern __shared__ uint32_t dyn[];
+  extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ int hist[256];
   __shared__ int sm_scan[8];
   __shared__ int sm_misc[8];
@@ -199,6 +253,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
 
   // all loads of this lane first (memory-level parallelism), then the math
   int logical[PASSES];
+  float keys[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     const int p = p_begin + (it * 4 + wave) * PPW + sub;
@@ -229,29 +284,65 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     }
 #pragma unroll
     for (int o = LANES / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    const int p = p_begin + (it * 4 + wave) * PPW + sub;
-    if (p < p_end && seg0 == 0) {
-      float key = part;
-      if (logical[it] < 0) key = -INFINITY;
-      else if (a.bias) key = key + a.bias[logical[it]];
-      sc[p] = key;
+    float key = part;
+    if (logical[it] < 0) key = -INFINITY;
+    else if (a.bias) key = key + a.bias[logical[it]];
+    keys[it] = key;
+  }
+  uint64_t* cand = reinterpret_cast<uint64_t*>(c.scores) + (size_t)r * a.n_chunks * 64;
+  if (a.topk <= 64) {
+    // this chunk's 64 pages as one sorted list
+    __shared__ uint64_t sm_keys[64];
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int p = p_begin + (it * 4 + wave) * PPW + sub;
+      if (seg0 == 0) sm_keys[p - p_begin] = (p < p_end) ? sel_key(keys[it], p) : 0ull;
+    }
+    __syncthreads();
+    if (wave == 0) cand[(size_t)chunk * 64 + lane] = wave_sort_desc(sm_keys[lane]);
+  } else {
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int p = p_begin + (it * 4 + wave) * PPW + sub;
+      if (p < p_end && seg0 == 0) sc[p] = keys[it];
     }
   }
   if (!last_block_arrive(&c.row_done[r], a.n_chunks, &sm_misc[4])) return;
-  select_tail(c, a, r, visible, dyn, hist, sm_scan, sm_misc);
+  if (a.topk <= 64) {
+    row_topk64_block(a.n_chunks, a.topk, a.sel_local + (size_t)r * a.topk, reinterpret_cast<uint64_t*>(dyn),
+                     [&](int ch) { return cand[(size_t)ch * 64 + lane]; });
+  } else {
+    row_topk_block(c.scores + (size_t)r * c.max_pages, visible, a.topk, a.sel_local + (size_t)r * a.topk,
+                   dyn, hist, sm_scan, sm_misc);
+  }
+  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+  select_finish(c, a, dyn, sm_scan);
 }
 
 // Tail-only launch: scores already in the workspace (prefill scoring kernel).
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows(DevCtx c, SelArgs a) {
-  extern __shared__ uint32_t dyn[];
+  extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ int hist[256];
   __shared__ int sm_scan[8];
   __shared__ int sm_misc[8];
   __shared__ int sm_b;
-  const int r = blockIdx.x;
+  const int r = blockIdx.x, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sm_b = request_of_row(a.row_start, a.B, r);
   __syncthreads();
-  select_tail(c, a, r, visible_pages(a, c.PS, sm_b, r), dyn, hist, sm_scan, sm_misc);
+  const int visible = visible_pages(a, c.PS, sm_b, r);
+  const float* sc = c.scores + (size_t)r * c.max_pages;
+  if (a.topk <= 64) {
+    const int n_lists = (visible + 63) / 64;
+    row_topk64_block(n_lists, a.topk, a.sel_local + (size_t)r * a.topk, reinterpret_cast<uint64_t*>(dyn),
+                     [&](int ch) {
+                       const int p = ch * 64 + lane;
+                       return wave_sort_desc(p < visible ? sel_key(sc[p], p) : 0ull);
+                     });
+  } else {
+    row_topk_block(sc, visible, a.topk, a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
+  }
+  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+  select_finish(c, a, dyn, sm_scan);
 }
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* needed, int W,
@@ -264,7 +355,9 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* n
 size_t select_dyn_lds(const DevCtx& c) {
   size_t keys = (size_t)c.max_pages * 4;
   size_t bm = (size_t)((c.max_pages + 31) / 32) * 4;
-  return keys > bm ? keys : bm;
+  size_t lists = 4 * 64 * 8;
+  size_t m = keys > bm ? keys : bm;
+  return m > lists ? m : lists;
 }
 
 hipError_t launch_select_scan(const DevCtx& c, const SelArgs& a, hipStream_t st) {
