@@ -23,7 +23,7 @@ import numpy as np
 from .attention import attend
 from .layout import RowLayout
 from .lru import LRUState
-from .select import compact_request, select_row
+from .select import compact_request, select_row, select_rows
 from .store import read_kv, slab_entry, write_tokens
 
 ERR_NOT_RESIDENT = 4      # store to a page that is not resident (pool not written)
@@ -146,7 +146,14 @@ class OracleTier:
         rows = q.shape[0]
         sel = np.full((rows, topk), -1, dtype=np.int32)
         for b in range(B):
-            for r in range(row_start[b], row_start[b + 1]):
+            r0, r1 = int(row_start[b]), int(row_start[b + 1])
+            if r1 - r0 > 8:
+                pos = None if row_pos is None else np.asarray(row_pos[r0:r1])
+                sel[r0:r1], cert = select_rows(q[r0:r1], self.slab[layer], block_table[b], int(n_pages[b]),
+                                               topk, self.Hkv, bias, pos, self.ps)
+                self.max_certificate = max(self.max_certificate, cert)
+                continue
+            for r in range(r0, r1):
                 pos = None if row_pos is None else int(row_pos[r])
                 sel[r], cert = select_row(q[r], self.slab[layer], block_table[b], int(n_pages[b]),
                                           topk, self.Hkv, bias, pos, self.ps)

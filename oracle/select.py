@@ -87,6 +87,27 @@ def select_row(q_row: np.ndarray, slab_layer: np.ndarray, block_row: np.ndarray,
     return topk_pages(keys, visible, k), score_certificate(qg, slab_pages)
 
 
+def select_rows(q_rows: np.ndarray, slab_layer: np.ndarray, block_row: np.ndarray, n_pages: int,
+                k: int, num_kv_heads: int, bias=None, row_pos=None, page_size: int = 64):
+    """Many rows of one request: the same definition as ``select_row``, with
+    the scores of all rows against all pages as one fp64 matrix product.
+    Returns (sel_local int32 [rows][k], certificate)."""
+    rows = q_rows.shape[0]
+    qg = np.stack([group_query(q_rows[r], num_kv_heads) for r in range(rows)])   # [rows][Hkv][d]
+    logical = block_row[:n_pages].astype(np.int64)
+    slab_pages = slab_layer[logical].astype(np.float64).reshape(n_pages, -1)
+    qmat = qg.astype(np.float64).reshape(rows, -1)
+    scores = qmat @ slab_pages.T                                                   # exact on the grids
+    cert = float((np.abs(qmat) @ np.abs(slab_pages).T).max()) if n_pages else 0.0
+    bias_pages = None if bias is None else bias[logical]
+    out = np.full((rows, k), -1, dtype=np.int32)
+    for r in range(rows):
+        visible = n_pages if row_pos is None else min(n_pages, int(row_pos[r]) // page_size + 1)
+        keys = keys_from_scores(scores[r, :visible], None if bias_pages is None else bias_pages[:visible])
+        out[r] = topk_pages(keys, visible, k)
+    return out, cert
+
+
 def compact_request(sel_rows: np.ndarray, block_row: np.ndarray, cap: int):
     """Union of one request's selections -> (needed logical ids int32 [cap],
     drops).  Ascending local ids, unique, first `cap` kept, -1 padded."""

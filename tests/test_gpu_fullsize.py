@@ -1,0 +1,108 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (fused decode_layer per layer, eager launches on one stream).
+
+Exact for every layer of the steps run: selections, compaction, slot maps,
+miss lists, LRU state and counters; the slab of every page; attention on
+sampled layers (every head of every row); mirror and pool bytes on sampled
+pages.  The oracle keeps no page bytes at these sizes: it rebuilds a page's
+row from the input generator when a sampled check reads it.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import run
+from workload import gen, get_workload
+
+from tests.gpu_compare import assert_close, bf16_to_f64, compare_state, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_fullsize(key, steps, attn_layers):
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload(key)
+    say(f"[fullsize] {key}: {wl.description}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    say(f"[fullsize] {key}: gpu setup done")
+    o = run.make_tier(wl, materialize=False)
+    run.setup(wl, o)
+    say(f"[fullsize] {key}: oracle setup done")
+    rng = np.random.default_rng(7)
+    sample_pages = sorted(set(rng.integers(0, wl.num_logical_pages, 6).tolist()))
+    compare_state(g, o, f"{key} after setup", sample_pages=sample_pages)
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    for s in range(steps):
+        g.decode_step(s)
+        torch.cuda.synchronize()
+        for layer in range(wl.num_layers):
+            where = f"{key} step {s} layer {layer}"
+            with_attn = layer in attn_layers
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias,
+                                 with_attention=with_attn)
+            assert np.array_equal(g.sel[layer].cpu().numpy(), rec["sel"]), f"{where}: sel"
+            assert np.array_equal(g.needed[layer].cpu().numpy(), rec["needed"]), f"{where}: needed"
+            assert np.array_equal(g.out_slots[layer].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+            m = int(g.miss_count[layer].item())
+            assert np.array_equal(g.miss[layer].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+            if with_attn:
+                assert_close(bf16_to_f64(g.out[layer]), rec["out"], f"{where}: attention")
+        say(f"[fullsize] {key}: step {s} ok")
+        compare_state(g, o, f"{key} step {s}", sample_pages=sample_pages)
+    c = g.tier.read_counters()
+    assert c["error_word"] == 0 and c["drops"] == 0
+    return wl, g, o
+
+
+def test_c2_fullsize():
+    _decode_fullsize("c2", steps=3, attn_layers={0, 7})
+
+
+def test_c3_fullsize():
+    wl, g, o = _decode_fullsize("c3", steps=3, attn_layers={0, 11})
+    c = g.tier.read_counters()
+    assert c["misses"] > 0 and c["evictions"] > 0
+
+
+def test_c4_fullsize():
+    _decode_fullsize("c4", steps=2, attn_layers={5})
+
+
+def test_c5_fullsize_prefill():
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c5")
+    say(f"[fullsize] c5: {wl.description}")
+    g = GpuWorkload(wl)
+    g.setup()
+    got = []
+
+    def on_layer(layer, bufs):
+        got.append({k: bufs[k].clone() for k in ("sel", "needed", "out_slots", "miss", "miss_count", "out")})
+
+    g.prefill(on_layer=on_layer)
+    torch.cuda.synchronize()
+    say("[fullsize] c5: gpu chunk done")
+    o = run.make_tier(wl, materialize=False)
+    run.setup(wl, o)
+    rows = [0, 1, 63, 64, 1000, 2047, 3000, 4095]
+    recs = run.prefill(wl, o, attention_rows=rows)
+    for layer, (gg, rec) in enumerate(zip(got, recs)):
+        where = f"c5 layer {layer}"
+        assert np.array_equal(gg["sel"].cpu().numpy(), rec["sel"]), f"{where}: sel"
+        assert np.array_equal(gg["needed"].cpu().numpy(), rec["needed"]), f"{where}: needed"
+        assert np.array_equal(gg["out_slots"].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+        m = int(gg["miss_count"].item())
+        assert np.array_equal(gg["miss"].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+        if layer in (0, wl.num_layers - 1):
+            out = bf16_to_f64(gg["out"][rows])
+            ref = np.stack([rec["out"][r] for r in rows])
+            assert_close(out, ref, f"{where}: attention")
+    new_pages = list(range(wl.contexts[0] // wl.page_size, wl.num_logical_pages))
+    compare_state(g, o, "c5 after the chunk", sample_pages=new_pages[:3] + new_pages[-2:])

@@ -1,0 +1,67 @@
+"""GPU parity of the prefill chunk (store with write-through, per-query causal
+top-k from the matrix-core indexer, union compaction, ensure, fetch, causal
+sparse attention) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import run
+from workload import gen, get_workload
+
+from tests.gpu_compare import assert_close, bf16_to_f64, compare_state, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(store):
+    def on_layer(layer, bufs):
+        store.append({k: bufs[k].clone() for k in ("sel", "needed", "out_slots", "miss", "miss_count", "out")})
+    return on_layer
+
+
+def test_prefill_small_bit_exact():
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c5s")
+    say(f"[prefill] {wl.name}")
+    g = GpuWorkload(wl)
+    g.setup()
+    got = []
+    g.prefill(on_layer=_capture(got))
+    torch.cuda.synchronize()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    recs = run.prefill(wl, o)
+    for layer, (gg, rec) in enumerate(zip(got, recs)):
+        where = f"c5s layer {layer}"
+        assert np.array_equal(gg["sel"].cpu().numpy(), rec["sel"]), f"{where}: sel"
+        assert np.array_equal(gg["needed"].cpu().numpy(), rec["needed"]), f"{where}: needed"
+        assert np.array_equal(gg["out_slots"].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+        m = int(gg["miss_count"].item())
+        assert np.array_equal(gg["miss"].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+        out = bf16_to_f64(gg["out"])
+        ref = np.stack([rec["out"][r] for r in range(wl.prefill_tokens)])
+        assert_close(out, ref, f"{where}: attention")
+    compare_state(g, o, "c5s after the chunk")
+
+
+def test_matrix_core_scores_equal_scan_scores():
+    """The prefill path (MFMA indexer) and the decode scan give the same
+    selections for the same causal rows."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c5s")
+    say("[prefill] MFMA vs scan selections")
+    g = GpuWorkload(wl)
+    g.setup()
+    bufs = g.prefill()
+    t = g.tier
+    layer = wl.num_layers - 1
+    n = wl.prefill_tokens
+    sel_mfma = bufs["sel"].clone()
+    one = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    sel1 = torch.empty((1, wl.topk), dtype=torch.int32, device="cuda")
+    need1 = torch.empty((1, g.C if g.C else wl.max_sel_pages), dtype=torch.int32, device="cuda")
+    for r in [0, 1, 63, 64, 200, n - 1]:
+        t.select_pages(layer, bufs["q"][r:r + 1], one, g.bt, g.n_pages, wl.topk, sel1, need1,
+                       row_pos=bufs["row_pos"][r:r + 1])
+        torch.cuda.synchronize()
+        assert torch.equal(sel1[0], sel_mfma[r]), r

@@ -121,3 +121,19 @@ def test_select_width_must_fit_pool():
     assert tier.set_select_width(1, 16) == 40
     with pytest.raises(CapacityError):
         tier.set_select_width(2, 16)
+
+
+def test_batched_rows_equal_single_rows():
+    """select_rows (one matrix product for all rows) == select_row row by row,
+    including causal rows and the page bias."""
+    from oracle.select import select_rows
+    rng = np.random.default_rng(12)
+    slab = _slab(90, seed=5)
+    bt = rng.permutation(90).astype(np.int32)
+    q = np.stack([_q(seed=s) for s in range(20)])
+    bias = (-np.log(1 + rng.permutation(90))).astype(np.float32)
+    pos = rng.integers(0, 90 * 64, 20)
+    got, _ = select_rows(q, slab, bt, 90, 7, 4, bias=bias, row_pos=pos)
+    for r in range(20):
+        exp, _ = select_row(q[r], slab, bt, 90, 7, 4, bias=bias, row_pos=int(pos[r]))
+        assert np.array_equal(got[r], exp)

@@ -53,7 +53,7 @@ struct Layout {
   // state offsets
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
-  size_t ws_scores, ws_sel_slots, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
+  size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
       ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_total;
 };
 
@@ -115,6 +115,7 @@ static Layout make_layout(const tkv_config* c) {
   o = 0;
   L.ws_scores = o; o = align256(o + R * ((P + 63) / 64) * 64 * 8);
   L.ws_sel_slots = o; o = align256(o + R * (size_t)c->max_topk * 4);
+  L.ws_qg = o; o = align256(o + R * H * D * 2);
   L.ws_row_done = o; o = align256(o + R * 4);
   L.ws_glob = o; o = align256(o + 16);
   L.ws_slot_of_j = o; o = align256(o + W * 4);
@@ -221,6 +222,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   uint8_t* ws = (uint8_t*)b->workspace;
   d.scores = (float*)(ws + L.ws_scores);
   d.sel_slots = (int32_t*)(ws + L.ws_sel_slots);
+  d.qg = (uint16_t*)(ws + L.ws_qg);
   d.row_done = (int32_t*)(ws + L.ws_row_done);
   d.glob_done = (int32_t*)(ws + L.ws_glob);
   d.slot_of_j = (int32_t*)(ws + L.ws_slot_of_j);
@@ -307,7 +309,12 @@ int tkv_select_pages(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   SelArgs a = make_sel(c, layer, q, rows, row_start, row_pos, block_table, max_pages, n_pages, B,
                        page_bias, topk, sel_local, needed);
   a.do_ensure = 0;
-  HIPCHECK(launch_select_scan(c->dev, a, (hipStream_t)stream), "select_pages launch");
+  if (row_pos && B == 1 && rows >= 64) {
+    // a chunk of query rows of one request: indexer scores as a matrix product
+    HIPCHECK(launch_prefill_scores(c->dev, a, (hipStream_t)stream), "select_pages (prefill) launch");
+  } else {
+    HIPCHECK(launch_select_scan(c->dev, a, (hipStream_t)stream), "select_pages launch");
+  }
   return TKV_OK;
 }
 

@@ -45,6 +45,7 @@ struct DevCtx {
   // workspace
   float* scores;            // [max_rows][max_pages rounded to 64] x 8 bytes: float scores or 64-bit keys
   int32_t* sel_slots;       // [max_rows][max_topk] slots of the selected pages (fused decode)
+  uint16_t* qg;             // [max_rows][Hkv*D] per-group query sums (prefill scoring)
   int32_t* row_done;        // [max_rows] last-block counters (kept at zero between calls)
   int32_t* glob_done;       // [4]
   int32_t* slot_of_j;       // [max_width]

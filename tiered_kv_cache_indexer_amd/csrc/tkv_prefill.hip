@@ -1,4 +1,121 @@
-// Prefill-chunk indexer scores on MFMA (gfx950): placeholder unit, filled in
-// with the bf16 GEMM of the chunk's per-group query sums against the slab.
+// Indexer scores of a prefill chunk on the matrix cores (gfx950).
+//
+// FreeToken PR #499, "Why this works for sparse attention": the indexer
+// scores pages on the GPU-resident compressed slab before any page is read.
+// For a chunk of query rows of one request this is a dense product: the
+// per-group query sums qg [rows][Hkv*d] (bf16) times the slab rows of the
+// request's pages [pages][Hkv*d] (bf16, gathered through the block table).
+//
+// k_group_q forms qg = bf16(fp32(exact sum of the group's query heads)).
+// k_prefill_scores: one 256-thread workgroup per 64 rows x 64 pages; each wave
+// owns 32 x 32 outputs as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16.  Lane i of
+// a wave loads row (i % 16) of a 16 x 32 A tile and page (i % 16) of the
+// 32 x 16 B tile, 8 consecutive features (16 bytes) at feature offset
+// 8 * (i / 16): A and B use the same feature slicing, so the product is the
+// dot product over all features.  Accumulation is fp32; with the inputs on
+// the indexer grids (qg on 2^-5, slab on 2^-10, sum |qg*slab| < 2^9) every
+// partial sum is exact, so the scores equal the decode scan's bit for bit.
 #include "tkv_dev.h"
 #include "tkv_launch.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(TKV_BLOCK) void k_group_q(DevCtx c, const uint16_t* q, int rows, uint16_t* qg) {
+  const int r = blockIdx.x;
+  const int G = c.Hq / c.Hkv, E = c.Hkv * c.D;
+  for (int e = threadIdx.x; e < E; e += TKV_BLOCK) {
+    const int g = e / c.D, dd = e - g * c.D;
+    double acc = 0.0;
+    for (int h = 0; h < G; ++h) acc += (double)bf16_to_f32(q[((size_t)r * c.Hq + g * G + h) * c.D + dd]);
+    qg[(size_t)r * E + e] = f32_to_bf16((float)acc);
+  }
+}
+
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <int E>
+__global__ __launch_bounds__(TKV_BLOCK) void k_prefill_scores(DevCtx c, SelArgs a, const uint16_t* qg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int row0 = blockIdx.y * 64 + wr * 32;
+  const int p0 = blockIdx.x * 64 + wc * 32;
+  const int m = lane & 15, kq = lane >> 4;
+  const int npg = min(a.n_pages[0], a.max_pages);
+  const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
+
+  // operand rows of this lane: 2 query rows, 2 pages
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+  int logical[2];
+  bool bok[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = min(row0 + t * 16 + m, a.rows - 1);
+    arow[t] = qg + (size_t)r * E + kq * 8;
+    const int p = p0 + t * 16 + m;
+    int lg = -1;
+    if (p < npg) lg = a.bt[p];
+    bok[t] = lg >= 0 && (int64_t)lg < c.N;
+    logical[t] = bok[t] ? lg : 0;
+    brow[t] = slab_l + (size_t)logical[t] * E + kq * 8;
+  }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+#pragma unroll 4
+  for (int k0 = 0; k0 < E; k0 += 32) {
+    bf16x8 av[2], bv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      av[t] = ld_bf16x8(arow[t] + k0);
+      bv[t] = bok[t] ? ld_bf16x8(brow[t] + k0) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  }
+  // output tile (i, j): lane holds rows 4*(lane/16) + v, page column lane % 16
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = p0 + j * 16 + m;
+    if (p >= npg) continue;
+    float bias = 0.f;
+    if (a.bias && bok[j]) bias = a.bias[logical[j]];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = row0 + i * 16 + kq * 4 + v;
+        if (r >= a.rows) continue;
+        float key = acc[i][j][v];
+        key = bok[j] ? (a.bias ? key + bias : key) : -INFINITY;
+        c.scores[(size_t)r * c.max_pages + p] = key;
+      }
+  }
+}
+
+hipError_t launch_prefill_scores(const DevCtx& c, const SelArgs& a, hipStream_t st) {
+  uint16_t* qg = c.qg;
+  hipLaunchKernelGGL(k_group_q, dim3(a.rows), dim3(TKV_BLOCK), 0, st, c, a.q, a.rows, qg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((a.max_pages + 63) / 64, (a.rows + 63) / 64);
+  const int E = c.Hkv * c.D;
+  if (E == 512) hipLaunchKernelGGL(k_prefill_scores<512>, grid, dim3(TKV_BLOCK), 0, st, c, a, qg);
+  else if (E == 128) hipLaunchKernelGGL(k_prefill_scores<128>, grid, dim3(TKV_BLOCK), 0, st, c, a, qg);
+  else if (E == 256) hipLaunchKernelGGL(k_prefill_scores<256>, grid, dim3(TKV_BLOCK), 0, st, c, a, qg);
+  else if (E == 1024) hipLaunchKernelGGL(k_prefill_scores<1024>, grid, dim3(TKV_BLOCK), 0, st, c, a, qg);
+  else return hipErrorInvalidValue;
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_select_rows(c, a, st);
+}
