@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--measure-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--graph", action="store_true", help="replay each decode step as a captured HIP graph")
     return ap.parse_args()
 
 
@@ -171,6 +172,119 @@ def cpu_baseline(wl, nsteps):
                         f"host has {cores} cores"))
 
 
+def bench_prefill(args, torch):
+    """c5: one 4,096-token prefill chunk over 65,536 cached tokens, 12 layers:
+    write-ensure, then per layer store (write-through) -> select (matrix-core
+    indexer, causal per-query top-32) -> ensure -> fetch -> causal sparse
+    attention.  Keys, values and queries are generated on the GPU before the
+    timed region; the tier is reset and the context rewritten (untimed)
+    before every repetition."""
+    import numpy as np
+
+    from workload import gen, get_workload, gpu_gen
+    from workload.gpu_run import GpuWorkload
+
+    wl = get_workload(args.config)
+    L, n, start = wl.num_layers, wl.prefill_tokens, wl.contexts[0]
+    g = GpuWorkload(wl)
+    t = g.tier
+    bufs = g.prefill_buffers()
+    K = torch.empty((L, n, wl.num_kv_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    Q = torch.empty((L, n, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    for layer in range(L):
+        gpu_gen.tokens(wl, gen.KIND_K, layer, 0, start, n, out=K[layer])
+        gpu_gen.tokens(wl, gen.KIND_V, layer, 0, start, n, out=V[layer])
+        gpu_gen.tokens(wl, gen.KIND_Q, layer, 0, 0, n, out=Q[layer])
+    run_req = torch.tensor([0], dtype=torch.int32, device="cuda")
+    run_start = torch.tensor([start], dtype=torch.int32, device="cuda")
+    run_len = torch.tensor([n], dtype=torch.int32, device="cuda")
+    run_off = torch.zeros(1, dtype=torch.int32, device="cuda")
+    old_len = torch.tensor([start], dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = ("store", "select", "ensure", "fetch", "attn")
+    reps = []
+    for rep in range(args.warmup + args.steps):
+        t.reset_residency()
+        t.set_select_width(1, wl.topk, 2 * wl.topk + 8)
+        g.setup()
+        torch.cuda.synchronize()
+        t.set_select_width(1, wl.topk, wl.max_sel_pages)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 5 * L)]
+        ev[0].record(stream)
+        t.ensure_write_pages(run_req, run_start, run_len, n, g.bt, old_len)
+        ev[1].record(stream)
+        for layer in range(L):
+            e = ev[2 + 5 * layer: 7 + 5 * layer]
+            t.store_kv_mirror(layer, K[layer], V[layer], run_req, run_start, run_len, run_off, n, g.bt)
+            e[0].record(stream)
+            t.select_pages(layer, Q[layer], bufs["row_start"], g.bt, g.n_pages, wl.topk, bufs["sel"],
+                           bufs["needed"], row_pos=bufs["row_pos"])
+            e[1].record(stream)
+            t.lru_ensure(bufs["needed"].view(-1), bufs["out_slots"], bufs["miss"], bufs["miss_count"])
+            e[2].record(stream)
+            t.fetch_pages(bufs["miss"], bufs["miss_count"])
+            e[3].record(stream)
+            t.sparse_paged_attn(layer, Q[layer], bufs["row_start"], bufs["ctx_len"], bufs["sel"], g.bt,
+                                bufs["out"], row_pos=bufs["row_pos"])
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        if rep < args.warmup:
+            continue
+        split = dict(write_ensure=ev[0].elapsed_time(ev[1]))
+        for i, nm in enumerate(names):
+            split[nm] = 0.0
+        for layer in range(L):
+            prev = ev[1] if layer == 0 else ev[1 + 5 * layer]
+            e = ev[2 + 5 * layer: 7 + 5 * layer]
+            split["store"] += prev.elapsed_time(e[0])
+            split["select"] += e[0].elapsed_time(e[1])
+            split["ensure"] += e[1].elapsed_time(e[2])
+            split["fetch"] += e[2].elapsed_time(e[3])
+            split["attn"] += e[3].elapsed_time(e[4])
+        split["total"] = ev[0].elapsed_time(ev[-1])
+        reps.append(split)
+    ms = {k: float(np.mean([r[k] for r in reps])) for k in reps[0]}
+    # algorithmic work of the last repetition's last layer, scaled by layers
+    sel = bufs["sel"].cpu().numpy()
+    pos = bufs["row_pos"].cpu().numpy()
+    ctxl = start + n
+    toks = 0
+    for r in range(n):
+        for i in sel[r]:
+            if i >= 0:
+                toks += max(0, min(wl.page_size, min(ctxl, int(pos[r]) + 1) - int(i) * wl.page_size))
+    toks = int(toks)
+    attn_flop_layer = toks * wl.num_q_heads * wl.head_dim * 4
+    gemm_flop_layer = 2 * n * wl.pages_of(0) * wl.num_kv_heads * wl.head_dim
+    tok_bytes = t.layer_bytes // wl.page_size
+    c = t.read_counters()
+    return {
+        "metric": "prefill chunk tokens/s (4,096 new over 65,536 cached, 12 layers)",
+        "value": round(n / (ms["total"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms["total"], 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 KV, bf16 q/out, bf16 MFMA indexer, fp32 math", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "chunk_tokens": n, "cached_tokens": start,
+                   "topk_pages": wl.topk, "pool_slots": wl.num_slots},
+        "split_ms": {k: round(v, 3) for k, v in ms.items()},
+        "roofline": {"kernel": "k_attn (causal sparse attention, prefill rows)", "bound": "alu",
+                     "achieved": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12, 2),
+                     "peak": 78.6, "unit": "TFLOP/s",
+                     "frac": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12 / 78.6, 4),
+                     "traffic": None, "note": "peak = non-packed fp32 VALU (256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz)"},
+        "roofline_mfma": {"kernel": "k_prefill_scores (+ per-row top-k, compaction)", "bound": "mfma",
+                          "achieved": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12, 2),
+                          "peak": 2500.0, "unit": "TFLOP/s",
+                          "frac": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12 / 2500.0, 5)},
+        "mirror_write_GBps": round(n * tok_bytes * L / (ms["store"] * 1e-3) / 1e9, 2),
+        "error_word": c["error_word"],
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,6 +299,10 @@ def main():
     from workload.gpu_run import GpuWorkload
 
     base = get_workload(args.config)
+    if base.prefill_tokens:
+        torch.cuda.set_device(0)
+        print(json.dumps(bench_prefill(args, torch)), flush=True)
+        return
     total = args.warmup + args.steps + args.measure_steps
     wl = dataclasses.replace(base, steps=max(base.steps, total))
     torch.cuda.set_device(0)
@@ -200,12 +318,23 @@ def main():
     for s in range(args.warmup):
         g.decode_step(s)
     torch.cuda.synchronize()
+    graphs = {}
+    if args.graph:
+        for s in range(args.warmup, args.warmup + args.steps):
+            cg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cg):
+                g.decode_step(s)
+            graphs[s] = cg
+        torch.cuda.synchronize()
     c0 = g.tier.read_counters()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for s in range(args.warmup, args.warmup + args.steps):
-        g.decode_step(s)
+        if args.graph:
+            graphs[s].replay()
+        else:
+            g.decode_step(s)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -251,6 +380,7 @@ def main():
                  "bytes_per_step": round(link_bytes_step),
                  "step_GBps": round(link_bytes_step / (ms * 1e-3) / 1e9, 2)},
         "calibration": calib,
+        "launch": "hip graph per step" if args.graph else "eager, one C call per layer",
         "error_word": err,
     }
     if not args.no_cpu_baseline:
