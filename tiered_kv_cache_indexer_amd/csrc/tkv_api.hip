@@ -9,7 +9,6 @@
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
-#define SEL_CHUNK_HOST 64
 
 struct tkv_ctx {
   tkv_config cfg;
@@ -292,7 +291,7 @@ static SelArgs make_sel(tkv_ctx* c, int layer, const uint16_t* q, int rows, cons
   a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
   a.bt = bt; a.max_pages = max_pages; a.n_pages = n_pages; a.B = B; a.bias = bias; a.topk = topk;
   a.sel_local = sel; a.needed = needed; a.C = c->C;
-  a.n_chunks = (max_pages + SEL_CHUNK_HOST - 1) / SEL_CHUNK_HOST;
+  a.n_chunks = (max_pages + SEL_CHUNK - 1) / SEL_CHUNK;
   return a;
 }
 

@@ -6,6 +6,7 @@
 
 #define TKV_BLOCK 256
 #define TKV_WAVE 64
+#define SEL_CHUNK 64   // pages scored per workgroup by the decode indexer scan
 
 // device error word bits (mirror the TKV_ERR_* values of the public header)
 #define DERR_PAGE_RANGE 1

@@ -21,7 +21,6 @@
 #include "tkv_launch.h"
 #include "tkv_lru_dev.h"
 
-#define SEL_CHUNK 64
 
 
 
@@ -114,7 +113,7 @@ __device__ void row_topk_block(const float* scores, int visible, int k, int32_t*
 template <typename LoadList>
 __device__ void row_topk64_block(int n_lists, int k, int32_t* out, uint64_t* lds64, LoadList load_list) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int BATCH = 8;   // lists loaded per wave before merging (loads in flight together)
+  constexpr int BATCH = 16;  // lists loaded per wave before merging (loads in flight together)
   uint64_t run = 0;
   for (int base = wave; base < n_lists; base += 4 * BATCH) {
     uint64_t v[BATCH];
@@ -199,8 +198,33 @@ __device__ void write_sel_slots(const DevCtx& c, const SelArgs& a) {
 }
 
 // Shared tail once every row's selection is written: compaction and ensure.
+// A request with one row: its selection is already ascending and unique, so
+// the compaction is a block-table lookup of the first C entries.
+__device__ void compact_single_row(const DevCtx& c, const SelArgs& a, int b, int r, int* sm_scan) {
+  const int32_t* sel = a.sel_local + (size_t)r * a.topk;
+  const int32_t* btb = a.bt + (size_t)b * a.max_pages;
+  int32_t* nd = a.needed + (size_t)b * a.C;
+  int valid = 0;
+  for (int j = threadIdx.x; j < a.topk; j += TKV_BLOCK) valid += sel[j] >= 0;
+  const int u = block_sum(valid, sm_scan);
+  for (int j = threadIdx.x; j < a.C; j += TKV_BLOCK) {
+    int v = -1;
+    if (j < a.topk) {
+      const int i = sel[j];
+      if (i >= 0 && i < a.max_pages) v = btb[i];
+    }
+    nd[j] = v;
+  }
+  if (threadIdx.x == 0 && u > a.C) c.hdr->counters[CNT_DROPS] += u - a.C;
+  __syncthreads();
+}
+
 __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan) {
-  for (int b = 0; b < a.B; ++b) compact_block(c, a, b, dyn, sm_scan);
+  for (int b = 0; b < a.B; ++b) {
+    const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
+    if (r1 - r0 == 1) compact_single_row(c, a, b, r0, sm_scan);
+    else compact_block(c, a, b, dyn, sm_scan);
+  }
   if (a.do_ensure) {
     EnsureOut o{a.out_slots, a.miss, a.miss_count};
     lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan);
@@ -217,43 +241,26 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   __shared__ int sm_misc[8];
   __shared__ int sm_b;
   __shared__ float sm_qg[E8 * 8];
+  __shared__ uint64_t sm_keys[4][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.y, chunk = blockIdx.x;
+  constexpr int G = 8;                                // query heads per KV head (validated on the host)
+  constexpr int E = E8 * 8;                           // Hkv * D
+  constexpr int PPW = E8 >= 64 ? 1 : 64 / E8;         // pages per wave pass
+  constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;         // 16-byte segments per lane
+  constexpr int LANES = E8 >= 64 ? 64 : E8;           // lanes per page
+  constexpr int PASSES = SEL_CHUNK / 4 / PPW;         // wave passes per chunk
   if (tid == 0) sm_b = request_of_row(a.row_start, a.B, r);
-  const int G = c.Hq / c.Hkv;
-  constexpr int E = E8 * 8;  // Hkv * D
-  // per-group query sum: exact (fp64) sum of the group's bf16 heads -> fp32 -> bf16
-  for (int e = tid; e < E; e += TKV_BLOCK) {
-    const int g = e / c.D, dd = e - g * c.D;
-    double acc = 0.0;
-    for (int h = 0; h < G; ++h) acc += (double)bf16_to_f32(a.q[((size_t)r * c.Hq + g * G + h) * c.D + dd]);
-    sm_qg[e] = bf16_to_f32(f32_to_bf16((float)acc));
-  }
   __syncthreads();
   const int b = sm_b;
   const int visible = visible_pages(a, c.PS, b, r);
-
-  constexpr int PPW = E8 >= 64 ? 1 : 64 / E8;       // pages per wave pass
-  constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;        // 16-byte segments per lane
-  constexpr int LANES = E8 >= 64 ? 64 : E8;          // lanes per page
-  constexpr int PASSES = SEL_CHUNK / 4 / PPW;        // wave passes per chunk
-  const int sub = lane / LANES;
-  const int seg0 = lane % LANES;
-  float qg[SPL][8];
-#pragma unroll
-  for (int s = 0; s < SPL; ++s)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qg[s][t] = sm_qg[(seg0 + s * 64) * 8 + t];
-
   const int p_begin = chunk * SEL_CHUNK;
   const int p_end = min(visible, p_begin + SEL_CHUNK);
   const int32_t* btb = a.bt + (size_t)b * a.max_pages;
-  const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
-  float* sc = c.scores + (size_t)r * c.max_pages;
+  const int sub = lane / LANES, seg0 = lane % LANES;
 
-  // all loads of this lane first (memory-level parallelism), then the math
+  // block-table entries first: independent of the query sums
   int logical[PASSES];
-  float keys[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     const int p = p_begin + (it * 4 + wave) * PPW + sub;
@@ -261,15 +268,35 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     if (p < p_end) lg = btb[p];
     logical[it] = ((int64_t)lg >= 0 && (int64_t)lg < c.N) ? lg : -1;
   }
+  // per-group query sum: exact (fp64) sum of the group's 8 bf16 heads -> fp32 -> bf16
+  for (int e = tid; e < E; e += TKV_BLOCK) {
+    const int g = e / c.D, dd = e - g * c.D;
+    const uint16_t* qp = a.q + ((size_t)r * c.Hq + g * G) * c.D + dd;
+    float v[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) v[h] = bf16_to_f32(qp[(size_t)h * c.D]);
+    double acc = 0.0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc += (double)v[h];
+    sm_qg[e] = bf16_to_f32(f32_to_bf16((float)acc));
+  }
+  __syncthreads();
+  float qg[SPL][8];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qg[s][t] = sm_qg[(seg0 + s * 64) * 8 + t];
+
+  const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
   uint4 v[PASSES][SPL];
 #pragma unroll
-  for (int it = 0; it < PASSES; ++it) {
+  for (int it = 0; it < PASSES; ++it)
 #pragma unroll
-    for (int s = 0; s < SPL; ++s) {
-      if (logical[it] >= 0) v[it][s] = reinterpret_cast<const uint4*>(slab_l + (size_t)logical[it] * E)[seg0 + s * 64];
-      else v[it][s] = make_uint4(0, 0, 0, 0);
-    }
-  }
+    for (int s = 0; s < SPL; ++s)
+      v[it][s] = logical[it] >= 0
+                     ? reinterpret_cast<const uint4*>(slab_l + (size_t)logical[it] * E)[seg0 + s * 64]
+                     : make_uint4(0, 0, 0, 0);
+  float keys[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     float part = 0.f;
@@ -284,22 +311,23 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     }
 #pragma unroll
     for (int o = LANES / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    const int lg = logical[it];
     float key = part;
-    if (logical[it] < 0) key = -INFINITY;
-    else if (a.bias) key = key + a.bias[logical[it]];
+    if (lg < 0) key = -INFINITY;
+    else if (a.bias) key = key + a.bias[lg];
     keys[it] = key;
   }
+  float* sc = c.scores + (size_t)r * c.max_pages;
   uint64_t* cand = reinterpret_cast<uint64_t*>(c.scores) + (size_t)r * a.n_chunks * 64;
   if (a.topk <= 64) {
     // this chunk's 64 pages as one sorted list
-    __shared__ uint64_t sm_keys[64];
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int p = p_begin + (it * 4 + wave) * PPW + sub;
-      if (seg0 == 0) sm_keys[p - p_begin] = (p < p_end) ? sel_key(keys[it], p) : 0ull;
+      if (seg0 == 0) sm_keys[0][p - p_begin] = (p < p_end) ? sel_key(keys[it], p) : 0ull;
     }
     __syncthreads();
-    if (wave == 0) cand[(size_t)chunk * 64 + lane] = wave_sort_desc(sm_keys[lane]);
+    if (wave == 0) cand[(size_t)chunk * 64 + lane] = wave_sort_desc(sm_keys[0][lane]);
   } else {
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
@@ -312,8 +340,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     row_topk64_block(a.n_chunks, a.topk, a.sel_local + (size_t)r * a.topk, reinterpret_cast<uint64_t*>(dyn),
                      [&](int ch) { return cand[(size_t)ch * 64 + lane]; });
   } else {
-    row_topk_block(c.scores + (size_t)r * c.max_pages, visible, a.topk, a.sel_local + (size_t)r * a.topk,
-                   dyn, hist, sm_scan, sm_misc);
+    row_topk_block(sc, visible, a.topk, a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
   }
   if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
   select_finish(c, a, dyn, sm_scan);
