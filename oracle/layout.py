@@ -7,7 +7,7 @@ of a page across all layers; PR #525 commit summary: the copy descriptor
 also carries the scale banks).  Per layer, at offset ``layer * layer_bytes``:
 
 * fp8:  K codes  uint8 [Hkv][page][d]
-        V codes  uint8 [Hkv][page][d]
+        V codes  uint8 [Hkv][d][page]     (transposed: a token's values are a column)
         K scales f32   [page]          (one scale per token over Hkv*d values)
         V scales f32   [page]
 * bf16: K        bf16  [Hkv][page][d]

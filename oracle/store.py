@@ -47,14 +47,14 @@ def write_tokens(row: np.ndarray, lay: RowLayout, layer: int, off: int,
         kc, ks = quantize_tokens(k)
         vc, vs = quantize_tokens(v)
         kblk = row[lay.k_off(layer):lay.k_off(layer) + lay.code_bytes].reshape(H, P, D)
-        vblk = row[lay.v_off(layer):lay.v_off(layer) + lay.code_bytes].reshape(H, P, D)
+        vblk = row[lay.v_off(layer):lay.v_off(layer) + lay.code_bytes].reshape(H, D, P)
         kblk[:, off:off + n, :] = kc.transpose(1, 0, 2)
-        vblk[:, off:off + n, :] = vc.transpose(1, 0, 2)
+        vblk[:, :, off:off + n] = vc.transpose(1, 2, 0)
         row[lay.ks_off(layer):lay.ks_off(layer) + 4 * P].view(np.float32)[off:off + n] = ks
         row[lay.vs_off(layer):lay.vs_off(layer) + 4 * P].view(np.float32)[off:off + n] = vs
         if off == 0:
             kblk[:, n:, :] = 0
-            vblk[:, n:, :] = 0
+            vblk[:, :, n:] = 0
             row[lay.ks_off(layer):lay.ks_off(layer) + 4 * P].view(np.float32)[n:] = 0
             row[lay.vs_off(layer):lay.vs_off(layer) + 4 * P].view(np.float32)[n:] = 0
     else:
@@ -81,7 +81,7 @@ def read_kv(row: np.ndarray, lay: RowLayout, layer: int):
     H, P, D = lay.num_kv_heads, lay.page_size, lay.head_dim
     if lay.fp8:
         kc = row[lay.k_off(layer):lay.k_off(layer) + lay.code_bytes].reshape(H, P, D)
-        vc = row[lay.v_off(layer):lay.v_off(layer) + lay.code_bytes].reshape(H, P, D)
+        vc = row[lay.v_off(layer):lay.v_off(layer) + lay.code_bytes].reshape(H, D, P).transpose(0, 2, 1)
         ks = row[lay.ks_off(layer):lay.ks_off(layer) + 4 * P].view(np.float32)
         vs = row[lay.vs_off(layer):lay.vs_off(layer) + 4 * P].view(np.float32)
         k = e4m3_decode(kc).astype(np.float64) * ks.astype(np.float64)[None, :, None]

@@ -98,3 +98,21 @@ def test_generator_values_on_grid_and_bf16_exact():
     gen.to_bf16_bits(k)
     q = gen.prefill_queries(get_workload("c5"), 0, 5, 70)
     assert q.shape == (70, 32, 128) and np.all(np.mod(q * 32, 1) == 0)
+
+
+def test_fp8_value_codes_are_stored_transposed():
+    """fp8 V codes of token t, head h, dim d sit at [h][d][t] of the layer's V
+    block (K codes at [h][t][d])."""
+    lay = RowLayout(1, 2, 8, 128, True)
+    row = np.zeros(lay.row_bytes, dtype=np.uint8)
+    k = np.zeros((8, 2, 128), dtype=np.float32)
+    v = np.zeros((8, 2, 128), dtype=np.float32)
+    v[5, 1, 77] = 3.0          # one nonzero value: its token's amax -> code 0x7E
+    k[2, 0, 9] = -2.0
+    write_tokens(row, lay, 0, 0, k, v)
+    vb = row[lay.v_off(0):lay.v_off(0) + lay.code_bytes]
+    kb = row[lay.k_off(0):lay.k_off(0) + lay.code_bytes]
+    assert np.flatnonzero(vb).tolist() == [(1 * 128 + 77) * 8 + 5] and vb[(1 * 128 + 77) * 8 + 5] == 0x7E
+    assert np.flatnonzero(kb).tolist() == [(0 * 8 + 2) * 128 + 9] and kb[(0 * 8 + 2) * 128 + 9] == 0xFE
+    kr, vr = read_kv(row, lay, 0)
+    assert vr[1, 5, 77] == 3.0 and kr[0, 2, 9] == -2.0
