@@ -33,8 +33,10 @@
  *
  * Page row layout (identical in a pool slot and a mirror row; one row holds
  * one logical page for ALL layers): for layer l at l*layer_bytes,
- *   fp8  : K codes u8[Hkv][page][d] | V codes u8[Hkv][page][d] |
+ *   fp8  : K codes u8[Hkv][page][d] | V codes u8[Hkv][d][page] |
  *          K scales f32[page] | V scales f32[page]
+ *          (V transposed: one head-dim row of a page is contiguous, the
+ *          operand order of the P.V matrix product)
  *   bf16 : K bf16[Hkv][page][d] | V bf16[Hkv][page][d]
  * fp8 is OCP E4M3FN; one fp32 scale per token per tensor over all Hkv*d
  * values: scale = amax/448 (1 if amax == 0), code = e4m3(x / scale), round

@@ -14,8 +14,8 @@
 //    parts with lane shuffles and scaled by the token's K scale;
 //  * softmax: one wave per two heads, exp2 domain (log2(e)/sqrt(d) folded
 //    into the query), the token's V scale folded into its probability;
-//  * PV: thread = (d, half of the tokens), V codes staged in LDS by 16-byte
-//    loads, 8 head accumulators per thread.
+//  * PV: thread = (d, half of the tokens), V codes (fp8: stored transposed,
+//    [d][page]) staged in LDS by 16-byte loads, 8 head accumulators per thread.
 // With several splits per (row, KV head) each split writes (o, m, l) and the
 // last split to finish (atomic counter) merges them and writes bf16 output.
 #include "tkv_dev.h"
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
     for (int t = tb; t < te; ++t) {
       float vv;
       if (FP8) {
-        const uint32_t code = sV[t * D + dcol];
+        const uint32_t code = sV[dcol * PS + t];   // fp8 V is stored transposed [d][page]
         vv = e4m3x2_lo(code).x;
       } else {
         vv = bf16_to_f32(reinterpret_cast<const uint16_t*>(sV)[t * D + dcol]);

@@ -9,9 +9,12 @@
 // time: each lane holds 8 of the token's Hkv*d bf16 values (one 16-byte
 // load), the wave reduces |x| to the token's amax, scale = amax/448 (1 if
 // amax is 0), code = e4m3(x / scale) with a correctly rounded fp32 division.
-// The same 8 code bytes go to the pool slot (HBM) and to the mirror row
-// (posted writes over the host link).  The workgroup also sums the page's
-// keys for the indexer slab: slab = bf16(running sum / tokens written).
+// K codes go straight to the pool slot (HBM) and the mirror row (posted
+// writes over the host link), 8 bytes per lane.  V codes are stored
+// transposed ([h][d][page]): each lane packs its 8 rows' bytes for 4
+// consecutive positions into words, the block is staged in LDS and written
+// out row by row.  The workgroup also sums the page's keys for the indexer
+// slab: slab = bf16(running sum / tokens written).
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
@@ -21,7 +24,9 @@ template <int E8, bool FP8>
 __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   constexpr int E = E8 * 8;
   constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;
+  constexpr int VT_WORDS = FP8 ? E * (64 / 4 + 1) : 1;   // transposed V block, rows padded by one word
   __shared__ float ksum_w[4][E];
+  __shared__ uint32_t vt[VT_WORDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x, j = blockIdx.y;
   const int PS = c.PS, D = c.D;
@@ -45,83 +50,114 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   uint8_t* mir = c.mirror + (size_t)page * c.row_bytes + (size_t)a.layer * c.layer_bytes;
   uint8_t* pol = slot >= 0 ? c.pool + (size_t)slot * c.row_bytes + (size_t)a.layer * c.layer_bytes : nullptr;
   const size_t cb = (size_t)c.code_bytes;
-  const int tok0 = a.run_tok_off[r] + (t0 - start);
+  const int tok_first = a.run_tok_off[r] + (t0 - start);  // input row of page position `off`
+  const int VROW = PS / 4 + 1;                             // words per staged V row (fp8)
+  if (FP8)
+    for (int w = tid; w < E * VROW; w += TKV_BLOCK) vt[w] = 0u;
 
   float ksum[SPL][8];
 #pragma unroll
   for (int s = 0; s < SPL; ++s)
 #pragma unroll
     for (int t = 0; t < 8; ++t) ksum[s][t] = 0.f;
+  if (FP8) __syncthreads();
 
-  for (int tt = wave; tt < n; tt += 4) {
-    const int pos = off + tt;  // position within the page
+  // a wave handles groups of 4 consecutive page positions
+  for (int grp = wave; grp * 4 < PS; grp += 4) {
+    const int pbase = grp * 4;
+    if (pbase + 3 < off || pbase >= off + n) continue;   // wave-uniform
+    uint32_t vpack[SPL][8];
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const uint16_t* src = (kv == 0 ? a.k : a.v) + (size_t)(tok0 + tt) * E;
-      float x[SPL][8];
-      bool act[SPL];
-      float amax = 0.f;
+    for (int s = 0; s < SPL; ++s)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) vpack[s][t] = 0u;
+    for (int u = 0; u < 4; ++u) {
+      const int pos = pbase + u;
+      if (pos < off || pos >= off + n) continue;         // wave-uniform
+      const int tok = tok_first + (pos - off);
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint16_t* src = (kv == 0 ? a.k : a.v) + (size_t)tok * E;
+        float x[SPL][8];
+        bool act[SPL];
+        uint4 raw[SPL];
+        float amax = 0.f;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const int seg = lane + s * 64;
+          act[s] = seg < E8;
+          raw[s] = act[s] ? reinterpret_cast<const uint4*>(src)[seg] : make_uint4(0, 0, 0, 0);
+          const uint32_t ww[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            x[s][2 * t] = __uint_as_float(ww[t] << 16);
+            x[s][2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(x[s][t]));
+          if (kv == 0)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) ksum[s][t] += x[s][t];
+        }
+        uint8_t* mblk = mir + kv * cb;
+        uint8_t* pblk = pol ? pol + kv * cb : nullptr;
+        if (FP8) {
+          amax = wave_max(amax);
+          const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            if (!act[s]) continue;
+            uint32_t code[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) code[t] = f32_to_e4m3(x[s][t] / scale);
+            if (kv == 0) {
+              // K codes [h][pos][d]: 8 consecutive bytes
+              const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
+              const uint2 val = make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
+                                           code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
+              const size_t o = ((size_t)h * PS + pos) * D + dd;
+              *reinterpret_cast<uint2*>(mblk + o) = val;
+              if (pblk) *reinterpret_cast<uint2*>(pblk + o) = val;
+            } else {
+              // V codes transposed [h][d][pos]: byte u of the group's word in each of 8 rows
+#pragma unroll
+              for (int t = 0; t < 8; ++t) vpack[s][t] |= code[t] << (8 * u);
+            }
+          }
+          if (lane == 0) {
+            const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
+            *reinterpret_cast<float*>(mir + so) = scale;
+            if (pol) *reinterpret_cast<float*>(pol + so) = scale;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < SPL; ++s) {
+            if (!act[s]) continue;
+            const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
+            const size_t o = (((size_t)h * PS + pos) * D + dd) * 2;
+            *reinterpret_cast<uint4*>(mblk + o) = raw[s];
+            if (pblk) *reinterpret_cast<uint4*>(pblk + o) = raw[s];
+          }
+        }
+      }
+    }
+    if (FP8) {
 #pragma unroll
       for (int s = 0; s < SPL; ++s) {
-        const int seg = lane + s * 64;
-        act[s] = seg < E8;
-        uint4 w = act[s] ? reinterpret_cast<const uint4*>(src)[seg] : make_uint4(0, 0, 0, 0);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        if (lane + s * 64 >= E8) continue;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          x[s][2 * t] = __uint_as_float(ww[t] << 16);
-          x[s][2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(x[s][t]));
-        if (kv == 0)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) ksum[s][t] += x[s][t];
-      }
-      uint8_t* mblk = mir + kv * cb;
-      uint8_t* pblk = pol ? pol + kv * cb : nullptr;
-      if (FP8) {
-        amax = wave_max(amax);
-        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-#pragma unroll
-        for (int s = 0; s < SPL; ++s) {
-          if (!act[s]) continue;
-          const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
-          uint32_t lo = 0, hi = 0;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) lo |= f32_to_e4m3(x[s][t] / scale) << (8 * t);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) hi |= f32_to_e4m3(x[s][4 + t] / scale) << (8 * t);
-          const size_t o = ((size_t)h * PS + pos) * D + dd;
-          const uint2 val = make_uint2(lo, hi);
-          *reinterpret_cast<uint2*>(mblk + o) = val;
-          if (pblk) *reinterpret_cast<uint2*>(pblk + o) = val;
-        }
-        if (lane == 0) {
-          const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
-          *reinterpret_cast<float*>(mir + so) = scale;
-          if (pol) *reinterpret_cast<float*>(pol + so) = scale;
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < SPL; ++s) {
-          if (!act[s]) continue;
-          const int e = (lane + s * 64) * 8, h = e / D, dd = e - h * D;
-          const uint4 w = reinterpret_cast<const uint4*>(src)[lane + s * 64];
-          const size_t o = (((size_t)h * PS + pos) * D + dd) * 2;
-          *reinterpret_cast<uint4*>(mblk + o) = w;
-          if (pblk) *reinterpret_cast<uint4*>(pblk + o) = w;
-        }
+        for (int t = 0; t < 8; ++t) vt[((lane + s * 64) * 8 + t) * VROW + grp] = vpack[s][t];
       }
     }
   }
 
   // a write that begins the page clears the page's later positions
-  if (off == 0 && n < PS) {
+  const bool zero_tail = (off == 0 && n < PS);
+  if (zero_tail) {
     const int elt = FP8 ? 1 : 2;
     const int H = c.Hkv;
-    const int tail = (PS - n) * D * elt;  // bytes per head
-    for (int kv = 0; kv < 2; ++kv)
+    const int tail = (PS - n) * D * elt;  // K bytes per head (and V bytes for bf16)
+    for (int kv = 0; kv < (FP8 ? 1 : 2); ++kv)
       for (int h = 0; h < H; ++h) {
         const size_t base = (size_t)kv * cb + ((size_t)h * PS + n) * D * elt;
         for (int i = tid * 4; i < tail; i += TKV_BLOCK * 4) {
@@ -136,6 +172,32 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
         if (pol) {
           reinterpret_cast<float*>(pol + 2 * cb)[i] = 0.f;
           reinterpret_cast<float*>(pol + 2 * cb + PS * 4)[i] = 0.f;
+        }
+      }
+    }
+  }
+
+  if (FP8) {
+    // transposed V rows out: positions [off, off+n) (through the page end when it begins the page)
+    __syncthreads();
+    const int lo = off, hi = zero_tail ? PS : off + n;
+    uint8_t* mv = mir + cb;
+    uint8_t* pv = pol ? pol + cb : nullptr;
+    const int wpr = PS / 4;
+    for (int idx = tid; idx < E * wpr; idx += TKV_BLOCK) {
+      const int e = idx / wpr, w = idx - e * wpr;
+      const int p0 = 4 * w;
+      if (p0 + 4 <= lo || p0 >= hi) continue;
+      const uint32_t word = vt[e * VROW + w];
+      const size_t o = (size_t)e * PS + p0;
+      if (p0 >= lo && p0 + 4 <= hi) {
+        *reinterpret_cast<uint32_t*>(mv + o) = word;
+        if (pv) *reinterpret_cast<uint32_t*>(pv + o) = word;
+      } else {
+        for (int b = 0; b < 4; ++b) {
+          if (p0 + b < lo || p0 + b >= hi) continue;
+          mv[o + b] = (uint8_t)(word >> (8 * b));
+          if (pv) pv[o + b] = (uint8_t)(word >> (8 * b));
         }
       }
     }
