@@ -241,6 +241,13 @@ int tkv_read_counters(tkv_ctx* ctx, tkv_counters* out, void* stream);
  * synchronises `stream`. */
 int tkv_debug_read_state(tkv_ctx* ctx, int32_t* page_to_slot, int32_t* slot_to_page,
                          int64_t* stamp, int64_t* clock, void* stream);
+/* Chooses the attention kernel of later calls: TKV_ATTN_AUTO (the matrix-core
+ * kernel where it applies: fp8, 64-token pages, d = 128, 8 query heads per
+ * KV head; else the vector kernel), TKV_ATTN_VECTOR, or TKV_ATTN_MATRIX
+ * (TKV_E_UNSUPPORTED_FORMAT when the shapes do not fit it).  Both compute the
+ * same softmax; tests compare them. */
+enum { TKV_ATTN_AUTO = 0, TKV_ATTN_VECTOR = 1, TKV_ATTN_MATRIX = 2 };
+int tkv_debug_set_attn_kernel(tkv_ctx* ctx, int32_t kernel);
 /* fp32 -> e4m3 codes with the store's encoder; device pointers. */
 int tkv_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 /* e4m3 codes -> fp32 with the attention kernel's decoder; device pointers. */

@@ -17,20 +17,27 @@ from tests.gpu_compare import compare_layer, compare_state, say
 pytestmark = pytest.mark.gpu
 
 
-def _pair(key):
+KERNELS = {"auto": 0, "vector": 1, "matrix": 2}
+
+
+def _pair(key, kernel="auto"):
     from workload.gpu_run import GpuWorkload
     wl = get_workload(key)
-    say(f"[parity] {key}: {wl.description or wl.name}")
+    say(f"[parity] {key} ({kernel} attention): {wl.description or wl.name}")
     g = GpuWorkload(wl)
+    g.tier.set_attn_kernel(KERNELS[kernel])
     g.setup()
     o = run.make_tier(wl, materialize=True)
     run.setup(wl, o)
     return wl, g, o
 
 
-@pytest.mark.parametrize("key", ["c1", "c2s", "c3s", "c4s"])
-def test_decode_chain_bit_exact(key):
-    wl, g, o = _pair(key)
+@pytest.mark.parametrize("key,kernel", [("c1", "auto"), ("c2s", "auto"), ("c3s", "auto"), ("c4s", "auto"),
+                                        ("c3s", "vector"), ("c4s", "vector")])
+def test_decode_chain_bit_exact(key, kernel):
+    """Fixed-point results bit-exact, attention within tolerance; `auto` runs
+    the matrix-core attention kernel on the fp8 configs, `vector` the other."""
+    wl, g, o = _pair(key, kernel)
     compare_state(g, o, f"{key} after setup")
     g.upload_queries()
     q = gen.decode_queries(wl)
@@ -79,6 +86,16 @@ def test_unfused_entry_points_match_fused_step():
     sa, sb = a.tier.read_state(), b.tier.read_state()
     for k in ("page_to_slot", "slot_to_page", "stamp"):
         assert np.array_equal(sa[k], sb[k])
+
+
+def test_matrix_attention_refused_where_it_does_not_apply():
+    from tiered_kv_cache_indexer_amd import TkvError
+    from workload.gpu_run import GpuWorkload
+    g = GpuWorkload(get_workload("c1"))          # bf16, 16-token pages
+    with pytest.raises(TkvError, match="matrix-core"):
+        g.tier.set_attn_kernel(2)
+    g.tier.set_attn_kernel(1)
+    g.tier.set_attn_kernel(0)
 
 
 def test_codecs_match_oracle():

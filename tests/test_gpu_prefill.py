@@ -19,11 +19,13 @@ def _capture(store):
     return on_layer
 
 
-def test_prefill_small_bit_exact():
+@pytest.mark.parametrize("kernel", [0, 1], ids=["auto", "vector"])
+def test_prefill_small_bit_exact(kernel):
     from workload.gpu_run import GpuWorkload
     wl = get_workload("c5s")
-    say(f"[prefill] {wl.name}")
+    say(f"[prefill] {wl.name} attention kernel {kernel}")
     g = GpuWorkload(wl)
+    g.tier.set_attn_kernel(kernel)
     g.setup()
     got = []
     g.prefill(on_layer=_capture(got))

@@ -75,6 +75,7 @@ SIGNATURES = {
     "tkv_debug_read_state": (C.c_int, [P, P, P, P, C.POINTER(C.c_int64), P]),
     "tkv_debug_e4m3_encode": (C.c_int, [P, P, I64, P]),
     "tkv_debug_e4m3_decode": (C.c_int, [P, P, I64, P]),
+    "tkv_debug_set_attn_kernel": (C.c_int, [P, I32]),
     "tkv_mirror_host_ptr": (C.c_void_p, [P]),
     "tkv_destroy": (None, [P]),
     "tkv_last_error": (C.c_char_p, []),

@@ -462,6 +462,22 @@ int tkv_debug_read_state(tkv_ctx* c, int32_t* page_to_slot, int32_t* slot_to_pag
   return TKV_OK;
 }
 
+int tkv_debug_set_attn_kernel(tkv_ctx* c, int32_t kernel) {
+  if (!c) return fail(TKV_E_INVALID_ARG, "ctx is null");
+  if (kernel < TKV_ATTN_AUTO || kernel > TKV_ATTN_MATRIX)
+    return fail(TKV_E_INVALID_ARG, "attention kernel=%d: expected 0 (auto), 1 (vector) or 2 (matrix)", kernel);
+  if (kernel == TKV_ATTN_MATRIX) {
+    const tkv_config& f = c->cfg;
+    if (!(f.kv_format == TKV_KV_FP8_E4M3_PER_TOKEN && f.page_size == 64 && f.head_dim == 128 &&
+          f.num_q_heads == 8 * f.num_kv_heads))
+      return fail(TKV_E_UNSUPPORTED_FORMAT,
+                  "the matrix-core attention kernel needs kv_format=fp8, page_size=64, head_dim=128, "
+                  "8 query heads per KV head");
+  }
+  c->dev.attn_impl = kernel == TKV_ATTN_VECTOR ? ATTN_VECTOR : kernel == TKV_ATTN_MATRIX ? ATTN_MATRIX : ATTN_AUTO;
+  return TKV_OK;
+}
+
 int tkv_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (!in || !out || n < 0) return fail(TKV_E_INVALID_ARG, "bad arguments");
   HIPCHECK(launch_e4m3_encode(in, out, n, (hipStream_t)stream), "e4m3 encode launch");

@@ -20,11 +20,12 @@
 // last split to finish (atomic counter) merges them and writes bf16 output.
 #include "tkv_dev.h"
 #include "tkv_launch.h"
+#include "tkv_attn_dev.h"
 
 
 
-#define ATT_D 128
-#define ATT_G 8
+
+
 #define ATT_MAXP 64   // pages one workgroup resolves at once
 
 template <int PS, bool FP8>
@@ -262,53 +263,12 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
     }
   }
   if (!last_block_arrive(&c.attn_done[r * c.Hkv + g], a.splits, &sflag[0])) return;
-  // merge the splits: thread = (head, 4 d values); every load of a pass is
-  // independent so the whole pass is one memory round trip
-  {
-    const int h = tid / 32, d0 = (tid % 32) * 4;
-    const float* base = c.attn_part + ((size_t)r * c.Hq + g * G + h) * a.splits * REC;
-    const int S = a.splits;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      float mv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) mv[u] = (s0 + u < S) ? base[(size_t)(s0 + u) * REC + D] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) M = fmaxf(M, mv[u]);
-    }
-    float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (M != -INFINITY) {
-      for (int s0 = 0; s0 < S; s0 += 16) {
-        float4 ov[16];
-        float2 ml[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (s0 + u < S) {
-            const float* rec = base + (size_t)(s0 + u) * REC;
-            ov[u] = *reinterpret_cast<const float4*>(rec + d0);
-            ml[u] = *reinterpret_cast<const float2*>(rec + D);
-          } else {
-            ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            ml[u] = make_float2(-INFINITY, 0.f);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float w = (ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
-          L += ml[u].y * w;
-          o.x += ov[u].x * w; o.y += ov[u].y * w; o.z += ov[u].z * w; o.w += ov[u].w * w;
-        }
-      }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint16_t* op = a.out + ((size_t)r * c.Hq + g * G + h) * D + d0;
-    op[0] = f32_to_bf16(o.x * inv); op[1] = f32_to_bf16(o.y * inv);
-    op[2] = f32_to_bf16(o.z * inv); op[3] = f32_to_bf16(o.w * inv);
-  }
+  attn_merge_splits(c, a, r, g, tid);
 }
 
 hipError_t launch_attn(const DevCtx& c, AttnArgs a, hipStream_t st) {
+  if (c.attn_impl != ATTN_VECTOR && attn_mfma_supported(c)) return launch_attn_mfma(c, a, st);
+  if (c.attn_impl == ATTN_MATRIX) return hipErrorInvalidValue;
   // splits: enough workgroups to cover the chip for small batches; one split
   // (no merge) when rows exceed the merge scratch (prefill chunks)
   int per = 1;

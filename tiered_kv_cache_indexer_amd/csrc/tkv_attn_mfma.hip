@@ -1,0 +1,319 @@
+// Sparse paged attention on the matrix cores (gfx950): fp8 e4m3 KV with
+// per-token scales, 64-token pages, d = 128, 8 query heads per KV head.
+//
+// FreeToken PR #499, "Design": after the ensure, attention reads only the
+// selected pages through the logical->physical translation; vLLM RFC #33980,
+// "Proposed Change": attention over the top-k KV.  The arithmetic is the
+// same softmax as the vector kernel; only the products move to
+// v_mfma_f32_16x16x32_bf16 (e4m3 codes are exact in bf16).
+//
+// One wave processes one selected page of one (row, KV head) at a time.
+//  * S^T = K . Q^T: the 64 keys of the page are four 16-row A tiles, the
+//    8 query heads are B columns 0..7 (columns 8..15 zero).  The
+//    contraction over d runs in an order in which a lane's A slice is two
+//    16-byte loads of its key row; the query operand (loaded once) uses the
+//    same order.  Row m of A tile `mt` is token 16*(m/4) + 4*mt + m%4, so
+//    the output fragment of lane (q = lane/16, h = lane%16) holds tokens
+//    16q .. 16q+15 of head h: the online softmax is per lane plus two
+//    cross-lane reductions.
+//  * The probabilities, times the token's V scale and rounded to bf16, are
+//    then already the B operand of O^T += V^T . P^T: lane (q, h) supplies
+//    tokens 16q + 8*kt .. +7 of head h for contraction step kt.  fp8 V is
+//    stored transposed ([d][page]), so the matching A slice (one d row,
+//    16 tokens) is one 16-byte load.  The accumulator columns are the
+//    heads, so the softmax rescale is one multiply per lane.
+// Wave-per-row mode (many rows, e.g. prefill chunks): each wave owns one
+// (row, KV head) and runs over all its pages; nothing is merged.  Split
+// mode (decode): a workgroup of 4 waves owns a (row, KV head, page range),
+// the waves' states are merged in LDS, and split records are merged by the
+// last workgroup to arrive.
+#include "tkv_dev.h"
+#include "tkv_launch.h"
+#include "tkv_attn_dev.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+namespace {
+
+constexpr int MD = ATT_D, MG = ATT_G, MPS = 64, MWAVES = TKV_BLOCK / 64;
+
+__device__ __forceinline__ uint32_t bits2(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 16 e4m3 codes (bytes in address order) -> bf16 operands of elements 0..7
+// and 8..15 (exact conversion)
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4 w, bf16x8& lo, bf16x8& hi) {
+  const uint4 l = make_uint4(bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, false)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.x, 1.0f, true)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, false)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.y, 1.0f, true)));
+  const uint4 h = make_uint4(bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.z, 1.0f, false)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.z, 1.0f, true)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.w, 1.0f, false)),
+                             bits2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w.w, 1.0f, true)));
+  lo = __builtin_bit_cast(bf16x8, l);
+  hi = __builtin_bit_cast(bf16x8, h);
+}
+
+__device__ __forceinline__ bf16x8 ld_q8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+struct WaveAttn {
+  f32x4 acc[8];   // O^T tiles: d = 16*dt + 4*(lane/16) + v, head lane%16
+  float m_run, l_run;
+};
+
+// One page (nt >= 1 visible tokens) of KV head g, layer block `blk` of a pool
+// slot, folded into the wave's running state.
+__device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, int nt, int lane,
+                                          const bf16x8 (&qop)[4], float qscale, WaveAttn& st) {
+  const int m = lane & 15, q = lane >> 4;
+  const uint8_t* kb = blk + (size_t)g * MPS * MD;
+  const uint8_t* vb = blk + cb + (size_t)g * MPS * MD;
+  const float* ksc = reinterpret_cast<const float*>(blk + 2 * cb);
+  uint4 kr[4][2], vr[8];
+  float4 ks4[4], vs4[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int t = 16 * (m >> 2) + 4 * mt + (m & 3);
+    kr[mt][0] = *reinterpret_cast<const uint4*>(kb + t * MD + 16 * q);
+    kr[mt][1] = *reinterpret_cast<const uint4*>(kb + t * MD + 64 + 16 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ks4[i] = *reinterpret_cast<const float4*>(ksc + 16 * q + 4 * i);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) vr[dt] = *reinterpret_cast<const uint4*>(vb + (16 * dt + m) * MPS + 16 * q);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vs4[i] = *reinterpret_cast<const float4*>(ksc + MPS + 16 * q + 4 * i);
+
+  // S^T tiles
+  f32x4 s[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    bf16x8 a0, a1, a2, a3;
+    fp8x16_to_bf16(kr[mt][0], a0, a1);
+    fp8x16_to_bf16(kr[mt][1], a2, a3);
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qop[0], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qop[1], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, qop[2], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, qop[3], z, 0, 0, 0);
+    s[mt] = z;
+  }
+  // logits in the exp2 domain, masked past the visible tokens
+  float mx = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float kv4[4] = {ks4[mt].x, ks4[mt].y, ks4[mt].z, ks4[mt].w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = 16 * q + 4 * mt + v;
+      const float x = tok < nt ? s[mt][v] * (kv4[v] * qscale) : -INFINITY;
+      s[mt][v] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m_run, mx);        // finite: token 0 is visible
+  const float alpha = exp2f(st.m_run - m_new);
+  float psum = 0.f;
+  f32x8 pv[2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float vv4[4] = {vs4[mt].x, vs4[mt].y, vs4[mt].z, vs4[mt].w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float p = exp2f(s[mt][v] - m_new);
+      psum += p;
+      pv[mt >> 1][4 * (mt & 1) + v] = p * vv4[v];
+    }
+  }
+  psum += __shfl_xor(psum, 16, 64);
+  psum += __shfl_xor(psum, 32, 64);
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+  const bf16x8 pb0 = __builtin_convertvector(pv[0], bf16x8);
+  const bf16x8 pb1 = __builtin_convertvector(pv[1], bf16x8);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    bf16x8 v0, v1;
+    fp8x16_to_bf16(vr[dt], v0, v1);
+    f32x4 o = st.acc[dt] * alpha;
+    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb0, o, 0, 0, 0);
+    o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb1, o, 0, 0, 0);
+    st.acc[dt] = o;
+  }
+}
+
+// Pages j = jbeg, jbeg + jstep, ... < jend of row r (request b), KV head g.
+__device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, int r, int b, int g,
+                                           int jbeg, int jend, int jstep, int lane,
+                                           const bf16x8 (&qop)[4], WaveAttn& st) {
+  int limit = a.ctx_len[b];
+  if (a.row_pos) limit = min(limit, a.row_pos[r] + 1);
+  const float qscale = 1.4426950408889634f / sqrtf((float)MD);
+  const uint8_t* pool_l = c.pool + (size_t)a.layer * c.layer_bytes;
+  const size_t cb = (size_t)c.code_bytes;
+  for (int base = jbeg; base < jend; base += 64 * jstep) {
+    // lane i resolves page base + i*jstep: local id -> slot, visible tokens
+    const int j = base + lane * jstep;
+    int slot = -1, nt = 0;
+    if (j < jend) {
+      const int i = a.sel[(size_t)r * a.topk + j];
+      if (a.slots) {
+        const int s = a.slots[(size_t)r * a.topk + j];
+        if (i >= 0 && s >= 0 && s < c.S) {
+          slot = s;
+          nt = min(MPS, limit - i * MPS);
+        }
+      } else if (i >= 0 && i < a.max_pages) {
+        const int page = a.bt[(size_t)b * a.max_pages + i];
+        if (page >= 0 && (int64_t)page < c.N) slot = c.page_to_slot[page];
+        nt = min(MPS, limit - i * MPS);
+      }
+      if (slot < 0) nt = 0;
+    }
+    const int cnt = min(64, (jend - base + jstep - 1) / jstep);
+    for (int i = 0; i < cnt; ++i) {
+      const int sl = __builtin_amdgcn_readlane(slot, i);
+      const int n = __builtin_amdgcn_readlane(nt, i);
+      if (n <= 0) continue;
+      wave_page(pool_l + (size_t)sl * c.row_bytes, cb, g, n, lane, qop, qscale, st);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_query(const AttnArgs& a, const DevCtx& c, int r, int g, int lane,
+                                           bf16x8 (&qop)[4]) {
+  const int h = lane & 15, q = lane >> 4;
+  if (h < MG) {
+    const uint16_t* qh = a.q + ((size_t)r * c.Hq + g * MG + h) * MD + 16 * q;
+    qop[0] = ld_q8(qh);
+    qop[1] = ld_q8(qh + 8);
+    qop[2] = ld_q8(qh + 64);
+    qop[3] = ld_q8(qh + 72);
+  } else {
+    const bf16x8 z = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    qop[0] = z; qop[1] = z; qop[2] = z; qop[3] = z;
+  }
+}
+
+__device__ __forceinline__ void init_state(WaveAttn& st) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+}
+
+// one wave per (row, KV head), all of the row's pages
+__global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * MWAVES + wave;
+  if (u >= a.rows * c.Hkv) return;
+  const int r = u / c.Hkv, g = u - r * c.Hkv;
+  const int b = attn_row_request(a, r);
+  bf16x8 qop[4];
+  load_query(a, c, r, g, lane, qop);
+  WaveAttn st;
+  init_state(st);
+  wave_pages(c, a, r, b, g, 0, a.topk, 1, lane, qop, st);
+  const int h = lane & 15, q = lane >> 4;
+  if (h >= MG) return;
+  const float inv = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
+  uint16_t* op = a.out + ((size_t)r * c.Hq + g * MG + h) * MD + 4 * q;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const f32x4 o = st.acc[dt] * inv;
+    const uint2 w = make_uint2((uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+                               (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16));
+    *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+  }
+}
+
+// a workgroup per (row, KV head, page range); wave w takes every 4th page
+__global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_split(DevCtx c, AttnArgs a) {
+  __shared__ __align__(16) float sO[MWAVES][MG][MD];
+  __shared__ float sM[MWAVES][MG], sL[MWAVES][MG];
+  __shared__ int sflag[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.y;
+  const int g = blockIdx.x % c.Hkv;
+  const int split = blockIdx.x / c.Hkv;
+  const int j0 = split * a.pages_per_split;
+  const int j1 = min(a.topk, j0 + a.pages_per_split);
+  const int b = attn_row_request(a, r);
+  bf16x8 qop[4];
+  load_query(a, c, r, g, lane, qop);
+  WaveAttn st;
+  init_state(st);
+  wave_pages(c, a, r, b, g, j0 + wave, j1, MWAVES, lane, qop, st);
+  const int h = lane & 15, q = lane >> 4;
+  if (h < MG) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(&sO[wave][h][16 * dt + 4 * q]) =
+          make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+    if (q == 0) {
+      sM[wave][h] = st.m_run;
+      sL[wave][h] = st.l_run;
+    }
+  }
+  __syncthreads();
+  // merge the waves: thread = (head, 4 d values)
+  const int hh = tid / 32, d0 = (tid % 32) * 4;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < MWAVES; ++w) M = fmaxf(M, sM[w][hh]);
+  float L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < MWAVES; ++w) {
+      const float mw = sM[w][hh];
+      const float wt = mw == -INFINITY ? 0.f : exp2f(mw - M);
+      const float4 ow = *reinterpret_cast<const float4*>(&sO[w][hh][d0]);
+      L += sL[w][hh] * wt;
+      o.x += ow.x * wt; o.y += ow.y * wt; o.z += ow.z * wt; o.w += ow.w * wt;
+    }
+  }
+  if (a.splits == 1) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint16_t* op = a.out + ((size_t)r * c.Hq + g * MG + hh) * MD + d0;
+    op[0] = f32_to_bf16(o.x * inv); op[1] = f32_to_bf16(o.y * inv);
+    op[2] = f32_to_bf16(o.z * inv); op[3] = f32_to_bf16(o.w * inv);
+    return;
+  }
+  float* rec = c.attn_part + (((size_t)r * c.Hq + g * MG + hh) * a.splits + split) * ATT_REC;
+  *reinterpret_cast<float4*>(rec + d0) = o;
+  if (d0 == 0) *reinterpret_cast<float2*>(rec + MD) = make_float2(M, L);
+  if (!last_block_arrive(&c.attn_done[r * c.Hkv + g], a.splits, &sflag[0])) return;
+  attn_merge_splits(c, a, r, g, tid);
+}
+
+}  // namespace
+
+bool attn_mfma_supported(const DevCtx& c) {
+  return c.fp8 && c.PS == MPS && c.D == MD && c.Hq == MG * c.Hkv;
+}
+
+hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
+  if (!attn_mfma_supported(c)) return hipErrorInvalidValue;
+  const long units = (long)a.rows * c.Hkv;
+  if (a.rows > c.max_batch || units >= 256) {
+    a.splits = 1;
+    a.pages_per_split = a.topk;
+    const int blocks = (int)((units + MWAVES - 1) / MWAVES);
+    hipLaunchKernelGGL(k_attn_mfma_rows, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a);
+    return hipGetLastError();
+  }
+  // one page per wave
+  a.pages_per_split = MWAVES;
+  a.splits = (a.topk + MWAVES - 1) / MWAVES;
+  dim3 grid(c.Hkv * a.splits, a.rows);
+  hipLaunchKernelGGL(k_attn_mfma_split, grid, dim3(TKV_BLOCK), 0, st, c, a);
+  return hipGetLastError();
+}

@@ -60,7 +60,10 @@ struct DevCtx {
   int32_t* attn_done;       // [max_batch][Hkv]
   int32_t* iota;            // [max_rows + 1] = 0, 1, 2, ... (row_start of one-row-per-request calls)
   int max_rows, max_pages, max_topk, max_batch, max_width;
+  int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
 };
+
+enum { ATTN_AUTO = 0, ATTN_VECTOR = 1, ATTN_MATRIX = 2 };
 
 // ------------------------------------------------------------- call arguments --
 struct SelArgs {

@@ -19,6 +19,8 @@ hipError_t launch_write_ensure(const DevCtx& c, int n_runs, const int32_t* run_r
                                hipStream_t st);
 hipError_t launch_store(const DevCtx& c, const StoreArgs& a, int max_run_len, hipStream_t st);
 hipError_t launch_attn(const DevCtx& c, AttnArgs a, hipStream_t st);
+bool attn_mfma_supported(const DevCtx& c);
+hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st);
 hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st);
 hipError_t launch_fill_bytes(void* p, int64_t n, uint8_t v, hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);

@@ -199,6 +199,12 @@ class TieredKV:
                                              _stream(None)))
         return out
 
+    ATTN_AUTO, ATTN_VECTOR, ATTN_MATRIX = 0, 1, 2
+
+    def set_attn_kernel(self, kernel: int) -> None:
+        """Attention kernel of later calls (tkv_debug_set_attn_kernel)."""
+        check(self.lib.tkv_debug_set_attn_kernel(self.ctx, int(kernel)))
+
     def e4m3_decode(self, codes: torch.Tensor) -> torch.Tensor:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
         check(self.lib.tkv_debug_e4m3_decode(_ptr(codes, torch.uint8, "codes"), out.data_ptr(),
