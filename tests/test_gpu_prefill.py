@@ -67,3 +67,45 @@ def test_matrix_core_scores_equal_scan_scores():
                        row_pos=bufs["row_pos"][r:r + 1])
         torch.cuda.synchronize()
         assert torch.equal(sel1[0], sel_mfma[r]), r
+
+
+def test_multi_row_requests_union_and_drops():
+    """Several requests with several causal rows each in one select call (the
+    scan path): per-row selections, the per-request unions (ascending, first C
+    kept) and the drop counter equal the oracle's.  Row counts straddle the
+    64-row groups of the union bitmaps."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c4s")
+    counts = [70, 1, 130, 65]
+    rows = sum(counts)
+    say(f"[prefill] multi-row select on {wl.name}, rows {counts}")
+    g = GpuWorkload(wl, max_rows=rows)
+    g.setup()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    t = g.tier
+    C = g.C                                   # 2*topk + 8: most unions overflow it
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    layer = wl.num_layers - 1
+    q = gen.prefill_queries(wl, layer, 0, rows)
+    ctx = gen.context_lengths(wl)
+    rng = np.random.default_rng(5)
+    row_start = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    row_pos = np.concatenate([np.sort(rng.integers(0, int(ctx[b]), counts[b])) for b in range(wl.batch)])
+    row_pos = row_pos.astype(np.int32)
+    bt, npg = gen.block_tables(wl)
+    bias = gen.page_bias(wl)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    qd = dev(gen.to_bf16_bits(q).view(np.int16)).view(torch.bfloat16)
+    sel = torch.full((rows, wl.topk), -7, dtype=torch.int32, device="cuda")
+    needed = torch.full((wl.batch, C), -7, dtype=torch.int32, device="cuda")
+    drops0 = t.read_counters()["drops"]
+    for rep in range(2):      # the bitmaps are cleared after use: a second call gives the same
+        t.select_pages(layer, qd, dev(row_start), g.bt, g.n_pages, wl.topk, sel, needed,
+                       page_bias=g.bias, row_pos=dev(row_pos))
+        torch.cuda.synchronize()
+        ref_sel, ref_needed = o.select(layer, q, row_start, row_pos, bt, npg, wl.topk, bias=bias)
+        assert np.array_equal(sel.cpu().numpy(), ref_sel), f"call {rep}: sel"
+        assert np.array_equal(needed.cpu().numpy(), ref_needed), f"call {rep}: needed"
+    drops = t.read_counters()["drops"] - drops0
+    assert drops == o.drops > 0

@@ -53,7 +53,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_total;
 };
 
 static int validate(const tkv_config* c) {
@@ -127,6 +127,7 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_part = o; o = align256(o + (size_t)c->max_batch * c->num_q_heads * c->max_topk * (D + 4) * 4);
   L.ws_attn_done = o; o = align256(o + (size_t)c->max_batch * H * 4);
   L.ws_iota = o; o = align256(o + (R + 1) * 4);
+  L.ws_sel_bm = o; o = align256(o + sel_bm_words(R, c->max_batch, P) * 4);
   L.ws_total = o;
   return L;
 }
@@ -234,6 +235,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.attn_part = (float*)(ws + L.ws_part);
   d.attn_done = (int32_t*)(ws + L.ws_attn_done);
   d.iota = (int32_t*)(ws + L.ws_iota);
+  d.sel_bm = (uint32_t*)(ws + L.ws_sel_bm);
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
   d.max_batch = f.max_batch; d.max_width = f.max_width;
   hipStream_t s = (hipStream_t)stream;

@@ -209,12 +209,31 @@ __device__ __forceinline__ void init_state(WaveAttn& st) {
   st.l_run = 0.f;
 }
 
+}  // namespace
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  When
+// the KV heads divide the XCDs evenly, a workgroup covers 4 rows of one KV
+// head and XCD x only ever serves head x / (8 / Hkv): each L2 then caches one
+// head's blocks of the pages instead of all of them.
+constexpr int NXCD = 8;
+
+__host__ __device__ __forceinline__ bool attn_rows_by_xcd(int Hkv) { return Hkv <= NXCD && NXCD % Hkv == 0; }
+
 // one wave per (row, KV head), all of the row's pages
 __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int u = blockIdx.x * MWAVES + wave;
-  if (u >= a.rows * c.Hkv) return;
-  const int r = u / c.Hkv, g = u - r * c.Hkv;
+  int r, g;
+  if (attn_rows_by_xcd(c.Hkv)) {
+    const int per = NXCD / c.Hkv;                       // XCDs per KV head
+    const int x = blockIdx.x % NXCD, k = blockIdx.x / NXCD;
+    g = x / per;
+    r = (k * per + x % per) * MWAVES + wave;
+  } else {
+    const int u = blockIdx.x * MWAVES + wave;
+    r = u / c.Hkv;
+    g = u - r * c.Hkv;
+  }
+  if (r >= a.rows) return;
   const int b = attn_row_request(a, r);
   bf16x8 qop[4];
   load_query(a, c, r, g, lane, qop);
@@ -294,8 +313,6 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_split(DevCtx c, AttnArg
   attn_merge_splits(c, a, r, g, tid);
 }
 
-}  // namespace
-
 bool attn_mfma_supported(const DevCtx& c) {
   return c.fp8 && c.PS == MPS && c.D == MD && c.Hq == MG * c.Hkv;
 }
@@ -306,7 +323,12 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
   if (a.rows > c.max_batch || units >= 256) {
     a.splits = 1;
     a.pages_per_split = a.topk;
-    const int blocks = (int)((units + MWAVES - 1) / MWAVES);
+    int blocks = (int)((units + MWAVES - 1) / MWAVES);
+    if (attn_rows_by_xcd(c.Hkv)) {
+      const int per = NXCD / c.Hkv;
+      const int groups = (a.rows + MWAVES - 1) / MWAVES;   // row groups per head
+      blocks = NXCD * ((groups + per - 1) / per);
+    }
     hipLaunchKernelGGL(k_attn_mfma_rows, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a);
     return hipGetLastError();
   }

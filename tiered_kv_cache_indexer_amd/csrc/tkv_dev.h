@@ -59,11 +59,19 @@ struct DevCtx {
   float* attn_part;         // [max_batch][Hq][max_topk][D+2]
   int32_t* attn_done;       // [max_batch][Hkv]
   int32_t* iota;            // [max_rows + 1] = 0, 1, 2, ... (row_start of one-row-per-request calls)
+  uint32_t* sel_bm;         // page bitmaps of requests with several rows, one per group of 64 of
+                            // the request's rows: [max_rows/64 + max_batch][max_pages/32], kept at zero
   int max_rows, max_pages, max_topk, max_batch, max_width;
   int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
 };
 
 enum { ATTN_AUTO = 0, ATTN_VECTOR = 1, ATTN_MATRIX = 2 };
+
+// Words of the selection bitmaps: sum over requests of ceil(rows_b / 64)
+// groups is at most ceil(max_rows / 64) + max_batch.
+inline size_t sel_bm_words(size_t max_rows, size_t max_batch, size_t max_pages) {
+  return ((max_rows + 63) / 64 + max_batch) * ((max_pages + 31) / 32);
+}
 
 // ------------------------------------------------------------- call arguments --
 struct SelArgs {

@@ -156,6 +156,9 @@ hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st) {
     if ((e = fill_i32(c.row_done, c.max_rows, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.glob_done, 4, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.attn_done, (int64_t)c.max_batch * c.Hkv, 0, st)) != hipSuccess) return e;
+    if ((e = fill_i32(reinterpret_cast<int32_t*>(c.sel_bm),
+                      (int64_t)sel_bm_words(c.max_rows, c.max_batch, c.max_pages), 0, st)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k_iota_i32, dim3((c.max_rows + 256) / 256), dim3(256), 0, st, c.iota, (int64_t)c.max_rows + 1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

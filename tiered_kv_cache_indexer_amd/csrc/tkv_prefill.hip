@@ -6,7 +6,9 @@
 // per-group query sums qg [rows][Hkv*d] (bf16) times the slab rows of the
 // request's pages [pages][Hkv*d] (bf16, gathered through the block table).
 //
-// k_group_q forms qg = bf16(fp32(exact sum of the group's query heads)).
+// k_group_q forms qg = bf16(exact sum of the group's query heads): the fp64
+// sum of 8 bf16 values is exact, and so is its conversion to fp32 for values
+// on the query grid, so the bf16 rounding is the only one.
 // k_prefill_scores: one 256-thread workgroup per 64 rows x 64 pages; each wave
 // owns 32 x 32 outputs as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16.  Lane i of
 // a wave loads row (i % 16) of a 16 x 32 A tile and page (i % 16) of the
@@ -21,15 +23,31 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// thread = 8 consecutive features of one row's group sum (16-byte loads)
 __global__ __launch_bounds__(TKV_BLOCK) void k_group_q(DevCtx c, const uint16_t* q, int rows, uint16_t* qg) {
-  const int r = blockIdx.x;
   const int G = c.Hq / c.Hkv, E = c.Hkv * c.D;
-  for (int e = threadIdx.x; e < E; e += TKV_BLOCK) {
-    const int g = e / c.D, dd = e - g * c.D;
-    double acc = 0.0;
-    for (int h = 0; h < G; ++h) acc += (double)bf16_to_f32(q[((size_t)r * c.Hq + g * G + h) * c.D + dd]);
-    qg[(size_t)r * E + e] = f32_to_bf16((float)acc);
+  const int per_row = E / 8;
+  const int t = blockIdx.x * TKV_BLOCK + threadIdx.x;
+  const int r = t / per_row, e0 = (t - r * per_row) * 8;
+  if (r >= rows) return;
+  const int g = e0 / c.D, dd = e0 - g * c.D;
+  double acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int h = 0; h < G; ++h) {
+    const uint4 w = *reinterpret_cast<const uint4*>(q + ((size_t)r * c.Hq + g * G + h) * c.D + dd);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += (double)__uint_as_float(ww[i] << 16);
+      acc[2 * i + 1] += (double)__uint_as_float(ww[i] & 0xFFFF0000u);
+    }
   }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)f32_to_bf16((float)acc[2 * i]) | ((uint32_t)f32_to_bf16((float)acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(qg + (size_t)r * E + e0) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
@@ -105,7 +123,9 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_prefill_scores(DevCtx c, SelArgs 
 
 hipError_t launch_prefill_scores(const DevCtx& c, const SelArgs& a, hipStream_t st) {
   uint16_t* qg = c.qg;
-  hipLaunchKernelGGL(k_group_q, dim3(a.rows), dim3(TKV_BLOCK), 0, st, c, a.q, a.rows, qg);
+  const long threads = (long)a.rows * (c.Hkv * c.D / 8);
+  hipLaunchKernelGGL(k_group_q, dim3((unsigned)((threads + TKV_BLOCK - 1) / TKV_BLOCK)), dim3(TKV_BLOCK), 0, st, c,
+                     a.q, a.rows, qg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((a.max_pages + 63) / 64, (a.rows + 63) / 64);

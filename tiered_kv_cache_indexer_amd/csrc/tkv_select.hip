@@ -138,16 +138,56 @@ __device__ void row_topk64_block(int n_lists, int k, int32_t* out, uint64_t* lds
 }
 
 // Union of request b's rows, ascending, unique; first C kept, rest counted.
+// Bitmap group of row r of request b: each request's rows are cut into groups
+// of 64, the groups of earlier requests first.
+__device__ __forceinline__ int sel_bm_group(const SelArgs& a, int b, int r) {
+  int g = 0;
+  for (int bb = 0; bb < b; ++bb) g += (a.row_start[bb + 1] - a.row_start[bb] + 63) >> 6;
+  return g + ((r - a.row_start[b]) >> 6);
+}
+
+// Called by the whole block once row r's selection is written: marks its pages
+// in its group's bitmap (requests with several rows only), so that the union
+// is a few bitmaps to OR instead of every row's list to re-read.
+__device__ void mark_row_pages(const DevCtx& c, const SelArgs& a, int b, int r) {
+  if (a.row_start[b + 1] - a.row_start[b] <= 1) return;
+  __syncthreads();
+  const int words = (a.max_pages + 31) >> 5;
+  uint32_t* bm = c.sel_bm + (size_t)sel_bm_group(a, b, r) * words;
+  for (int j = threadIdx.x; j < a.topk; j += TKV_BLOCK) {
+    const int i = a.sel_local[(size_t)r * a.topk + j];
+    if (i >= 0 && i < a.max_pages) atomicOr(&bm[i >> 5], 1u << (i & 31));
+  }
+}
+
+// Union of a multi-row request's selections: OR of its group bitmaps (which
+// are cleared again), ascending local ids, first C kept, the rest counted as
+// drops, translated through the block table.
 __device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t* bm, int* sm_scan) {
   const int tid = threadIdx.x;
   const int words = (a.max_pages + 31) >> 5;
   for (int w = tid; w < words; w += TKV_BLOCK) bm[w] = 0;
   __syncthreads();
   const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
-  const int total = (r1 - r0) * a.topk;
-  for (int idx = tid; idx < total; idx += TKV_BLOCK) {
-    int i = a.sel_local[(size_t)r0 * a.topk + idx];
-    if (i >= 0 && i < a.max_pages) atomicOr(&bm[i >> 5], 1u << (i & 31));
+  const int ng = (r1 - r0 + 63) >> 6;
+  uint32_t* gbm = c.sel_bm + (size_t)sel_bm_group(a, b, r0) * words;
+  const int tot = ng * words;
+  constexpr int U = 8;
+  for (int base = 0; base < tot; base += TKV_BLOCK * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * TKV_BLOCK + tid;
+      v[u] = idx < tot ? gbm[idx] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * TKV_BLOCK + tid;
+      if (idx < tot) {
+        if (v[u]) atomicOr(&bm[idx % words], v[u]);
+        gbm[idx] = 0u;
+      }
+    }
   }
   __syncthreads();
   const int WPT = (words + TKV_BLOCK - 1) / TKV_BLOCK;
@@ -172,10 +212,6 @@ __device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t
   __syncthreads();
 }
 
-// After the ensure: translated slots of every row's selection (fused decode).
-// A request with one row whose selection fits the compaction width has
-// needed[b][j] = block_table[b][sel[j]], so its slots are the ensure's
-// out_slots[b*C + j]; other requests translate through the page->slot map.
 __device__ void write_sel_slots(const DevCtx& c, const SelArgs& a) {
   for (int b = 0; b < a.B; ++b) {
     const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
@@ -342,11 +378,16 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   } else {
     row_topk_block(sc, visible, a.topk, a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
   }
+  mark_row_pages(c, a, b, r);
   if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
   select_finish(c, a, dyn, sm_scan);
 }
 
 // Tail-only launch: scores already in the workspace (prefill scoring kernel).
+// One workgroup per row; the union and compaction run in k_select_finish
+// after it.  With thousands of rows a last-workgroup hand-off would cost every
+// workgroup an L2 write-back (the release between XCDs); the kernel boundary
+// pays it once.
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows(DevCtx c, SelArgs a) {
   extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ int hist[256];
@@ -356,7 +397,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows(DevCtx c, SelArgs a) 
   const int r = blockIdx.x, lane = threadIdx.x & 63;
   if (threadIdx.x == 0) sm_b = request_of_row(a.row_start, a.B, r);
   __syncthreads();
-  const int visible = visible_pages(a, c.PS, sm_b, r);
+  const int b = sm_b;
+  const int visible = visible_pages(a, c.PS, b, r);
   const float* sc = c.scores + (size_t)r * c.max_pages;
   if (a.topk <= 64) {
     const int n_lists = (visible + 63) / 64;
@@ -368,7 +410,79 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows(DevCtx c, SelArgs a) 
   } else {
     row_topk_block(sc, visible, a.topk, a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
   }
-  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+  mark_row_pages(c, a, b, r);
+}
+
+// Wave count of a per-lane count below 2^6: one ballot per bit.
+__device__ __forceinline__ int wave_count6(int cnt) {
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < 6; ++j) tot += __popcll(__ballot((cnt >> j) & 1)) << j;
+  return tot;
+}
+
+// One wave per row, keys of up to 64*NPL visible pages in registers.  The
+// k-th largest key T is found by a radix descent from the top bit: a bit is
+// kept when at least k keys are >= the prefix with it set, and the descent
+// stops early once exactly k keys are >= the prefix.  Keys are unique (the
+// low word is ~page), so exactly min(k, visible) keys are >= T; they are
+// written in ascending page order by ballot prefix counts.
+template <int NPL>
+__global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * (TKV_BLOCK / 64) + (threadIdx.x >> 6);
+  if (r >= a.rows) return;
+  const int b = request_of_row(a.row_start, a.B, r);
+  const int visible = visible_pages(a, c.PS, b, r);
+  const int nl = (visible + 63) >> 6;
+  const float* sc = c.scores + (size_t)r * c.max_pages;
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int p = i * 64 + lane;
+    key[i] = (i < nl && p < visible) ? sel_key(sc[p], p) : 0ull;   // valid keys are nonzero
+  }
+  const int k = a.topk;
+  uint64_t thr = 1;
+  if (visible > k) {
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (i < nl) cnt += key[i] >= cand ? 1 : 0;
+      const int tot = wave_count6(cnt);
+      if (tot >= k) {
+        t = cand;
+        if (tot == k) break;
+      }
+    }
+    thr = t;
+  }
+  int32_t* out = a.sel_local + (size_t)r * k;
+  const bool multi = a.row_start[b + 1] - a.row_start[b] > 1;
+  uint32_t* bm = multi ? c.sel_bm + (size_t)sel_bm_group(a, b, r) * ((a.max_pages + 31) >> 5) : nullptr;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    if (i >= nl) break;
+    const bool s = key[i] >= thr;
+    const uint64_t m = __ballot(s);
+    if (s) {
+      const int p = i * 64 + lane;
+      out[base + __popcll(m & below)] = p;
+      if (bm) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    }
+    base += __popcll(m);
+  }
+  for (int j = base + lane; j < k; j += 64) out[j] = -1;
+}
+
+__global__ __launch_bounds__(TKV_BLOCK) void k_select_finish(DevCtx c, SelArgs a) {
+  extern __shared__ __align__(16) uint32_t dyn[];
+  __shared__ int sm_scan[8];
   select_finish(c, a, dyn, sm_scan);
 }
 
@@ -400,7 +514,14 @@ hipError_t launch_select_scan(const DevCtx& c, const SelArgs& a, hipStream_t st)
 }
 
 hipError_t launch_select_rows(const DevCtx& c, const SelArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_select_rows, dim3(a.rows), dim3(TKV_BLOCK), select_dyn_lds(c), st, c, a);
+  const dim3 wgrid((a.rows + 3) / 4);
+  if (a.max_pages <= 512) hipLaunchKernelGGL(k_select_rows_wave<8>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
+  else if (a.max_pages <= 1024) hipLaunchKernelGGL(k_select_rows_wave<16>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
+  else if (a.max_pages <= 2048) hipLaunchKernelGGL(k_select_rows_wave<32>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
+  else hipLaunchKernelGGL(k_select_rows, dim3(a.rows), dim3(TKV_BLOCK), select_dyn_lds(c), st, c, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_finish, dim3(1), dim3(TKV_BLOCK), select_dyn_lds(c), st, c, a);
   return hipGetLastError();
 }
 

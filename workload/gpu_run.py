@@ -23,7 +23,7 @@ def _dev(x, dtype):
 
 
 class GpuWorkload:
-    def __init__(self, wl: Workload):
+    def __init__(self, wl: Workload, max_rows: int | None = None):
         self.wl = wl
         B = wl.batch
         C = wl.max_sel_pages
@@ -40,7 +40,7 @@ class GpuWorkload:
             num_layers=wl.num_layers, num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
             head_dim=wl.head_dim, page_size=wl.page_size, kv_format=wl.kv_format,
             num_logical_pages=wl.num_logical_pages, num_slots=wl.num_slots, max_batch=B,
-            max_rows=max(B, wl.prefill_tokens), max_topk=wl.topk, max_pages_per_req=wl.max_pages,
+            max_rows=max(B, wl.prefill_tokens, max_rows or 0), max_topk=wl.topk, max_pages_per_req=wl.max_pages,
             max_width=width)
         self.C = self.tier.set_select_width(B, wl.topk, wl.max_sel_pages)
         L = wl.num_layers
