@@ -178,8 +178,14 @@ class OracleTier:
                 self._lazy_pool[int(slot)] = (int(page), self.mirror_row(int(page)).copy())
             self.bytes_fetched += self.lay.row_bytes
 
-    def gather_kv(self, layer, b, sel_row, block_table, ctx_len, row_pos=None):
-        """Dequantised K, V [Hkv][T][d] of the selected resident pages' visible tokens."""
+    def gather_kv(self, layer, b, sel_row, block_table, ctx_len, row_pos=None, host_tail=False):
+        """Dequantised K, V [Hkv][T][d] of the selected pages' visible tokens.
+
+        Resident pages are read from their pool slot.  A page that is not
+        resident is skipped, or with ``host_tail`` read in place from its
+        mirror row (vLLM RFC #33980, discussion: the tail of the KV space is
+        host memory that the attention kernel loads over the interconnect,
+        with no staging copy; only this layer's block of the row is used)."""
         ks, vs = [], []
         limit = int(ctx_len[b]) if row_pos is None else min(int(ctx_len[b]), int(row_pos) + 1)
         for i in sel_row:
@@ -187,12 +193,13 @@ class OracleTier:
                 continue
             page = int(block_table[b][i])
             slot = int(self.lru.page_to_slot[page])
-            if slot < 0:
+            if slot < 0 and not host_tail:
                 continue
             n = min(self.ps, limit - int(i) * self.ps)
             if n <= 0:
                 continue
-            k, v = read_kv(self.pool_row(slot), self.lay, layer)
+            row = self.pool_row(slot) if slot >= 0 else self.mirror_row(page)
+            k, v = read_kv(row, self.lay, layer)
             ks.append(k[:, :n])
             vs.append(v[:, :n])
         if not ks:
@@ -200,16 +207,16 @@ class OracleTier:
             return z, z
         return np.concatenate(ks, axis=1), np.concatenate(vs, axis=1)
 
-    def attention_row(self, layer, q_row, b, sel_row, block_table, ctx_len, row_pos=None):
-        k, v = self.gather_kv(layer, b, sel_row, block_table, ctx_len, row_pos)
+    def attention_row(self, layer, q_row, b, sel_row, block_table, ctx_len, row_pos=None, host_tail=False):
+        k, v = self.gather_kv(layer, b, sel_row, block_table, ctx_len, row_pos, host_tail)
         return attend(q_row.astype(np.float64), k, v)
 
-    def attention(self, layer, q, row_start, row_pos, ctx_len, sel, block_table):
+    def attention(self, layer, q, row_start, row_pos, ctx_len, sel, block_table, host_tail=False):
         out = np.zeros(q.shape, dtype=np.float64)
         for b in range(len(row_start) - 1):
             for r in range(row_start[b], row_start[b + 1]):
                 pos = None if row_pos is None else row_pos[r]
-                out[r] = self.attention_row(layer, q[r], b, sel[r], block_table, ctx_len, pos)
+                out[r] = self.attention_row(layer, q[r], b, sel[r], block_table, ctx_len, pos, host_tail)
         return out
 
     def decode_layer(self, layer, q, row_start, block_table, n_pages, ctx_len, topk,
@@ -220,6 +227,15 @@ class OracleTier:
         out = (self.attention(layer, q, row_start, row_pos, ctx_len, sel, block_table)
                if with_attention else None)
         return dict(sel=sel, needed=needed, out_slots=out_slots, misses=misses, out=out)
+
+    def decode_layer_host_tail(self, layer, q, row_start, block_table, n_pages, ctx_len, topk,
+                               bias=None, row_pos=None):
+        """The decode layer with the host tail read in place: selection and
+        compaction as usual, no ensure and no fetch (the residency state does
+        not move), attention over pool slots and mirror rows."""
+        sel, needed = self.select(layer, q, row_start, row_pos, block_table, n_pages, topk, bias)
+        out = self.attention(layer, q, row_start, row_pos, ctx_len, sel, block_table, host_tail=True)
+        return dict(sel=sel, needed=needed, out=out)
 
     def counters(self):
         c = dict(self.lru.counters)

@@ -139,3 +139,57 @@ def test_prefill_chain_small():
         assert sel[0].max() <= n0
         assert np.all(rec["out_slots"][rec["needed"][0] >= 0] >= 0)
     assert tier.counters()["error_word"] == 0
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_host_tail_with_empty_pool_equals_dense(fmt):
+    """Host tail read in place: with nothing resident every selected page comes
+    from its mirror row, and with the budget covering the context the output
+    is dense attention over the quantised keys and values."""
+    base = get_workload("c1")
+    wl = replace(base, kv_format=fmt, contexts=(256,), topk=16, num_slots=48, steps=1)
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    tier.reset_residency()
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    tier.set_select_width(1, wl.topk, wl.max_sel_pages)
+    rec = tier.decode_layer_host_tail(0, q[0, 0], np.array([0, 1]), bt, npg, ctx, wl.topk)
+    assert not np.any(tier.lru.page_to_slot >= 0)          # nothing was made resident
+    k = gen.kv_tokens(wl, gen.KIND_K, 0, 0, 0, 256)
+    v = gen.kv_tokens(wl, gen.KIND_V, 0, 0, 0, 256)
+    if fmt == "fp8":
+        kc, ks = quantize_tokens(k)
+        vc, vs = quantize_tokens(v)
+        k = e4m3_decode(kc).astype(np.float64) * ks[:, None, None]
+        v = e4m3_decode(vc).astype(np.float64) * vs[:, None, None]
+    ref = dense_reference(q[0, 0, 0].astype(np.float64), k.transpose(1, 0, 2).astype(np.float64),
+                          v.transpose(1, 0, 2).astype(np.float64))
+    assert np.allclose(rec["out"][0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_host_tail_leaves_residency_and_matches_fetch_path():
+    """The in-place read gives the fetch path's output exactly (mirror rows
+    hold the pool's bytes) and moves no residency state."""
+    wl = get_workload("c3s")
+    a = run.make_tier(wl, materialize=True)
+    b = run.make_tier(wl, materialize=True)
+    run.setup(wl, a)
+    run.setup(wl, b)
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.array([0, 1])
+    for t in (a, b):
+        t.set_select_width(1, wl.topk, wl.max_sel_pages)
+    state = (b.lru.page_to_slot.copy(), b.lru.stamp.copy(), b.lru.clock, dict(b.lru.counters))
+    for layer in range(wl.num_layers):
+        ra = a.decode_layer(layer, q[0, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+        rb = b.decode_layer_host_tail(layer, q[0, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+        assert np.array_equal(ra["sel"], rb["sel"]) and np.array_equal(ra["needed"], rb["needed"])
+        assert np.array_equal(ra["out"], rb["out"])
+    assert a.lru.counters["misses"] > 0                     # the fetch path did move pages
+    assert np.array_equal(b.lru.page_to_slot, state[0]) and np.array_equal(b.lru.stamp, state[1])
+    assert b.lru.clock == state[2] and dict(b.lru.counters) == state[3]
