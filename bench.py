@@ -195,6 +195,42 @@ def cpu_baseline(wl, nsteps):
                         f"host has {cores} cores"))
 
 
+def bench_host_tail(torch, g, s0, steps):
+    """Decode steps with the host tail read in place (tkv_select_pages +
+    tkv_sparse_paged_attn_host_tail per layer; no ensure, no fetch), on the
+    pool as the fetch path left it.  Host bytes per step = selected pages that
+    are not resident x one layer's block of the row."""
+    import numpy as np
+    wl, t = g.wl, g.tier
+    n_q = g.q.shape[0]
+    for i in range(2):
+        g.decode_step_host_tail((s0 + i) % n_q)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        g.decode_step_host_tail((s0 + 2 + i) % n_q)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    p2s = t.read_state()["page_to_slot"]
+    sel = g.sel.cpu().numpy()
+    bt = g.bt_np
+    host_pages = 0
+    for layer in range(wl.num_layers):
+        for b in range(wl.batch):
+            for i in sel[layer, b]:
+                if i >= 0 and p2s[bt[b][i]] < 0:
+                    host_pages += 1
+    host_bytes = host_pages * t.layer_bytes
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 2),
+            "host_pages_last_step": host_pages, "host_bytes_last_step": host_bytes,
+            "host_read_GBps_lower_bound": round(host_bytes / (ms * 1e-3) / 1e9, 2),
+            "note": "select_pages + sparse_paged_attn_host_tail per layer (no ensure, no fetch); "
+                    "pool as the fetch path left it; GB/s = last step's host bytes / mean step time"}
+
+
 def bench_prefill(args, torch):
     """c5: one 4,096-token prefill chunk over 65,536 cached tokens, 12 layers:
     write-ensure, then per layer store (write-through) -> select (matrix-core
@@ -408,6 +444,9 @@ def main():
         "launch": "hip graph per step" if args.graph else "eager, one C call per layer",
         "error_word": err,
     }
+    result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
+                                          min(args.steps, 50))
+    log(f"[bench] host tail {result['host_tail']}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_steps)

@@ -198,6 +198,21 @@ int tkv_sparse_paged_attn(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_
                           const int32_t* block_table, int32_t max_pages, int32_t topk,
                           uint16_t* out, void* stream);
 
+/* Sparse paged attention with the host tail read in place (vLLM RFC #33980,
+ * discussion: KV beyond the HBM tier is host memory that the attention
+ * kernel loads over the interconnect, with no staging copy).  Arguments and
+ * results as tkv_sparse_paged_attn; a selected page that is not resident is
+ * read from its mirror row (this layer's block only: K and V codes and
+ * scales, 66,048 bytes at 4 KV heads x d 128 x 64-token fp8 pages) instead of
+ * being skipped.  Nothing is fetched, no slot is bound, the LRU state and the
+ * counters do not move, so a step built from tkv_select_pages and this call
+ * leaves the pool as it was.  Mirror rows of pages never written read as
+ * zeros. */
+int tkv_sparse_paged_attn_host_tail(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t rows,
+                                    const int32_t* row_start, const int32_t* row_pos, const int32_t* ctx_len,
+                                    int32_t B, const int32_t* sel_local, const int32_t* block_table,
+                                    int32_t max_pages, int32_t topk, uint16_t* out, void* stream);
+
 /* One decode step of one layer for B requests with one query row each:
  * select + compact + ensure in one launch, then fetch, then attention.
  * Same semantics as tkv_select_pages -> tkv_lru_ensure(needed, B*C) ->

@@ -340,10 +340,10 @@ int tkv_fetch_pages(tkv_ctx* c, const int32_t* miss, const int32_t* miss_count, 
   return TKV_OK;
 }
 
-int tkv_sparse_paged_attn(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
-                          const int32_t* row_start, const int32_t* row_pos, const int32_t* ctx_len,
-                          int32_t B, const int32_t* sel_local, const int32_t* block_table,
-                          int32_t max_pages, int32_t topk, uint16_t* out, void* stream) {
+static int attn_call(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows, const int32_t* row_start,
+                     const int32_t* row_pos, const int32_t* ctx_len, int32_t B, const int32_t* sel_local,
+                     const int32_t* block_table, int32_t max_pages, int32_t topk, uint16_t* out, void* stream,
+                     int host_tail) {
   int rc = need_attached(c);
   if (rc) return rc;
   if ((rc = check_rows(c, layer, rows, B, max_pages, topk))) return rc;
@@ -354,9 +354,25 @@ int tkv_sparse_paged_attn(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t 
   AttnArgs a{};
   a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
   a.ctx_len = ctx_len; a.sel = sel_local; a.bt = block_table; a.max_pages = max_pages; a.topk = topk;
-  a.B = B; a.out = out;
+  a.B = B; a.out = out; a.host_tail = host_tail;
   HIPCHECK(launch_attn(c->dev, a, (hipStream_t)stream), "sparse_paged_attn launch");
   return TKV_OK;
+}
+
+int tkv_sparse_paged_attn(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
+                          const int32_t* row_start, const int32_t* row_pos, const int32_t* ctx_len,
+                          int32_t B, const int32_t* sel_local, const int32_t* block_table,
+                          int32_t max_pages, int32_t topk, uint16_t* out, void* stream) {
+  return attn_call(c, layer, q, rows, row_start, row_pos, ctx_len, B, sel_local, block_table, max_pages, topk,
+                   out, stream, 0);
+}
+
+int tkv_sparse_paged_attn_host_tail(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
+                                    const int32_t* row_start, const int32_t* row_pos, const int32_t* ctx_len,
+                                    int32_t B, const int32_t* sel_local, const int32_t* block_table,
+                                    int32_t max_pages, int32_t topk, uint16_t* out, void* stream) {
+  return attn_call(c, layer, q, rows, row_start, row_pos, ctx_len, B, sel_local, block_table, max_pages, topk,
+                   out, stream, 1);
 }
 
 int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, const int32_t* block_table,

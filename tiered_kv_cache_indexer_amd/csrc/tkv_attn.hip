@@ -43,7 +43,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
   __shared__ float sS[G][PS];
   __shared__ __align__(16) float sP[PS][G];
   __shared__ float sAlpha[G], sM[G], sL[G];
-  __shared__ int sSlot[ATT_MAXP], sNtok[ATT_MAXP];
+  __shared__ const uint8_t* sBase[ATT_MAXP];
+  __shared__ int sNtok[ATT_MAXP];
   __shared__ int sb;
   __shared__ int sflag[2];
   __shared__ __align__(16) float sRed[G][D];
@@ -66,23 +67,29 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
   int limit = a.ctx_len[b];
   if (a.row_pos) limit = min(limit, a.row_pos[r] + 1);
 
-  // resolve the split's pages: local id -> logical -> slot, visible tokens
+  // resolve the split's pages: local id -> logical -> pool slot (or, for the
+  // host tail, the page's mirror row), visible tokens
   for (int jj = tid; jj < np && jj < ATT_MAXP; jj += TKV_BLOCK) {
     const int i = a.sel[(size_t)r * a.topk + j0 + jj];
-    int slot = -1, nt = 0;
+    const uint8_t* base = nullptr;
+    int nt = 0;
     if (a.slots) {
       const int s = a.slots[(size_t)r * a.topk + j0 + jj];
       if (i >= 0 && s >= 0 && s < c.S) {
-        slot = s;
+        base = c.pool + (size_t)s * c.row_bytes;
         nt = min(PS, limit - i * PS);
       }
     } else if (i >= 0 && i < a.max_pages) {
       const int page = a.bt[(size_t)b * a.max_pages + i];
-      if (page >= 0 && (int64_t)page < c.N) slot = c.page_to_slot[page];
+      if (page >= 0 && (int64_t)page < c.N) {
+        const int slot = c.page_to_slot[page];
+        if (slot >= 0) base = c.pool + (size_t)slot * c.row_bytes;
+        else if (a.host_tail) base = c.mirror + (size_t)page * c.row_bytes;
+      }
       nt = min(PS, limit - i * PS);
     }
-    sSlot[jj] = slot;
-    sNtok[jj] = (slot >= 0 && nt > 0) ? nt : 0;
+    sBase[jj] = base;
+    sNtok[jj] = (base && nt > 0) ? nt : 0;
   }
 
   // query slice in registers, pre-scaled for exp2
@@ -112,9 +119,9 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
   __syncthreads();
 
   for (int jj = 0; jj < np && jj < ATT_MAXP; ++jj) {
-    const int slot = sSlot[jj], nt = sNtok[jj];
+    const int nt = sNtok[jj];
     if (nt <= 0) continue;  // uniform
-    const uint8_t* blk = c.pool + (size_t)slot * c.row_bytes + (size_t)a.layer * c.layer_bytes;
+    const uint8_t* blk = sBase[jj] + (size_t)a.layer * c.layer_bytes;
     const uint8_t* kb = blk + (size_t)g * PS * D * ELT;
     const uint8_t* vb = blk + (size_t)c.code_bytes + (size_t)g * PS * D * ELT;
     // stage V codes and the scales

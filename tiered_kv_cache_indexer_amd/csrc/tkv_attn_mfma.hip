@@ -156,33 +156,42 @@ __device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, i
   int limit = a.ctx_len[b];
   if (a.row_pos) limit = min(limit, a.row_pos[r] + 1);
   const float qscale = 1.4426950408889634f / sqrtf((float)MD);
-  const uint8_t* pool_l = c.pool + (size_t)a.layer * c.layer_bytes;
   const size_t cb = (size_t)c.code_bytes;
   for (int base = jbeg; base < jend; base += 64 * jstep) {
-    // lane i resolves page base + i*jstep: local id -> slot, visible tokens
+    // lane i resolves page base + i*jstep: local id -> pool slot (or, for
+    // the host tail, the page's mirror row), visible tokens
     const int j = base + lane * jstep;
-    int slot = -1, nt = 0;
+    const uint8_t* row = nullptr;
+    int nt = 0;
     if (j < jend) {
       const int i = a.sel[(size_t)r * a.topk + j];
       if (a.slots) {
         const int s = a.slots[(size_t)r * a.topk + j];
         if (i >= 0 && s >= 0 && s < c.S) {
-          slot = s;
+          row = c.pool + (size_t)s * c.row_bytes;
           nt = min(MPS, limit - i * MPS);
         }
       } else if (i >= 0 && i < a.max_pages) {
         const int page = a.bt[(size_t)b * a.max_pages + i];
-        if (page >= 0 && (int64_t)page < c.N) slot = c.page_to_slot[page];
+        if (page >= 0 && (int64_t)page < c.N) {
+          const int slot = c.page_to_slot[page];
+          if (slot >= 0) row = c.pool + (size_t)slot * c.row_bytes;
+          else if (a.host_tail) row = c.mirror + (size_t)page * c.row_bytes;
+        }
         nt = min(MPS, limit - i * MPS);
       }
-      if (slot < 0) nt = 0;
+      if (!row) nt = 0;
     }
+    const uint64_t rowv = reinterpret_cast<uint64_t>(row);
+    const uint32_t row_lo = (uint32_t)rowv, row_hi = (uint32_t)(rowv >> 32);
     const int cnt = min(64, (jend - base + jstep - 1) / jstep);
     for (int i = 0; i < cnt; ++i) {
-      const int sl = __builtin_amdgcn_readlane(slot, i);
       const int n = __builtin_amdgcn_readlane(nt, i);
       if (n <= 0) continue;
-      wave_page(pool_l + (size_t)sl * c.row_bytes, cb, g, n, lane, qop, qscale, st);
+      const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, i) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)row_lo, i);
+      wave_page(reinterpret_cast<const uint8_t*>(pv) + (size_t)a.layer * c.layer_bytes, cb, g, n, lane, qop,
+                qscale, st);
     }
   }
 }

@@ -123,8 +123,9 @@ class TieredKV:
                                        _ptr(miss_count, torch.int32, "miss_count"), width, _stream(stream)))
 
     def sparse_paged_attn(self, layer, q, row_start, ctx_len, sel_local, block_table, out,
-                          row_pos=None, stream=None):
-        check(self.lib.tkv_sparse_paged_attn(
+                          row_pos=None, stream=None, host_tail=False):
+        fn = self.lib.tkv_sparse_paged_attn_host_tail if host_tail else self.lib.tkv_sparse_paged_attn
+        check(fn(
             self.ctx, layer, _ptr(q, torch.bfloat16, "q"), q.shape[0],
             _ptr(row_start, torch.int32, "row_start"), _ptr(row_pos, torch.int32, "row_pos"),
             _ptr(ctx_len, torch.int32, "ctx_len"), ctx_len.shape[0],

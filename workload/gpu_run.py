@@ -51,6 +51,7 @@ class GpuWorkload:
         self.miss_count = torch.zeros((L, 1), dtype=torch.int32, device="cuda")
         self.out = torch.zeros((L, B, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
         self.q = None
+        self.row_start = torch.arange(B + 1, dtype=torch.int32, device="cuda")
 
     # -------------------------------------------------------------- setup --
     def setup(self):
@@ -93,6 +94,18 @@ class GpuWorkload:
                                    self.sel[layer], self.needed[layer], self.out_slots[layer],
                                    self.miss[layer], self.miss_count[layer], self.out[layer],
                                    page_bias=self.bias, stream=stream)
+
+    def decode_step_host_tail(self, s, q=None, stream=None):
+        """One decode step with the host tail read in place: per layer,
+        select_pages then the attention that reads non-resident pages from
+        their mirror rows.  No ensure, no fetch: the pool does not change."""
+        wl, t = self.wl, self.tier
+        q = self.q if q is None else q
+        for layer in range(wl.num_layers):
+            t.select_pages(layer, q[s, layer], self.row_start, self.bt, self.n_pages, wl.topk, self.sel[layer],
+                           self.needed[layer], page_bias=self.bias, stream=stream)
+            t.sparse_paged_attn(layer, q[s, layer], self.row_start, self.ctx_len, self.sel[layer], self.bt,
+                                self.out[layer], stream=stream, host_tail=True)
 
     # ------------------------------------------------------------ prefill --
     def prefill_buffers(self):
