@@ -73,9 +73,30 @@ def store_run(tier, layer, b, start, length, k, v, bt):
     tier.store(layer, [(b, start, length)], k, v, bt)
 
 
+def append_token(wl: Workload, tier: OracleTier, s: int, layer: int, bt):
+    """Write step s's appended token of every request for one layer: the
+    write-ensure of its page, then the store (write-through, slab update).
+
+    Reading taken: the write-ensure runs for each layer right before that
+    layer's store (a batched call over the requests), so the target page is
+    resident when it is written even if earlier layers' ensures evicted it;
+    the request's old length counts the new token as present once layer 0
+    has written it, so a page that holds earlier layers' bytes is fetched,
+    never allocated blank."""
+    ctx = gen.context_lengths(wl)
+    runs = [(b, int(ctx[b]) + s, 1) for b in range(wl.batch)]
+    old = [int(ctx[b]) + s + (1 if layer > 0 else 0) for b in range(wl.batch)]
+    tier.ensure_write_pages(runs, bt, old)
+    k = np.concatenate([gen.kv_tokens(wl, gen.KIND_K, layer, b, int(ctx[b]) + s, 1) for b in range(wl.batch)])
+    v = np.concatenate([gen.kv_tokens(wl, gen.KIND_V, layer, b, int(ctx[b]) + s, 1) for b in range(wl.batch)])
+    tier.store(layer, runs, k, v, bt)
+
+
 def decode(wl: Workload, tier: OracleTier, steps=None, attention=False, on_layer=None):
     """Run decode steps; returns a list over steps of lists over layers of the
-    per-layer record (sel, needed, out_slots, misses[, out])."""
+    per-layer record (sel, needed, out_slots, misses[, out]).  Appending
+    workloads write each step's new token before every layer's selection and
+    attend over the grown context."""
     bt, npg = gen.block_tables(wl)
     ctx = gen.context_lengths(wl)
     bias = gen.page_bias(wl)
@@ -86,7 +107,11 @@ def decode(wl: Workload, tier: OracleTier, steps=None, attention=False, on_layer
     nsteps = wl.steps if steps is None else steps
     for s in range(nsteps):
         per_layer = []
+        if wl.append:
+            ctx, npg = gen.append_lengths(wl, s)
         for layer in range(wl.num_layers):
+            if wl.append:
+                append_token(wl, tier, s, layer, bt)
             rec = tier.decode_layer(layer, q[s, layer], row_start, bt, npg, ctx, wl.topk,
                                     bias=bias, with_attention=attention)
             if on_layer is not None:

@@ -193,3 +193,61 @@ def test_host_tail_leaves_residency_and_matches_fetch_path():
     assert a.lru.counters["misses"] > 0                     # the fetch path did move pages
     assert np.array_equal(b.lru.page_to_slot, state[0]) and np.array_equal(b.lru.stamp, state[1])
     assert b.lru.clock == state[2] and dict(b.lru.counters) == state[3]
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_append_decode_attends_over_grown_context(fmt):
+    """Decode with one appended token per step: with the budget covering the
+    context, every layer's output is dense attention over all tokens written
+    so far, the new one included (stored before the layer's selection)."""
+    base = get_workload("c1")
+    wl = replace(base, kv_format=fmt, contexts=(200,), topk=16, num_slots=48, steps=3, append=True,
+                 num_layers=2)
+    assert wl.pages_of(0) == 13
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+    tr = run.decode(wl, tier, attention=True)
+    q = gen.decode_queries(wl)
+    for s in range(wl.steps):
+        n = 200 + s + 1
+        for layer in range(wl.num_layers):
+            k = gen.kv_tokens(wl, gen.KIND_K, layer, 0, 0, n)
+            v = gen.kv_tokens(wl, gen.KIND_V, layer, 0, 0, n)
+            if fmt == "fp8":
+                kc, ks = quantize_tokens(k)
+                vc, vs = quantize_tokens(v)
+                k = e4m3_decode(kc).astype(np.float64) * ks[:, None, None]
+                v = e4m3_decode(vc).astype(np.float64) * vs[:, None, None]
+            out = tr[s][layer]["out"][0]
+            for h in (0, 5):
+                ref = dense_reference(q[s, layer, 0, h:h + 1].astype(np.float64),
+                                      k.transpose(1, 0, 2).astype(np.float64),
+                                      v.transpose(1, 0, 2).astype(np.float64))
+                assert np.allclose(out[h], ref[0], rtol=1e-12, atol=1e-12), (s, layer, h)
+    _check_drop_clean(tier)
+
+
+def test_append_under_thrash_keeps_pool_rows_clean():
+    """Appending on the thrashing small workload: every layer's write-ensure
+    brings the page back if an earlier layer evicted it, so after each step
+    (every layer has written its block of a freshly allocated page) resident
+    pool rows equal their mirror rows, and the mirror holds every appended
+    token."""
+    wl = get_workload("c3sa")
+    tier = run.make_tier(wl, materialize=True)
+    run.setup(wl, tier)
+
+    def at_layer(s, layer, rec):
+        if layer == wl.num_layers - 1:
+            _check_drop_clean(tier)
+
+    run.decode(wl, tier, on_layer=at_layer)
+    assert tier.lru.counters["evictions"] > 0
+    bt, _ = gen.block_tables(wl)
+    from oracle.store import read_kv
+    last = wl.contexts[0] + wl.steps - 1
+    page = int(bt[0][last // wl.page_size])
+    k, _ = read_kv(tier.mirror_row(page), tier.lay, wl.num_layers - 1)
+    kc, ks = quantize_tokens(gen.kv_tokens(wl, gen.KIND_K, wl.num_layers - 1, 0, last, 1))
+    ref = e4m3_decode(kc).astype(np.float64) * ks[:, None, None]
+    assert np.array_equal(k[:, last % wl.page_size], ref[0])

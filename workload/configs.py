@@ -30,6 +30,7 @@ class Workload:
     permute_pages: bool = False
     setup_chunk: int = 4096   # tokens written per setup call
     prefill_tokens: int = 0   # >0: one prefill chunk of this many new tokens
+    append: bool = False      # decode steps append one token per request
     zipf_s: float = 1.1
     description: str = field(default="", compare=False)
 
@@ -43,8 +44,9 @@ class Workload:
         return self.num_q_heads // self.num_kv_heads
 
     def pages_of(self, b: int) -> int:
-        """Pages request b holds after setup (and after the prefill chunk)."""
-        toks = self.contexts[b] + (self.prefill_tokens if b == 0 else 0)
+        """Pages request b holds after setup (and after the prefill chunk, or
+        after the last appended decode token)."""
+        toks = self.contexts[b] + (self.prefill_tokens if b == 0 else 0) + (self.steps if self.append else 0)
         return -(-toks // self.page_size)
 
     @property
@@ -108,6 +110,14 @@ WORKLOADS.update({
                    num_slots=160, num_layers=2, steps=5, setup_chunk=2048, topk=8),
     "c5s": replace(WORKLOADS["c5"], name="c5_small_prefill", contexts=(4096,), prefill_tokens=512,
                    num_slots=160, num_layers=2, setup_chunk=2048, topk=8),
+})
+
+# Decode with one appended token per request per step (the new token's K/V
+# stored with write-through before each layer's selection).
+WORKLOADS.update({
+    "c3a": replace(WORKLOADS["c3"], name="c3_196k_thrash_append", append=True, steps=48),
+    "c3sa": replace(WORKLOADS["c3s"], name="c3_small_thrash_append", append=True),
+    "c4sa": replace(WORKLOADS["c4s"], name="c4_small_mixed_append", append=True, steps=6),
 })
 
 

@@ -176,3 +176,10 @@ def page_bias(wl: Workload):
 def context_lengths(wl: Workload) -> np.ndarray:
     """Decode context length per request (int32 [B])."""
     return np.array(wl.contexts, dtype=np.int32)
+
+
+def append_lengths(wl: Workload, s: int):
+    """Appending workloads: per request, the context length once step s's token
+    is written and the pages it spans (int32 [B] each)."""
+    ctx = context_lengths(wl) + np.int32(s + 1)
+    return ctx, ((ctx + wl.page_size - 1) // wl.page_size).astype(np.int32)
