@@ -195,6 +195,44 @@ def cpu_baseline(wl, nsteps):
                         f"host has {cores} cores"))
 
 
+def bench_append(torch, key, steps, warmup):
+    """Decode steps that append one token per request (write-ensure + store
+    with write-through + fused decode layer, per layer) on a fresh tier of the
+    appending variant of the workload.  New tokens' K/V are generated before
+    the timed region."""
+    import dataclasses
+
+    from workload import get_workload
+    from workload.gpu_run import GpuWorkload
+    wl = dataclasses.replace(get_workload(key), steps=warmup + steps)
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    kv = g.append_kv()
+    for s in range(warmup):
+        g.decode_step_append(s, kv)
+    torch.cuda.synchronize()
+    c0 = g.tier.read_counters()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(warmup, warmup + steps):
+        g.decode_step_append(s, kv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    c1 = g.tier.read_counters()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"workload": wl.name, "ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 2),
+           "misses_per_step": round((c1["misses"] - c0["misses"]) / steps, 1),
+           "fresh_allocs": c1["fresh_allocs"] - c0["fresh_allocs"],
+           "mirrored_bytes_per_step": round((c1["bytes_mirrored"] - c0["bytes_mirrored"]) / steps),
+           "error_word": c1["error_word"],
+           "note": "per layer: ensure_write_pages + store_kv_mirror (1 token/request) + decode_layer"}
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_host_tail(torch, g, s0, steps):
     """Decode steps with the host tail read in place (tkv_select_pages +
     tkv_sparse_paged_attn_host_tail per layer; no ensure, no fetch), on the
@@ -447,6 +485,13 @@ def main():
     result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
                                           min(args.steps, 50))
     log(f"[bench] host tail {result['host_tail']}")
+    if args.config == "c3":
+        del g
+        torch.cuda.empty_cache()
+        result["decode_append"] = bench_append(torch, "c3a", min(args.steps, 40), 4)
+        log(f"[bench] decode append {result['decode_append']}")
+    else:
+        result["decode_append"] = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_steps)

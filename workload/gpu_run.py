@@ -95,6 +95,44 @@ class GpuWorkload:
                                    self.miss[layer], self.miss_count[layer], self.out[layer],
                                    page_bias=self.bias, stream=stream)
 
+    # ------------------------------------------------------------- append --
+    def append_kv(self, steps=None):
+        """Keys and values of the appended tokens, generated on the GPU:
+        bf16 [2][steps][L][B][Hkv][d] (token of step s at position ctx + s)."""
+        wl = self.wl
+        steps = wl.steps if steps is None else steps
+        kv = torch.empty((2, steps, wl.num_layers, wl.batch, wl.num_kv_heads, wl.head_dim),
+                         dtype=torch.bfloat16, device="cuda")
+        for s in range(steps):
+            for layer in range(wl.num_layers):
+                for b in range(wl.batch):
+                    for i, kind in enumerate((gen.KIND_K, gen.KIND_V)):
+                        gpu_gen.tokens(wl, kind, layer, b, wl.contexts[b] + s, 1, out=kv[i, s, layer, b:b + 1])
+        return kv
+
+    def decode_step_append(self, s, kv, q=None, stream=None):
+        """One decode step that appends one token per request: per layer, a
+        batched write-ensure of the new tokens' pages, their store (write-
+        through), then the fused decode layer over the grown context.  The
+        old length counts the new token once layer 0 has written it."""
+        wl, t = self.wl, self.tier
+        q = self.q if q is None else q
+        if not hasattr(self, "_run_req"):
+            B = wl.batch
+            self._run_req = torch.arange(B, dtype=torch.int32, device="cuda")
+            self._run_one = torch.ones(B, dtype=torch.int32, device="cuda")
+        start = self.ctx_len + s
+        ctx_s = start + 1
+        npg_s = torch.div(ctx_s + (wl.page_size - 1), wl.page_size, rounding_mode="floor").to(torch.int32)
+        for layer in range(wl.num_layers):
+            t.ensure_write_pages(self._run_req, start, self._run_one, 1, self.bt, start if layer == 0 else ctx_s,
+                                 stream=stream)
+            t.store_kv_mirror(layer, kv[0, s, layer], kv[1, s, layer], self._run_req, start, self._run_one,
+                              self._run_req, 1, self.bt, stream=stream)
+            t.decode_layer(layer, q[s, layer], self.bt, npg_s, ctx_s, wl.topk, self.sel[layer],
+                           self.needed[layer], self.out_slots[layer], self.miss[layer], self.miss_count[layer],
+                           self.out[layer], page_bias=self.bias, stream=stream)
+
     def decode_step_host_tail(self, s, q=None, stream=None):
         """One decode step with the host tail read in place: per layer,
         select_pages then the attention that reads non-resident pages from
