@@ -228,6 +228,23 @@ class OracleTier:
                if with_attention else None)
         return dict(sel=sel, needed=needed, out_slots=out_slots, misses=misses, out=out)
 
+    def decode_layer_prefetch(self, layer, q, row_start, block_table, n_pages, ctx_len, topk, pred,
+                              bias=None, row_pos=None, with_attention=True):
+        """The decode layer preceded by a preload of a predicted page list
+        (vLLM RFC #33980, "Topk KV preload": an earlier top-k index -- from
+        the previous step or layer -- is loaded ahead, and only the pages it
+        missed are loaded after the real selection).  Reading taken: the
+        preload is an ensure of ``pred`` (logical ids, -1 ignored) with the
+        fetch of its misses, ordered before this layer's selection; its copy
+        may overlap the selection in time, which changes no result."""
+        pred = np.asarray(pred, dtype=np.int64).reshape(-1)
+        pre_slots, pre_misses = self.ensure(pred)
+        self.fetch(pre_misses)
+        rec = self.decode_layer(layer, q, row_start, block_table, n_pages, ctx_len, topk, bias=bias,
+                                row_pos=row_pos, with_attention=with_attention)
+        rec["pre_misses"] = pre_misses
+        return rec
+
     def decode_layer_host_tail(self, layer, q, row_start, block_table, n_pages, ctx_len, topk,
                                bias=None, row_pos=None):
         """The decode layer with the host tail read in place: selection and

@@ -251,3 +251,40 @@ def test_append_under_thrash_keeps_pool_rows_clean():
     kc, ks = quantize_tokens(gen.kv_tokens(wl, gen.KIND_K, wl.num_layers - 1, 0, last, 1))
     ref = e4m3_decode(kc).astype(np.float64) * ks[:, None, None]
     assert np.array_equal(k[:, last % wl.page_size], ref[0])
+
+
+def test_prefetch_with_perfect_prediction_moves_every_miss_to_the_preload():
+    """Preload of the exact list the layer is about to need: the preload
+    fetches precisely the plain path's misses (same slots, same order), the
+    layer itself then misses nothing, slot maps and attention are those of
+    the plain path; with an empty prediction the layer is the plain one."""
+    wl = get_workload("c3s")
+    a = run.make_tier(wl, materialize=True)
+    b = run.make_tier(wl, materialize=True)
+    run.setup(wl, a)
+    run.setup(wl, b)
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.array([0, 1])
+    for t in (a, b):
+        t.set_select_width(1, wl.topk, wl.max_sel_pages)
+    ca, cb = a.lru.counters["ensure_calls"], b.lru.counters["ensure_calls"]
+    moved = 0
+    for s in range(3):
+        for layer in range(wl.num_layers):
+            ra = a.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+            pred = ra["needed"] if s > 0 else np.full_like(ra["needed"], -1)
+            rb = b.decode_layer_prefetch(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, pred, bias=bias)
+            if s > 0:
+                assert np.array_equal(rb["pre_misses"], ra["misses"])
+                assert len(rb["misses"]) == 0
+                moved += len(ra["misses"])
+            else:
+                assert len(rb["pre_misses"]) == 0 and np.array_equal(rb["misses"], ra["misses"])
+            assert np.array_equal(ra["sel"], rb["sel"]) and np.array_equal(ra["out_slots"], rb["out_slots"])
+            assert np.array_equal(ra["out"], rb["out"])
+            assert np.array_equal(a.lru.page_to_slot, b.lru.page_to_slot)
+    assert moved > 0
+    assert b.lru.counters["ensure_calls"] - cb == 2 * (a.lru.counters["ensure_calls"] - ca)
