@@ -233,6 +233,48 @@ def bench_append(torch, key, steps, warmup):
     return out
 
 
+def bench_prefetch(torch, g, s0, steps):
+    """Decode steps with the top-k preload: layer l preloads the page list
+    layer l+1 needed last time, its copy on a second stream under layer l's
+    selection (tkv_decode_layer_prefetch).  Continues from the tier state the
+    fetch path left."""
+    wl, t = g.wl, g.tier
+    n_q = g.q.shape[0]
+    side = torch.cuda.Stream()
+    for i in range(2):
+        g.decode_step_prefetch((s0 + i) % n_q, side)
+    torch.cuda.synchronize()
+    c0 = t.read_counters()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        g.decode_step_prefetch((s0 + 2 + i) % n_q, side)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    c1 = t.read_counters()
+    ms = e0.elapsed_time(e1) / steps
+    # how good the prediction is: share of a layer's needed pages that were in
+    # its needed list of the step before (untimed extra steps)
+    import numpy as np
+    prev = g.needed.cpu().numpy()
+    shares = []
+    for i in range(4):
+        g.decode_step_prefetch((s0 + 2 + steps + i) % n_q, side)
+        cur = g.needed.cpu().numpy()
+        for layer in range(wl.num_layers):
+            a = set(cur[layer].ravel().tolist()) - {-1}
+            b = set(prev[layer].ravel().tolist()) - {-1}
+            if a:
+                shares.append(len(a & b) / len(a))
+        prev = cur
+    return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 2),
+            "misses_per_step": round((c1["misses"] - c0["misses"]) / steps, 1),
+            "link_bytes_per_step": round((c1["bytes_fetched"] - c0["bytes_fetched"]) / steps),
+            "prediction_hit_share": round(float(np.mean(shares)), 3),
+            "note": "misses include the preloads'; prediction = the next layer's last needed list"}
+
+
 def bench_host_tail(torch, g, s0, steps):
     """Decode steps with the host tail read in place (tkv_select_pages +
     tkv_sparse_paged_attn_host_tail per layer; no ensure, no fetch), on the
@@ -482,6 +524,9 @@ def main():
         "launch": "hip graph per step" if args.graph else "eager, one C call per layer",
         "error_word": err,
     }
+    result["prefetch"] = bench_prefetch(torch, g, args.warmup + args.steps + args.measure_steps,
+                                        min(args.steps, 50))
+    log(f"[bench] prefetch {result['prefetch']}")
     result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
                                           min(args.steps, 50))
     log(f"[bench] host tail {result['host_tail']}")

@@ -224,6 +224,27 @@ int tkv_decode_layer(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
                      int32_t* sel_local, int32_t* needed, int32_t* out_slots, int32_t* miss,
                      int32_t* miss_count, uint16_t* out, void* stream);
 
+/* tkv_decode_layer preceded by a preload of a predicted page list (vLLM RFC
+ * #33980, "Topk KV preload": an earlier top-k index, e.g. the next layer's
+ * needed list from the previous step, is loaded ahead; after the real
+ * selection only the pages it missed are loaded).  pred: int32 [pred_width]
+ * logical page ids, -1 ignored, pred_width <= min(max_width, num_slots);
+ * device memory, read on `stream` before anything else of this call.  The
+ * preload is an LRU ensure of pred on `stream`; the copy of its misses runs
+ * on `copy_stream` (a different stream; NULL or `stream` itself = serial),
+ * overlapped with this layer's selection and ensure; this layer's fetch and
+ * attention wait for that copy, since this layer's ensure may rebind a slot
+ * the copy still writes.  Results (sel, needed, slots, misses, attention,
+ * LRU state) are those of an ensure+fetch of pred followed by
+ * tkv_decode_layer.  Uses one preload workspace per ctx: calls on one ctx
+ * must not overlap. */
+int tkv_decode_layer_prefetch(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                              const int32_t* ctx_len, const float* page_bias, int32_t topk, int32_t* sel_local,
+                              int32_t* needed, int32_t* out_slots, int32_t* miss, int32_t* miss_count,
+                              uint16_t* out, const int32_t* pred, int32_t pred_width, void* stream,
+                              void* copy_stream);
+
 /* ensure_write_pages (PR #499 "Design": one fixed-shape launch of stride
  * samples plus one boundary sample per request run): run r writes tokens
  * run_start[r] .. run_start[r]+run_len[r]-1 of request run_req[r].  Every

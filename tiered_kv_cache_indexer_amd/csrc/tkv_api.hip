@@ -19,6 +19,7 @@ struct tkv_ctx {
   bool attached = false;
   DevCtx dev{};
   int C = 0;            // compaction width (set_select_width)
+  hipEvent_t ev_pre = nullptr, ev_copy = nullptr;   // preload ordering (created on first use)
 };
 
 static thread_local std::string g_err;
@@ -53,7 +54,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_total;
 };
 
 static int validate(const tkv_config* c) {
@@ -128,6 +129,9 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_attn_done = o; o = align256(o + (size_t)c->max_batch * H * 4);
   L.ws_iota = o; o = align256(o + (R + 1) * 4);
   L.ws_sel_bm = o; o = align256(o + sel_bm_words(R, c->max_batch, P) * 4);
+  L.ws_pout = o; o = align256(o + W * 4);
+  L.ws_pmiss = o; o = align256(o + W * 8);
+  L.ws_pmiss_count = o; o = align256(o + 4);
   L.ws_total = o;
   return L;
 }
@@ -185,6 +189,8 @@ int tkv_create(const tkv_config* cfg, tkv_ctx** out) {
 
 void tkv_destroy(tkv_ctx* c) {
   if (!c) return;
+  if (c->ev_pre) hipEventDestroy(c->ev_pre);
+  if (c->ev_copy) hipEventDestroy(c->ev_copy);
   if (c->mirror_host) hipHostFree(c->mirror_host);
   delete c;
 }
@@ -236,6 +242,9 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.attn_done = (int32_t*)(ws + L.ws_attn_done);
   d.iota = (int32_t*)(ws + L.ws_iota);
   d.sel_bm = (uint32_t*)(ws + L.ws_sel_bm);
+  d.pout = (int32_t*)(ws + L.ws_pout);
+  d.pmiss = (int32_t*)(ws + L.ws_pmiss);
+  d.pmiss_count = (int32_t*)(ws + L.ws_pmiss_count);
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
   d.max_batch = f.max_batch; d.max_width = f.max_width;
   hipStream_t s = (hipStream_t)stream;
@@ -375,10 +384,12 @@ int tkv_sparse_paged_attn_host_tail(tkv_ctx* c, int32_t layer, const uint16_t* q
                    out, stream, 1);
 }
 
-int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, const int32_t* block_table,
-                     int32_t max_pages, const int32_t* n_pages, const int32_t* ctx_len,
-                     const float* page_bias, int32_t topk, int32_t* sel_local, int32_t* needed,
-                     int32_t* out_slots, int32_t* miss, int32_t* miss_count, uint16_t* out, void* stream) {
+static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B,
+                             const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                             const int32_t* ctx_len, const float* page_bias, int32_t topk, int32_t* sel_local,
+                             int32_t* needed, int32_t* out_slots, int32_t* miss, int32_t* miss_count,
+                             uint16_t* out, const int32_t* pred, int32_t pred_width, void* stream,
+                             void* copy_stream) {
   int rc = need_attached(c);
   if (rc) return rc;
   if ((rc = check_rows(c, layer, B, B, max_pages, topk))) return rc;
@@ -388,6 +399,27 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
   if ((int64_t)B * c->C > c->cfg.max_width || (int64_t)B * c->C > c->cfg.num_slots)
     return fail(TKV_E_CAPACITY, "B*max_sel_pages=%lld exceeds num_slots or max_width", (long long)B * c->C);
   hipStream_t s = (hipStream_t)stream;
+  hipStream_t cs = (hipStream_t)copy_stream;
+  const bool overlap = pred && cs && cs != s;
+  if (pred) {
+    if (pred_width < 1 || pred_width > c->cfg.max_width || pred_width > c->cfg.num_slots)
+      return fail(TKV_E_INVALID_ARG, "pred_width=%d out of [1, min(max_width=%d, num_slots=%d)]", pred_width,
+                  c->cfg.max_width, c->cfg.num_slots);
+    if (overlap && !c->ev_pre) {
+      HIPCHECK(hipEventCreateWithFlags(&c->ev_pre, hipEventDisableTiming), "hipEventCreate");
+      HIPCHECK(hipEventCreateWithFlags(&c->ev_copy, hipEventDisableTiming), "hipEventCreate");
+    }
+    HIPCHECK(launch_ensure(c->dev, pred, pred_width, nullptr, c->dev.pout, c->dev.pmiss, c->dev.pmiss_count, s),
+             "preload ensure launch");
+    if (overlap) {
+      HIPCHECK(hipEventRecord(c->ev_pre, s), "hipEventRecord");
+      HIPCHECK(hipStreamWaitEvent(cs, c->ev_pre, 0), "hipStreamWaitEvent");
+      HIPCHECK(launch_fetch(c->dev, c->dev.pmiss, c->dev.pmiss_count, pred_width, cs), "preload fetch launch");
+      HIPCHECK(hipEventRecord(c->ev_copy, cs), "hipEventRecord");
+    } else {
+      HIPCHECK(launch_fetch(c->dev, c->dev.pmiss, c->dev.pmiss_count, pred_width, s), "preload fetch launch");
+    }
+  }
   SelArgs a = make_sel(c, layer, q, B, c->dev.iota, nullptr, block_table, max_pages, n_pages, B,
                        page_bias, topk, sel_local, needed);
   a.do_ensure = 1;
@@ -396,6 +428,9 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
   a.miss_count = miss_count;
   a.sel_slots = c->dev.sel_slots;
   HIPCHECK(launch_select_scan(c->dev, a, s), "decode select+ensure launch");
+  // the layer's ensure may have rebound a slot the preload copy still writes:
+  // its own fetch (and the attention) wait for that copy
+  if (overlap) HIPCHECK(hipStreamWaitEvent(s, c->ev_copy, 0), "hipStreamWaitEvent");
   HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
   AttnArgs t{};
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
@@ -404,6 +439,25 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
   t.slots = c->dev.sel_slots;
   HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");
   return TKV_OK;
+}
+
+int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* n_pages, const int32_t* ctx_len,
+                     const float* page_bias, int32_t topk, int32_t* sel_local, int32_t* needed,
+                     int32_t* out_slots, int32_t* miss, int32_t* miss_count, uint16_t* out, void* stream) {
+  return decode_layer_impl(c, layer, q, B, block_table, max_pages, n_pages, ctx_len, page_bias, topk, sel_local,
+                           needed, out_slots, miss, miss_count, out, nullptr, 0, stream, nullptr);
+}
+
+int tkv_decode_layer_prefetch(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B,
+                              const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                              const int32_t* ctx_len, const float* page_bias, int32_t topk, int32_t* sel_local,
+                              int32_t* needed, int32_t* out_slots, int32_t* miss, int32_t* miss_count,
+                              uint16_t* out, const int32_t* pred, int32_t pred_width, void* stream,
+                              void* copy_stream) {
+  if (!pred) return fail(TKV_E_INVALID_ARG, "pred is NULL");
+  return decode_layer_impl(c, layer, q, B, block_table, max_pages, n_pages, ctx_len, page_bias, topk, sel_local,
+                           needed, out_slots, miss, miss_count, out, pred, pred_width, stream, copy_stream);
 }
 
 int tkv_ensure_write_pages(tkv_ctx* c, int32_t n_runs, const int32_t* run_req, const int32_t* run_start,

@@ -61,6 +61,9 @@ struct DevCtx {
   int32_t* iota;            // [max_rows + 1] = 0, 1, 2, ... (row_start of one-row-per-request calls)
   uint32_t* sel_bm;         // page bitmaps of requests with several rows, one per group of 64 of
                             // the request's rows: [max_rows/64 + max_batch][max_pages/32], kept at zero
+  int32_t* pout;            // [max_width] preload ensure: slots
+  int32_t* pmiss;           // [max_width][2] preload ensure: misses
+  int32_t* pmiss_count;     // [1]
   int max_rows, max_pages, max_topk, max_batch, max_width;
   int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
 };

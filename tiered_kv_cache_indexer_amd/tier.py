@@ -143,6 +143,18 @@ class TieredKV:
             _ptr(miss, torch.int32, "miss"), _ptr(miss_count, torch.int32, "miss_count"),
             _ptr(out, torch.bfloat16, "out"), _stream(stream)))
 
+    def decode_layer_prefetch(self, layer, q, block_table, n_pages, ctx_len, topk, sel_local, needed, out_slots,
+                              miss, miss_count, out, pred, page_bias=None, stream=None, copy_stream=None):
+        check(self.lib.tkv_decode_layer_prefetch(
+            self.ctx, layer, _ptr(q, torch.bfloat16, "q"), q.shape[0],
+            _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+            _ptr(n_pages, torch.int32, "n_pages"), _ptr(ctx_len, torch.int32, "ctx_len"),
+            _ptr(page_bias, torch.float32, "page_bias"), topk, _ptr(sel_local, torch.int32, "sel_local"),
+            _ptr(needed, torch.int32, "needed"), _ptr(out_slots, torch.int32, "out_slots"),
+            _ptr(miss, torch.int32, "miss"), _ptr(miss_count, torch.int32, "miss_count"),
+            _ptr(out, torch.bfloat16, "out"), _ptr(pred, torch.int32, "pred"), pred.numel(), _stream(stream),
+            _stream(copy_stream) if copy_stream is not None else None))
+
     def ensure_write_pages(self, run_req, run_start, run_len, max_run_len, block_table, old_len,
                            stream=None):
         check(self.lib.tkv_ensure_write_pages(

@@ -95,6 +95,20 @@ class GpuWorkload:
                                    self.miss[layer], self.miss_count[layer], self.out[layer],
                                    page_bias=self.bias, stream=stream)
 
+    def decode_step_prefetch(self, s, copy_stream, q=None, stream=None):
+        """One decode step where layer l first preloads the page list layer
+        l+1 needed last time (the next step's layer 0 for the last layer),
+        its copy on `copy_stream` overlapping layer l's selection."""
+        wl = self.wl
+        q = self.q if q is None else q
+        L = wl.num_layers
+        for layer in range(L):
+            self.tier.decode_layer_prefetch(layer, q[s, layer], self.bt, self.n_pages, self.ctx_len, wl.topk,
+                                            self.sel[layer], self.needed[layer], self.out_slots[layer],
+                                            self.miss[layer], self.miss_count[layer], self.out[layer],
+                                            self.needed[(layer + 1) % L].view(-1), page_bias=self.bias,
+                                            stream=stream, copy_stream=copy_stream)
+
     # ------------------------------------------------------------- append --
     def append_kv(self, steps=None):
         """Keys and values of the appended tokens, generated on the GPU:
