@@ -87,6 +87,42 @@ class OracleTier:
             return held[1]
         return self.row_builder(page)
 
+    # ----------------------------------------------------- prefix tier ---
+    def prefix_save(self, pages):
+        """Copy-out of a cold prefix (FreeToken PR #525, "What the patch does",
+        items 2 and 4): the pages' mirror rows and their indexer slab entries
+        (bf16 values and the key sums of partly written pages), host side,
+        since the mirror holds every written byte.  Returns a record list."""
+        assert self.materialize, "prefix records need materialised rows"
+        recs = []
+        for p in pages:
+            p = int(p)
+            recs.append(dict(row=self.mirror_row(p).copy(), slab=self.slab[:, p].copy(),
+                             sums={l: self._partial_sums[(l, p)].copy() for l in range(self.L)
+                                   if (l, p) in self._partial_sums},
+                             written=int(self.written[p])))
+        return recs
+
+    def prefix_restore(self, pages, recs):
+        """Rehydration (PR #525, item 3: with the offloader active the copy is
+        host to host into its mirror and its lazy fetch covers residency):
+        the records land in the mirror rows and slab entries of ``pages``
+        (new logical ids), and any of these ids that is resident is unbound
+        -- its slot holds the id's previous content -- keeping the slot's
+        recency.  Nothing is fetched."""
+        assert self.materialize and len(pages) == len(recs)
+        assert len(set(int(p) for p in pages)) == len(pages)
+        for p, r in zip(pages, recs):
+            p = int(p)
+            self.mirror[p] = r["row"].copy()
+            self.slab[:, p] = r["slab"]
+            for l in range(self.L):
+                self._partial_sums.pop((l, p), None)
+            for l, v in r["sums"].items():
+                self._partial_sums[(l, p)] = v.copy()
+            self.written[p] = r["written"]
+            self.lru.unbind(p)
+
     # ------------------------------------------------------------ write ---
     def ensure_write_pages(self, runs, block_table, old_len):
         """runs: list of (req, start, length).  Every page a run touches is made

@@ -43,6 +43,15 @@ class LRUState:
         self.counters = dict(ensure_calls=0, hits=0, misses=0, fresh_allocs=0, evictions=0)
         self.error_word = 0
 
+    def unbind(self, page):
+        """Forget a resident page: its slot becomes empty and keeps its stamp
+        (its place in the recency order); later taking it as a victim evicts
+        nothing."""
+        s = int(self.page_to_slot[page])
+        if s >= 0:
+            self.page_to_slot[page] = -1
+            self.slot_to_page[s] = -1
+
     def ensure(self, needed, no_fetch=None):
         """Returns (out_slots int32 [W], miss list int32 [m][2] as (slot, page))."""
         needed = np.asarray(needed, dtype=np.int64).reshape(-1)

@@ -288,3 +288,39 @@ def test_prefetch_with_perfect_prediction_moves_every_miss_to_the_preload():
             assert np.array_equal(a.lru.page_to_slot, b.lru.page_to_slot)
     assert moved > 0
     assert b.lru.counters["ensure_calls"] - cb == 2 * (a.lru.counters["ensure_calls"] - ca)
+
+
+def test_prefix_save_restore_under_new_ids_decodes_like_the_original():
+    """A request's prefix saved, then rehydrated under another request's
+    logical ids (whose resident slots get unbound): decoding it through a
+    block table pointing at the new ids gives exactly the original's
+    selections and attention, with the moved pages fetched lazily."""
+    wl = replace(get_workload("c4s"), contexts=(4096, 4096, 2048, 8192), steps=3)
+    bt, npg = gen.block_tables(wl)
+    a = run.make_tier(wl, materialize=True)
+    b = run.make_tier(wl, materialize=True)
+    run.setup(wl, a)
+    run.setup(wl, b)
+    ctx = gen.context_lengths(wl)
+    q = gen.decode_queries(wl)
+    rs = np.arange(wl.batch + 1)
+    for t in (a, b):
+        t.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    for layer in range(wl.num_layers):           # step 0 on both: some of request 0's pages get resident
+        for t in (a, b):
+            t.decode_layer(layer, q[0, layer], rs, bt, npg, ctx, wl.topk)
+    src, dst = bt[1, :npg[1]], bt[0, :npg[0]]
+    resident_before = int(np.sum(b.lru.page_to_slot[dst] >= 0))
+    assert resident_before > 0
+    b.prefix_restore(dst, b.prefix_save(src))
+    assert not np.any(b.lru.page_to_slot[dst] >= 0)
+    bt2 = bt.copy()
+    bt2[1, :npg[1]] = dst                      # request 1 now lives on request 0's old ids
+    m0 = b.lru.counters["misses"]
+    for s in range(1, wl.steps):
+        for layer in range(wl.num_layers):
+            ra = a.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk)
+            rb = b.decode_layer(layer, q[s, layer], rs, bt2, npg, ctx, wl.topk)
+            assert np.array_equal(ra["sel"][1], rb["sel"][1])
+            assert np.array_equal(ra["out"][1], rb["out"][1])
+    assert b.lru.counters["misses"] > m0
