@@ -275,6 +275,26 @@ def bench_prefetch(torch, g, s0, steps):
             "note": "misses include the preloads'; prediction = the next layer's last needed list"}
 
 
+def bench_prefix(g, n):
+    """Cold-prefix records of n pages of request 0 (n = 375: a 24k-token
+    prefix) saved and restored in place: rows host to host, slab entries
+    over the link.  Wall time of each call (both synchronise)."""
+    t = g.tier
+    pages = g.bt_np[0, :n]
+    t.prefix_save(pages)                                    # warm the threads and the staging path
+    a = time.perf_counter()
+    recs = t.prefix_save(pages)
+    b = time.perf_counter()
+    t.prefix_restore(pages, recs)
+    c = time.perf_counter()
+    row_bytes = n * t.row_bytes
+    return {"pages": n, "record_bytes": int(recs.nbytes), "save_ms": round((b - a) * 1e3, 2),
+            "restore_ms": round((c - b) * 1e3, 2),
+            "save_rows_GBps": round(row_bytes / (b - a) / 1e9, 2),
+            "restore_rows_GBps": round(row_bytes / (c - b) / 1e9, 2),
+            "note": "rows host to host (8 threads), slab entries via the GPU in 128-page slices"}
+
+
 def bench_host_tail(torch, g, s0, steps):
     """Decode steps with the host tail read in place (tkv_select_pages +
     tkv_sparse_paged_attn_host_tail per layer; no ensure, no fetch), on the
@@ -530,6 +550,8 @@ def main():
     result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
                                           min(args.steps, 50))
     log(f"[bench] host tail {result['host_tail']}")
+    result["prefix_rehydrate"] = bench_prefix(g, 375)
+    log(f"[bench] prefix {result['prefix_rehydrate']}")
     if args.config == "c3":
         del g
         torch.cuda.empty_cache()

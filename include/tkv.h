@@ -269,6 +269,35 @@ int tkv_store_kv_mirror(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const ui
                         const int32_t* run_len, const int32_t* run_tok_off, int32_t max_run_len,
                         const int32_t* block_table, int32_t max_pages, void* stream);
 
+/* Cold-prefix records (FreeToken PR #525, "What the patch does", items
+ * 2-4: a prefix leaving the tier is copied out because logical ids get
+ * reused; on a later hit it comes back host to host into the mirror and the
+ * LRU's fetch on selection covers residency).  A record is one page's
+ * mirror row (row_bytes) followed by its indexer slab entries for every
+ * layer: bf16 values [L][Hkv*d], then fp32 key sums [L][Hkv*d] (what a
+ * partly written page's later tokens add to); tkv_prefix_record_bytes
+ * gives its size. */
+int64_t tkv_prefix_record_bytes(const tkv_ctx* ctx);
+
+/* Copies the records of `n` logical pages (pages: host int32 [n], each in
+ * [0, num_logical_pages)) into `records` (host memory, n records).  Rows
+ * are copied host to host from the pinned mirror (which holds every
+ * written byte); the slab entries come from the GPU in 128-page slices
+ * through a staging buffer this call allocates and frees.  Synchronises
+ * `stream` first (stores queued before it have landed) and before
+ * returning.  The tier's state does not change. */
+int tkv_prefix_save(tkv_ctx* ctx, const int32_t* pages, int32_t n, void* records, void* stream);
+
+/* Rehydration: writes `n` records into the mirror rows and slab entries of
+ * `pages` (host int32 [n], distinct, each in [0, num_logical_pages); they
+ * may differ from the ids the records were saved from), and unbinds any of
+ * these ids that is resident in the pool (its slot holds the id's previous
+ * content; the slot keeps its recency and is reused in LRU order).
+ * Nothing is fetched: a later ensure brings a page in when it is needed.
+ * Synchronises `stream` first (no queued copy still reads these rows) and
+ * before returning; allocates and frees a staging buffer. */
+int tkv_prefix_restore(tkv_ctx* ctx, const int32_t* pages, int32_t n, const void* records, void* stream);
+
 /* Copies the counters to the host.  Synchronises `stream`. */
 int tkv_read_counters(tkv_ctx* ctx, tkv_counters* out, void* stream);
 

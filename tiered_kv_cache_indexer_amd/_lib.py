@@ -78,6 +78,9 @@ SIGNATURES = {
     "tkv_debug_e4m3_encode": (C.c_int, [P, P, I64, P]),
     "tkv_debug_e4m3_decode": (C.c_int, [P, P, I64, P]),
     "tkv_debug_set_attn_kernel": (C.c_int, [P, I32]),
+    "tkv_prefix_record_bytes": (I64, [P]),
+    "tkv_prefix_save": (C.c_int, [P, P, I32, P, P]),
+    "tkv_prefix_restore": (C.c_int, [P, P, I32, P, P]),
     "tkv_mirror_host_ptr": (C.c_void_p, [P]),
     "tkv_destroy": (None, [P]),
     "tkv_last_error": (C.c_char_p, []),

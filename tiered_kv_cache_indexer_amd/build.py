@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtkv.so")
 SOURCES = ["tkv_api.hip", "tkv_select.hip", "tkv_prefill.hip", "tkv_fetch.hip", "tkv_store.hip",
-           "tkv_attn.hip", "tkv_attn_mfma.hip"]
+           "tkv_attn.hip", "tkv_attn_mfma.hip", "tkv_prefix.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

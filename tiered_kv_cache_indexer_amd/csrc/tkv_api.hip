@@ -1,3 +1,5 @@
+#include <algorithm>
+#include <vector>
 // C ABI of the tiered KV-cache library: validation, buffer layout, launches.
 #include <stdarg.h>
 #include <stdio.h>
@@ -532,6 +534,100 @@ int tkv_debug_read_state(tkv_ctx* c, int32_t* page_to_slot, int32_t* slot_to_pag
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
   if (clock) *clock = h.clock;
   return TKV_OK;
+}
+
+int64_t tkv_prefix_record_bytes(const tkv_ctx* c) {
+  if (!c) return 0;
+  const int64_t E = (int64_t)c->cfg.num_kv_heads * c->cfg.head_dim;
+  return (int64_t)c->row_bytes + (int64_t)c->cfg.num_layers * E * 6;
+}
+
+static int check_prefix_pages(tkv_ctx* c, const int32_t* pages, int32_t n, bool distinct) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (!pages || n < 1) return fail(TKV_E_INVALID_ARG, "pages is NULL or n=%d < 1", n);
+  for (int i = 0; i < n; ++i)
+    if (pages[i] < 0 || (int64_t)pages[i] >= c->cfg.num_logical_pages)
+      return fail(TKV_E_INVALID_ARG, "pages[%d]=%d out of [0, num_logical_pages=%lld)", i, pages[i],
+                  (long long)c->cfg.num_logical_pages);
+  if (distinct) {
+    std::vector<int32_t> v(pages, pages + n);
+    std::sort(v.begin(), v.end());
+    if (std::adjacent_find(v.begin(), v.end()) != v.end())
+      return fail(TKV_E_INVALID_ARG, "pages has duplicates");
+  }
+  return TKV_OK;
+}
+
+// Slab entries of `n` pages between records and the device, 128 pages at a time.
+static int prefix_slab(tkv_ctx* c, const int32_t* pages, int32_t n, uint8_t* recs, bool save, hipStream_t s) {
+  const size_t E = (size_t)c->cfg.num_kv_heads * c->cfg.head_dim, L = c->cfg.num_layers;
+  const size_t rec = (size_t)tkv_prefix_record_bytes(c), vbytes = L * E * 2, sbytes = L * E * 4;
+  const int SLICE = 128;
+  const int m = std::min(n, SLICE);
+  void* dev = nullptr;
+  HIPCHECK(hipMalloc(&dev, m * (vbytes + sbytes) + (size_t)m * 4), "hipMalloc (prefix staging)");
+  uint16_t* dv = (uint16_t*)dev;
+  float* ds = (float*)((uint8_t*)dev + m * vbytes);
+  int32_t* dp = (int32_t*)((uint8_t*)dev + m * (vbytes + sbytes));
+  std::vector<uint8_t> host(m * (vbytes + sbytes));
+  hipError_t e = hipSuccess;
+  for (int i0 = 0; i0 < n && e == hipSuccess; i0 += SLICE) {
+    const int k = std::min(SLICE, n - i0);
+    e = hipMemcpyAsync(dp, pages + i0, (size_t)k * 4, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) break;
+    if (save) {
+      if ((e = launch_slab_gather(c->dev, dp, k, dv, ds, s)) != hipSuccess) break;
+      if ((e = hipMemcpyAsync(host.data(), dv, k * vbytes, hipMemcpyDeviceToHost, s)) != hipSuccess) break;
+      if ((e = hipMemcpyAsync(host.data() + m * vbytes, ds, k * sbytes, hipMemcpyDeviceToHost, s)) != hipSuccess)
+        break;
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
+      for (int i = 0; i < k; ++i) {
+        uint8_t* r = recs + (size_t)(i0 + i) * rec + c->row_bytes;
+        memcpy(r, host.data() + (size_t)i * vbytes, vbytes);
+        memcpy(r + vbytes, host.data() + m * vbytes + (size_t)i * sbytes, sbytes);
+      }
+    } else {
+      for (int i = 0; i < k; ++i) {
+        const uint8_t* r = recs + (size_t)(i0 + i) * rec + c->row_bytes;
+        memcpy(host.data() + (size_t)i * vbytes, r, vbytes);
+        memcpy(host.data() + m * vbytes + (size_t)i * sbytes, r + vbytes, sbytes);
+      }
+      if ((e = hipMemcpyAsync(dv, host.data(), k * vbytes, hipMemcpyHostToDevice, s)) != hipSuccess) break;
+      if ((e = hipMemcpyAsync(ds, host.data() + m * vbytes, k * sbytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+        break;
+      if ((e = launch_slab_scatter(c->dev, dp, k, dv, ds, s)) != hipSuccess) break;
+      if ((e = launch_unbind(c->dev, dp, k, s)) != hipSuccess) break;
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) break;
+    }
+  }
+  hipError_t e2 = hipStreamSynchronize(s);
+  hipFree(dev);
+  if (e == hipSuccess) e = e2;
+  HIPCHECK(e, save ? "prefix save (slab)" : "prefix restore (slab, unbind)");
+  return TKV_OK;
+}
+
+int tkv_prefix_save(tkv_ctx* c, const int32_t* pages, int32_t n, void* records, void* stream) {
+  int rc = check_prefix_pages(c, pages, n, false);
+  if (rc) return rc;
+  if (!records) return fail(TKV_E_INVALID_ARG, "records is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // stores to the mirror have landed
+  const size_t rec = (size_t)tkv_prefix_record_bytes(c);
+  prefix_copy_rows((uint8_t*)records, rec, c->mirror_host, c->row_bytes, c->row_bytes, pages, n, false);
+  return prefix_slab(c, pages, n, (uint8_t*)records, true, s);
+}
+
+int tkv_prefix_restore(tkv_ctx* c, const int32_t* pages, int32_t n, const void* records, void* stream) {
+  int rc = check_prefix_pages(c, pages, n, true);
+  if (rc) return rc;
+  if (!records) return fail(TKV_E_INVALID_ARG, "records is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // no copy still reads these rows
+  const size_t rec = (size_t)tkv_prefix_record_bytes(c);
+  prefix_copy_rows(c->mirror_host, c->row_bytes, (const uint8_t*)records, rec, c->row_bytes, pages, n, true);
+  return prefix_slab(c, pages, n, const_cast<uint8_t*>((const uint8_t*)records), false, s);
 }
 
 int tkv_debug_set_attn_kernel(tkv_ctx* c, int32_t kernel) {

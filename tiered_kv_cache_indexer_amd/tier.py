@@ -212,6 +212,25 @@ class TieredKV:
                                              _stream(None)))
         return out
 
+    # ------------------------------------------------------ prefix tier ---
+    def prefix_record_bytes(self) -> int:
+        return int(self.lib.tkv_prefix_record_bytes(self.ctx))
+
+    def prefix_save(self, pages, stream=None) -> np.ndarray:
+        """Records of the given logical pages: uint8 [n][prefix_record_bytes]."""
+        pages = np.ascontiguousarray(pages, dtype=np.int32)
+        out = np.empty((len(pages), self.prefix_record_bytes()), dtype=np.uint8)
+        check(self.lib.tkv_prefix_save(self.ctx, pages.ctypes.data, len(pages), out.ctypes.data, _stream(stream)))
+        return out
+
+    def prefix_restore(self, pages, records: np.ndarray, stream=None) -> None:
+        pages = np.ascontiguousarray(pages, dtype=np.int32)
+        records = np.ascontiguousarray(records, dtype=np.uint8)
+        if records.shape != (len(pages), self.prefix_record_bytes()):
+            raise ValueError(f"records shape {records.shape} != ({len(pages)}, {self.prefix_record_bytes()})")
+        check(self.lib.tkv_prefix_restore(self.ctx, pages.ctypes.data, len(pages), records.ctypes.data,
+                                          _stream(stream)))
+
     ATTN_AUTO, ATTN_VECTOR, ATTN_MATRIX = 0, 1, 2
 
     def set_attn_kernel(self, kernel: int) -> None:
