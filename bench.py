@@ -46,6 +46,29 @@ def fetch_traffic():
     return round(rec["fetch_KiB"] * 1024), round(rec["write_KiB"] * 1024)
 
 
+def pmc_traffic(summary, kernel, source):
+    """Bytes per launch of `kernel` past L2 (FETCH_SIZE and WRITE_SIZE scaled
+    by the calibration copy) from a committed PMC summary, or None when the
+    kernel's source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    src = os.path.join(ROOT, "tiered_kv_cache_indexer_amd", "csrc", source)
+    try:
+        doc = json.load(open(path))
+        rec = doc[kernel]
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except Exception:
+        return None
+    if rec.get("source_sha256_16") != sha:
+        return None
+    return round((rec["fetch_KiB"] * doc.get("fetch_scale", 2.0) + rec["write_KiB"] * doc.get("write_scale", 1.0))
+                 * 1024)
+
+
+def prefill_attn_traffic():
+    return pmc_traffic("c5_pmc_traffic.json", "k_attn_mfma_rows", "tkv_attn_mfma.hip")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -60,6 +83,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--graph", action="store_true", help="replay each decode step as a captured HIP graph")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the preload, host-tail, prefix and append figures (profiling runs)")
     return ap.parse_args()
 
 
@@ -415,6 +440,10 @@ def bench_prefill(args, torch):
                 toks += max(0, min(wl.page_size, min(ctxl, int(pos[r]) + 1) - int(i) * wl.page_size))
     toks = int(toks)
     attn_flop_layer = toks * wl.num_q_heads * wl.head_dim * 4
+    pages_read = int(sum(1 for r in range(n) for i in sel[r]
+                         if i >= 0 and int(i) * wl.page_size <= min(ctxl - 1, int(pos[r]))))
+    attn_bytes_layer = pages_read * wl.num_kv_heads * (2 * wl.page_size * wl.head_dim + 8 * wl.page_size)
+    attn_traffic = prefill_attn_traffic()
     gemm_flop_layer = 2 * n * wl.pages_of(0) * wl.num_kv_heads * wl.head_dim
     tok_bytes = t.layer_bytes // wl.page_size
     c = t.read_counters()
@@ -429,11 +458,17 @@ def bench_prefill(args, torch):
         "config": {"workload": wl.name, "layers": L, "chunk_tokens": n, "cached_tokens": start,
                    "topk_pages": wl.topk, "pool_slots": wl.num_slots},
         "split_ms": {k: round(v, 3) for k, v in ms.items()},
-        "roofline": {"kernel": "k_attn (causal sparse attention, prefill rows)", "bound": "alu",
-                     "achieved": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12, 2),
-                     "peak": 78.6, "unit": "TFLOP/s",
-                     "frac": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12 / 78.6, 4),
-                     "traffic": None, "note": "peak = non-packed fp32 VALU (256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz)"},
+        "roofline": {"kernel": "k_attn_mfma_rows (causal sparse attention, one wave per row and KV head)",
+                     "bound": "hbm",
+                     "achieved": round(attn_bytes_layer * L / (ms["attn"] * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(attn_bytes_layer * L / (ms["attn"] * 1e-3) / 1e9 / 8000.0, 4),
+                     "traffic": attn_traffic,
+                     "bytes_per_launch": attn_bytes_layer,
+                     "flop_per_launch": attn_flop_layer,
+                     "TFLOPs": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12, 2),
+                     "note": "bytes = K+V codes and scales of every (row, KV head, selected page) read; "
+                             "most are served by the Infinity Cache, so HBM 8 TB/s is the reference peak"},
         "roofline_mfma": {"kernel": "k_prefill_scores (+ per-row top-k, compaction)", "bound": "mfma",
                           "achieved": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12, 2),
                           "peak": 2500.0, "unit": "TFLOP/s",
@@ -530,9 +565,11 @@ def main():
                      "traffic_hbm_write": t_write,
                      "bytes_per_launch": round(k["fetch_bytes_per_launch"]),
                      "avg_launch_us": round(k["fetch_us"], 2), "step_time_share": round(fetch_share, 3)},
-        "roofline_hbm": {"kernel": "k_attn (sparse paged attention)", "bound": "hbm",
+        "roofline_hbm": {"kernel": "k_attn_mfma_split (sparse paged attention, split pages + merge)",
+                         "bound": "hbm",
                          "achieved": round(k["attn_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(k["attn_GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(k["attn_GBps"] / HBM_PEAK_GBPS, 4),
+                         "traffic": pmc_traffic("c3_pmc_traffic.json", "k_attn_mfma_split", "tkv_attn_mfma.hip"),
                          "bytes_per_launch": k["attn_bytes_per_launch"],
                          "avg_launch_us": round(k["attn_us"], 2)},
         "select_ensure": {"avg_us": round(k["select_ensure_us"], 2),
@@ -544,21 +581,24 @@ def main():
         "launch": "hip graph per step" if args.graph else "eager, one C call per layer",
         "error_word": err,
     }
-    result["prefetch"] = bench_prefetch(torch, g, args.warmup + args.steps + args.measure_steps,
-                                        min(args.steps, 50))
-    log(f"[bench] prefetch {result['prefetch']}")
-    result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
-                                          min(args.steps, 50))
-    log(f"[bench] host tail {result['host_tail']}")
-    result["prefix_rehydrate"] = bench_prefix(g, 375)
-    log(f"[bench] prefix {result['prefix_rehydrate']}")
-    if args.config == "c3":
-        del g
-        torch.cuda.empty_cache()
-        result["decode_append"] = bench_append(torch, "c3a", min(args.steps, 40), 4)
-        log(f"[bench] decode append {result['decode_append']}")
+    if args.no_extras:
+        result.update(prefetch=None, host_tail=None, prefix_rehydrate=None, decode_append=None)
     else:
-        result["decode_append"] = None
+        result["prefetch"] = bench_prefetch(torch, g, args.warmup + args.steps + args.measure_steps,
+                                            min(args.steps, 50))
+        log(f"[bench] prefetch {result['prefetch']}")
+        result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
+                                              min(args.steps, 50))
+        log(f"[bench] host tail {result['host_tail']}")
+        result["prefix_rehydrate"] = bench_prefix(g, 375)
+        log(f"[bench] prefix {result['prefix_rehydrate']}")
+        if args.config == "c3":
+            del g
+            torch.cuda.empty_cache()
+            result["decode_append"] = bench_append(torch, "c3a", min(args.steps, 40), 4)
+            log(f"[bench] decode append {result['decode_append']}")
+        else:
+            result["decode_append"] = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(base, args.cpu_steps)
