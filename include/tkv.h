@@ -313,6 +313,13 @@ int tkv_debug_read_state(tkv_ctx* ctx, int32_t* page_to_slot, int32_t* slot_to_p
  * same softmax; tests compare them. */
 enum { TKV_ATTN_AUTO = 0, TKV_ATTN_VECTOR = 1, TKV_ATTN_MATRIX = 2 };
 int tkv_debug_set_attn_kernel(tkv_ctx* ctx, int32_t kernel);
+/* Pages per range of the multi-pass attention over many rows (prefill
+ * chunks on the matrix-core kernel): one launch per range of `pages` local
+ * page ids, the softmax state carried between launches; 0 = a single pass
+ * (the default: the passes cut the bytes past the L2s 3.6x at 192 pages but
+ * the kernel is bound by instruction issue, not by those bytes).  Both give
+ * the same bits; tests compare them. */
+int tkv_debug_set_attn_range(tkv_ctx* ctx, int32_t pages);
 /* fp32 -> e4m3 codes with the store's encoder; device pointers. */
 int tkv_debug_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 /* e4m3 codes -> fp32 with the attention kernel's decoder; device pointers. */

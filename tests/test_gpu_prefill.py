@@ -19,13 +19,14 @@ def _capture(store):
     return on_layer
 
 
-@pytest.mark.parametrize("kernel", [0, 1], ids=["auto", "vector"])
-def test_prefill_small_bit_exact(kernel):
+@pytest.mark.parametrize("kernel,ranges", [(0, 0), (0, 16), (1, 0)], ids=["auto", "auto-16-page-ranges", "vector"])
+def test_prefill_small_bit_exact(kernel, ranges):
     from workload.gpu_run import GpuWorkload
     wl = get_workload("c5s")
-    say(f"[prefill] {wl.name} attention kernel {kernel}")
+    say(f"[prefill] {wl.name} attention kernel {kernel}, range pages {ranges}")
     g = GpuWorkload(wl)
     g.tier.set_attn_kernel(kernel)
+    g.tier.set_attn_range(ranges)
     g.setup()
     got = []
     g.prefill(on_layer=_capture(got))
@@ -109,3 +110,29 @@ def test_multi_row_requests_union_and_drops():
         assert np.array_equal(needed.cpu().numpy(), ref_needed), f"call {rep}: needed"
     drops = t.read_counters()["drops"] - drops0
     assert drops == o.drops > 0
+
+
+@pytest.mark.parametrize("pages", [7, 16, 64])
+def test_range_passes_equal_single_pass(pages):
+    """The multi-pass prefill attention (one launch per range of local page
+    ids, softmax state carried in fp32 records) gives the single pass's bits,
+    including rows whose pages skip ranges and ragged last ranges."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c5s")
+    say(f"[prefill] range passes of {pages} pages vs one pass")
+    g = GpuWorkload(wl)
+    g.setup()
+    bufs = g.prefill()
+    torch.cuda.synchronize()
+    t = g.tier
+    layer = wl.num_layers - 1
+    outs = []
+    for rp in (0, pages):
+        t.set_attn_range(rp)
+        out = torch.full_like(bufs["out"], 7.0)
+        t.sparse_paged_attn(layer, bufs["q"], bufs["row_start"], bufs["ctx_len"], bufs["sel"], g.bt, out,
+                            row_pos=bufs["row_pos"])
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], bufs["out"])

@@ -78,6 +78,7 @@ SIGNATURES = {
     "tkv_debug_e4m3_encode": (C.c_int, [P, P, I64, P]),
     "tkv_debug_e4m3_decode": (C.c_int, [P, P, I64, P]),
     "tkv_debug_set_attn_kernel": (C.c_int, [P, I32]),
+    "tkv_debug_set_attn_range": (C.c_int, [P, I32]),
     "tkv_prefix_record_bytes": (I64, [P]),
     "tkv_prefix_save": (C.c_int, [P, P, I32, P, P]),
     "tkv_prefix_restore": (C.c_int, [P, P, I32, P, P]),

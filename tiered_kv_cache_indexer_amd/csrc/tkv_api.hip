@@ -56,7 +56,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_attn_state, ws_total;
 };
 
 static int validate(const tkv_config* c) {
@@ -134,6 +134,9 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_pout = o; o = align256(o + W * 4);
   L.ws_pmiss = o; o = align256(o + W * 8);
   L.ws_pmiss_count = o; o = align256(o + 4);
+  // records of the page-range prefill attention: only configs with more rows than requests
+  L.ws_attn_state = o;
+  if (c->max_rows > c->max_batch) o = align256(o + R * (size_t)H * ATTN_STATE_FLOATS * 4);
   L.ws_total = o;
   return L;
 }
@@ -247,6 +250,8 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.pout = (int32_t*)(ws + L.ws_pout);
   d.pmiss = (int32_t*)(ws + L.ws_pmiss);
   d.pmiss_count = (int32_t*)(ws + L.ws_pmiss_count);
+  d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;
+  d.attn_range_pages = ATTN_RANGE_PAGES_DEFAULT;
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
   d.max_batch = f.max_batch; d.max_width = f.max_width;
   hipStream_t s = (hipStream_t)stream;
@@ -643,6 +648,13 @@ int tkv_debug_set_attn_kernel(tkv_ctx* c, int32_t kernel) {
                   "8 query heads per KV head");
   }
   c->dev.attn_impl = kernel == TKV_ATTN_VECTOR ? ATTN_VECTOR : kernel == TKV_ATTN_MATRIX ? ATTN_MATRIX : ATTN_AUTO;
+  return TKV_OK;
+}
+
+int tkv_debug_set_attn_range(tkv_ctx* c, int32_t pages) {
+  if (!c) return fail(TKV_E_INVALID_ARG, "ctx is null");
+  if (pages < 0) return fail(TKV_E_INVALID_ARG, "pages=%d < 0", pages);
+  c->dev.attn_range_pages = pages;
   return TKV_OK;
 }
 

@@ -42,6 +42,17 @@ constexpr int MD = ATT_D, MG = ATT_G, MPS = 64, MWAVES = TKV_BLOCK / 64;
 
 __device__ __forceinline__ uint32_t bits2(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Page rows are pool slots or mapped mirror rows, both global memory; the
+// row pointer is rebuilt from lane values, so say so explicitly (otherwise
+// the loads become flat loads).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T gld(const uint8_t* p) {
+  static_assert(sizeof(T) == 16, "16-byte loads");
+  const u32x4v v = *(const __attribute__((address_space(1))) u32x4v*)(p);
+  return __builtin_bit_cast(T, v);
+}
+
 // 16 e4m3 codes (bytes in address order) -> bf16 operands of elements 0..7
 // and 8..15 (exact conversion)
 __device__ __forceinline__ void fp8x16_to_bf16(const uint4 w, bf16x8& lo, bf16x8& hi) {
@@ -79,15 +90,15 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int t = 16 * (m >> 2) + 4 * mt + (m & 3);
-    kr[mt][0] = *reinterpret_cast<const uint4*>(kb + t * MD + 16 * q);
-    kr[mt][1] = *reinterpret_cast<const uint4*>(kb + t * MD + 64 + 16 * q);
+    kr[mt][0] = gld<uint4>(kb + t * MD + 16 * q);
+    kr[mt][1] = gld<uint4>(kb + t * MD + 64 + 16 * q);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ks4[i] = *reinterpret_cast<const float4*>(ksc + 16 * q + 4 * i);
+  for (int i = 0; i < 4; ++i) ks4[i] = gld<float4>(reinterpret_cast<const uint8_t*>(ksc + 16 * q + 4 * i));
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) vr[dt] = *reinterpret_cast<const uint4*>(vb + (16 * dt + m) * MPS + 16 * q);
+  for (int dt = 0; dt < 8; ++dt) vr[dt] = gld<uint4>(vb + (16 * dt + m) * MPS + 16 * q);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vs4[i] = *reinterpret_cast<const float4*>(ksc + MPS + 16 * q + 4 * i);
+  for (int i = 0; i < 4; ++i) vs4[i] = gld<float4>(reinterpret_cast<const uint8_t*>(ksc + MPS + 16 * q + 4 * i));
 
   // S^T tiles
   f32x4 s[4];
@@ -103,23 +114,38 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
     z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, qop[3], z, 0, 0, 0);
     s[mt] = z;
   }
-  // logits in the exp2 domain, masked past the visible tokens
+  // logits in the exp2 domain, masked past the visible tokens (a full page,
+  // the common case, needs no mask)
   float mx = -INFINITY;
+  const bool full = nt >= MPS;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const float kv4[4] = {ks4[mt].x, ks4[mt].y, ks4[mt].z, ks4[mt].w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int tok = 16 * q + 4 * mt + v;
-      const float x = tok < nt ? s[mt][v] * (kv4[v] * qscale) : -INFINITY;
+      float x = s[mt][v] * (kv4[v] * qscale);
+      if (!full) x = (16 * q + 4 * mt + v) < nt ? x : -INFINITY;
       s[mt][v] = x;
       mx = fmaxf(mx, x);
     }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(st.m_run, mx);        // finite: token 0 is visible
-  const float alpha = exp2f(st.m_run - m_new);
+  // Lazy rescale: the running reference max moves only when some head's
+  // page max exceeds it by more than 2^8 (so p <= 256, no overflow); the
+  // output o / l does not depend on the reference.  The first page always
+  // sets it (the accumulator is still zero then).
+  if (__ballot((lane & 15) < MG && mx > st.m_run + 8.0f)) {   // the 8 real head columns decide
+    const float m_new = fmaxf(st.m_run, mx);        // finite: token 0 is visible
+    if (st.m_run != -INFINITY) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+      st.l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
+    }
+    st.m_run = m_new;
+  }
+  const float m_ref = st.m_run;
   float psum = 0.f;
   f32x8 pv[2];
 #pragma unroll
@@ -127,22 +153,21 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
     const float vv4[4] = {vs4[mt].x, vs4[mt].y, vs4[mt].z, vs4[mt].w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float p = exp2f(s[mt][v] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[mt][v] - m_ref);
       psum += p;
       pv[mt >> 1][4 * (mt & 1) + v] = p * vv4[v];
     }
   }
   psum += __shfl_xor(psum, 16, 64);
   psum += __shfl_xor(psum, 32, 64);
-  st.l_run = st.l_run * alpha + psum;
-  st.m_run = m_new;
+  st.l_run += psum;
   const bf16x8 pb0 = __builtin_convertvector(pv[0], bf16x8);
   const bf16x8 pb1 = __builtin_convertvector(pv[1], bf16x8);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     bf16x8 v0, v1;
     fp8x16_to_bf16(vr[dt], v0, v1);
-    f32x4 o = st.acc[dt] * alpha;
+    f32x4 o = st.acc[dt];
     o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb0, o, 0, 0, 0);
     o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb1, o, 0, 0, 0);
     st.acc[dt] = o;
@@ -262,6 +287,122 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs
   }
 }
 
+// Page-range passes for many rows (prefill chunks).  Rows select their pages
+// all over the request's page space, so a single pass keeps every page of
+// every KV head in flight at once and most reads miss the L2s.  Instead the
+// attention runs as one launch per range of RP local page ids: in launch r
+// each (row, KV head) wave folds in only its selected pages in range r, so
+// the pages in flight are one range -- one KV head's blocks of it fit an
+// XCD's L2 -- and the online-softmax state (O^T tiles, m, l) is carried
+// between launches in an fp32 record per (row, KV head).  Pages are still
+// folded in ascending order and the state round-trips exactly, so the result
+// is bit-identical to the single pass.  A unit touches the record only
+// between its first and last non-empty range: the first starts from an empty
+// state, the last writes the bf16 output.
+constexpr int ST_FLOATS = ATTN_STATE_FLOATS;   // O^T tiles of the 32 live lanes, then (m, l) per head
+static_assert(ST_FLOATS == 8 * 32 * 4 + MG * 2, "record layout");
+
+__global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_range(DevCtx c, AttnArgs a, int r, int RP) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int row, g;
+  if (attn_rows_by_xcd(c.Hkv)) {
+    const int per = NXCD / c.Hkv;
+    const int x = blockIdx.x % NXCD, k = blockIdx.x / NXCD;
+    g = x / per;
+    row = (k * per + x % per) * MWAVES + wave;
+  } else {
+    const int u = blockIdx.x * MWAVES + wave;
+    row = u / c.Hkv;
+    g = u - row * c.Hkv;
+  }
+  if (row >= a.rows) return;
+  const int b = attn_row_request(a, row);
+  int limit = a.ctx_len[b];
+  if (a.row_pos) limit = min(limit, a.row_pos[row] + 1);
+  // lane j resolves the row's j-th selected page (topk <= 64)
+  const uint8_t* base = nullptr;
+  int nt = 0, rg = -1;
+  if (lane < a.topk) {
+    const int i = a.sel[(size_t)row * a.topk + lane];
+    if (i >= 0 && i < a.max_pages) {
+      const int page = a.bt[(size_t)b * a.max_pages + i];
+      if (page >= 0 && (int64_t)page < c.N) {
+        const int slot = c.page_to_slot[page];
+        if (slot >= 0) base = c.pool + (size_t)slot * c.row_bytes;
+        else if (a.host_tail) base = c.mirror + (size_t)page * c.row_bytes;
+      }
+      nt = min(MPS, limit - i * MPS);
+      rg = i / RP;
+    }
+    if (!base || nt <= 0) {
+      nt = 0;
+      rg = -1;
+    }
+  }
+  int first = rg >= 0 ? rg : 0x7FFFFFFF, last = rg;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    first = min(first, __shfl_xor(first, o, 64));
+    last = max(last, __shfl_xor(last, o, 64));
+  }
+  const int h = lane & 15, q = lane >> 4;
+  uint16_t* op = a.out + ((size_t)row * c.Hq + g * MG + (h < MG ? h : 0)) * MD + 4 * q;
+  if (last < 0) {                                       // no page at all: zeros, once
+    if (r == 0 && h < MG)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(0u, 0u);
+    return;
+  }
+  if (r < first || r > last) return;
+  uint64_t mine = __ballot(rg == r);
+  if (!mine) return;                                    // nothing in this range: the record stays
+  bf16x8 qop[4];
+  load_query(a, c, row, g, lane, qop);
+  float* rec = c.attn_state + ((size_t)row * c.Hkv + g) * ST_FLOATS;
+  WaveAttn st;
+  init_state(st);
+  const int k = q * MG + h;                             // live lane index (h < 8)
+  if (r != first) {
+    if (h < MG) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) st.acc[dt] = *reinterpret_cast<const f32x4*>(rec + (dt * 32 + k) * 4);
+      const float2 ml = *reinterpret_cast<const float2*>(rec + 8 * 32 * 4 + 2 * h);
+      st.m_run = ml.x;
+      st.l_run = ml.y;
+    } else {
+      st.m_run = 0.f;   // the zero-query columns' max after any page, as in one pass
+    }
+  }
+  const float qscale = 1.4426950408889634f / sqrtf((float)MD);
+  const size_t cb = (size_t)c.code_bytes;
+  const uint64_t bv = reinterpret_cast<uint64_t>(base);
+  const uint32_t b_lo = (uint32_t)bv, b_hi = (uint32_t)(bv >> 32);
+  while (mine) {
+    const int j = __builtin_ctzll(mine);
+    mine &= mine - 1;
+    const int n = __builtin_amdgcn_readlane(nt, j);
+    const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)b_hi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)b_lo, j);
+    wave_page(reinterpret_cast<const uint8_t*>(pv) + (size_t)a.layer * c.layer_bytes, cb, g, n, lane, qop, qscale,
+              st);
+  }
+  if (h >= MG) return;
+  if (r == last) {
+    const float inv = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 o = st.acc[dt] * inv;
+      const uint2 w = make_uint2((uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+                                 (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16));
+      *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(rec + (dt * 32 + k) * 4) = st.acc[dt];
+  if (q == 0) *reinterpret_cast<float2*>(rec + 8 * 32 * 4 + 2 * h) = make_float2(st.m_run, st.l_run);
+}
+
 // a workgroup per (row, KV head, page range); wave w takes every 4th page
 __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_split(DevCtx c, AttnArgs a) {
   __shared__ __align__(16) float sO[MWAVES][MG][MD];
@@ -337,6 +478,16 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
       const int per = NXCD / c.Hkv;
       const int groups = (a.rows + MWAVES - 1) / MWAVES;   // row groups per head
       blocks = NXCD * ((groups + per - 1) / per);
+    }
+    const int RP = c.attn_range_pages;
+    if (RP > 0 && c.attn_state && a.topk <= 64 && a.rows <= c.max_rows && a.max_pages > RP) {
+      const int nr = (a.max_pages + RP - 1) / RP;
+      for (int r = 0; r < nr; ++r) {
+        hipLaunchKernelGGL(k_attn_mfma_range, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a, r, RP);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
     hipLaunchKernelGGL(k_attn_mfma_rows, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a);
     return hipGetLastError();

@@ -64,11 +64,15 @@ struct DevCtx {
   int32_t* pout;            // [max_width] preload ensure: slots
   int32_t* pmiss;           // [max_width][2] preload ensure: misses
   int32_t* pmiss_count;     // [1]
+  float* attn_state;        // [max_rows][Hkv][ATTN_STATE_FLOATS] page-range attention records (or null)
   int max_rows, max_pages, max_topk, max_batch, max_width;
-  int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
+  int attn_impl;
+  int attn_range_pages;     // pages per range of the multi-pass prefill attention (0 = one pass)            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
 };
 
 enum { ATTN_AUTO = 0, ATTN_VECTOR = 1, ATTN_MATRIX = 2 };
+#define ATTN_STATE_FLOATS (8 * 32 * 4 + 8 * 2)
+#define ATTN_RANGE_PAGES_DEFAULT 0
 
 // Words of the selection bitmaps: sum over requests of ceil(rows_b / 64)
 // groups is at most ceil(max_rows / 64) + max_batch.

@@ -237,6 +237,10 @@ class TieredKV:
         """Attention kernel of later calls (tkv_debug_set_attn_kernel)."""
         check(self.lib.tkv_debug_set_attn_kernel(self.ctx, int(kernel)))
 
+    def set_attn_range(self, pages: int) -> None:
+        """Pages per range of the multi-pass prefill attention (0 = one pass)."""
+        check(self.lib.tkv_debug_set_attn_range(self.ctx, int(pages)))
+
     def e4m3_decode(self, codes: torch.Tensor) -> torch.Tensor:
         out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
         check(self.lib.tkv_debug_e4m3_decode(_ptr(codes, torch.uint8, "codes"), out.data_ptr(),
