@@ -17,6 +17,8 @@
 #pragma once
 #include "tkv_dev.h"
 
+#define LRU_CH 8   // order entries per thread per pass
+
 struct EnsureOut {
   int32_t* out_slots;   // [W] or null
   int32_t* miss;        // [W][2]
@@ -91,20 +93,34 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
   }
   __syncthreads();
 
-  // D: victims = the first M slots of the (stamp, slot) order not hit here
+  // D: victims = the first M slots of the (stamp, slot) order not hit here.
+  // Each thread owns ch = ceil(S / 256) (at most LRU_CH) consecutive order
+  // entries, so a pass over up to 256 * LRU_CH slots is one round of loads
+  // and one block scan (ranks stay in order: earlier threads own earlier
+  // entries).
+  const int ch = min(LRU_CH, (c.S + TKV_BLOCK - 1) / TKV_BLOCK);   // entries per thread
   {
     int got = 0;
     const int32_t* ord = c.order + (size_t)par * c.S;
-    for (int base = 0; base < c.S && got < M; base += TKV_BLOCK) {
-      int i = base + tid;
-      int cand = 0, s = 0;
-      if (i < c.S) {
-        s = ord[i];
-        cand = c.touched[s] ? 0 : 1;
+    for (int base = 0; base < c.S && got < M; base += TKV_BLOCK * ch) {
+      const int i0 = base + tid * ch;
+      int sl[LRU_CH], cand[LRU_CH];
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u) sl[u] = (u < ch && i0 + u < c.S) ? ord[i0 + u] : 0;
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u) {
+        cand[u] = (u < ch && i0 + u < c.S) && !c.touched[sl[u]];
+        cnt += cand[u];
       }
       int tot;
-      int ex = block_excl_scan(cand, &tot, sm_scan);
-      if (cand && got + ex < M) c.victims[got + ex] = s;
+      int r = got + block_excl_scan(cnt, &tot, sm_scan);
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u)
+        if (cand[u]) {
+          if (r < M) c.victims[r] = sl[u];
+          ++r;
+        }
       got += tot;
     }
   }
@@ -162,32 +178,47 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
   }
 
   // H: next order = untouched slots in old order, then touched slots by index
+  // (ch consecutive entries per thread per pass, as in D)
   {
     const int32_t* ord = c.order + (size_t)par * c.S;
     int32_t* nxt = c.order + (size_t)(1 - par) * c.S;
     int run = 0;
-    for (int base = 0; base < c.S; base += TKV_BLOCK) {
-      int i = base + tid;
-      int u = 0, s = 0;
-      if (i < c.S) {
-        s = ord[i];
-        u = c.touched[s] ? 0 : 1;
+    for (int base = 0; base < c.S; base += TKV_BLOCK * ch) {
+      const int i0 = base + tid * ch;
+      int sl[LRU_CH], keep[LRU_CH];
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u) sl[u] = (u < ch && i0 + u < c.S) ? ord[i0 + u] : 0;
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u) {
+        keep[u] = (u < ch && i0 + u < c.S) && !c.touched[sl[u]];
+        cnt += keep[u];
       }
       int tot;
-      int ex = block_excl_scan(u, &tot, sm_scan);
-      if (u) nxt[run + ex] = s;
+      int r = run + block_excl_scan(cnt, &tot, sm_scan);
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u)
+        if (keep[u]) nxt[r++] = sl[u];
       run += tot;
     }
     __syncthreads();
-    for (int base = 0; base < c.S; base += TKV_BLOCK) {
-      int s = base + tid;
-      int t = (s < c.S) ? c.touched[s] : 0;
-      int tot;
-      int ex = block_excl_scan(t, &tot, sm_scan);
-      if (t) {
-        nxt[run + ex] = s;
-        c.touched[s] = 0;
+    for (int base = 0; base < c.S; base += TKV_BLOCK * ch) {
+      const int s0 = base + tid * ch;
+      int t[LRU_CH];
+      int cnt = 0;
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u) {
+        t[u] = (u < ch && s0 + u < c.S) ? c.touched[s0 + u] : 0;
+        cnt += t[u];
       }
+      int tot;
+      int r = run + block_excl_scan(cnt, &tot, sm_scan);
+#pragma unroll
+      for (int u = 0; u < LRU_CH; ++u)
+        if (t[u]) {
+          nxt[r++] = s0 + u;
+          c.touched[s0 + u] = 0;
+        }
       run += tot;
     }
   }

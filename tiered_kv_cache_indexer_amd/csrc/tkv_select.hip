@@ -434,13 +434,17 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
   if (r >= a.rows) return;
   const int b = request_of_row(a.row_start, a.B, r);
   const int visible = visible_pages(a, c.PS, b, r);
-  const int nl = (visible + 63) >> 6;
   const float* sc = c.scores + (size_t)r * c.max_pages;
+  // keys stay in registers: every load is in bounds (index clamped) and every
+  // loop below is fully unrolled without data-dependent branches; keys past
+  // the visible pages are 0, which no threshold (>= 1) counts
   uint64_t key[NPL];
+  const int pmax = visible > 0 ? visible - 1 : 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int p = i * 64 + lane;
-    key[i] = (i < nl && p < visible) ? sel_key(sc[p], p) : 0ull;   // valid keys are nonzero
+    const float v = sc[min(p, pmax)];
+    key[i] = p < visible ? sel_key(v, p) : 0ull;   // valid keys are nonzero
   }
   const int k = a.topk;
   uint64_t thr = 1;
@@ -450,8 +454,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
       const uint64_t cand = t | (1ull << bit);
       int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (i < nl) cnt += key[i] >= cand ? 1 : 0;
+      for (int i = 0; i < NPL; ++i) cnt += key[i] >= cand ? 1 : 0;
       const int tot = wave_count6(cnt);
       if (tot >= k) {
         t = cand;
@@ -467,7 +470,6 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
   int base = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    if (i >= nl) break;
     const bool s = key[i] >= thr;
     const uint64_t m = __ballot(s);
     if (s) {
