@@ -35,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -77,41 +78,124 @@ struct WaveAttn {
   float m_run, l_run;
 };
 
-// One page (nt >= 1 visible tokens) of KV head g, layer block `blk` of a pool
-// slot, folded into the wave's running state.
-__device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, int nt, int lane,
-                                          const bf16x8 (&qop)[4], float qscale, WaveAttn& st) {
+// Query operand of S^T = K.Q^T on the fp8 matrix cores
+// (v_mfma_scale_f32_16x16x128_f8f6f4: lane l supplies row l%16 of A and
+// column l%16 of B over contraction indices 32*(l/16) .. +31, one byte each).
+// The K codes are the A operand as stored.  The query, scaled by 2^-e so its
+// largest magnitude is in [128, 256), is split into two e4m3 parts,
+// q' = hi + lo (hi = e4m3(q'), lo = e4m3(q' - hi)); the instruction's E8M0
+// B scale 2^e undoes the scaling exactly.  For a query on a 2^-5 grid
+// bounded by 4 the split is exact; in general hi + lo carries 8 significant
+// bits, as the bf16 query does.
+struct QOp {
+  i32x8 hi, lo;
+  int scale;   // E8M0: 127 + e
+};
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c2, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c2, d, w, true);
+  return (uint32_t)w;
+}
+
+// The row's query slice this lane needs: head lane%16 (< 8), elements
+// 32*(lane/16) .. +31, as raw bf16 (four 16-byte loads).
+__device__ __forceinline__ void load_query_raw(const AttnArgs& a, const DevCtx& c, int r, int g, int lane,
+                                               uint4 (&raw)[4]) {
+  const int h = lane & 15, q = lane >> 4;
+  if (h < MG) {
+    const uint16_t* qh = a.q + ((size_t)r * c.Hq + g * MG + h) * MD + 32 * q;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>(qh + 8 * u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+__device__ __forceinline__ void make_qop(const uint4 (&raw)[4], QOp& qo) {
+  float x[32];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t ww[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[8 * u + 2 * t] = __uint_as_float(ww[t] << 16);
+      x[8 * u + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+    }
+  }
+  // the wave's largest magnitude -> e with max * 2^-e in [128, 256)
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mx = fmaxf(mx, fabsf(x[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  int e = 0;
+  if (mx > 0.f) e = min(max(ilogbf(mx) - 7, -126), 126);
+  qo.scale = 127 + e;
+  uint32_t hw[8], lw[8];
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    float y[4], lo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) y[t] = ldexpf(x[i + t], -e);
+    const uint32_t hb = fp8x4(y[0], y[1], y[2], y[3]);
+    const f32x2 h01 = e4m3x2_lo(hb), h23 = e4m3x2_hi(hb);
+    lo[0] = y[0] - h01.x; lo[1] = y[1] - h01.y; lo[2] = y[2] - h23.x; lo[3] = y[3] - h23.y;
+    hw[i / 4] = hb;
+    lw[i / 4] = fp8x4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  qo.hi = i32x8{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
+  qo.lo = i32x8{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
+}
+
+__device__ __forceinline__ void load_query(const AttnArgs& a, const DevCtx& c, int r, int g, int lane, QOp& qo) {
+  uint4 raw[4];
+  load_query_raw(a, c, r, g, lane, raw);
+  make_qop(raw, qo);
+}
+
+// One page of one KV head in registers: K codes as the fp8 A operand of the
+// four S tiles, V^T codes (16 tokens of one d row per lane and d tile), and
+// the K and V scales of the 16 tokens this lane's output fragment holds.
+struct PageRegs {
+  i32x8 ka[4];
+  uint4 vr[8];
+  float4 ks4[4], vs4[4];   // K / V scales of tokens 16q + 4i .. +3 (q = lane / 16)
+};
+
+__device__ __forceinline__ void load_page(const uint8_t* blk, size_t cb, int g, int lane, PageRegs& pr) {
   const int m = lane & 15, q = lane >> 4;
   const uint8_t* kb = blk + (size_t)g * MPS * MD;
   const uint8_t* vb = blk + cb + (size_t)g * MPS * MD;
-  const float* ksc = reinterpret_cast<const float*>(blk + 2 * cb);
-  uint4 kr[4][2], vr[8];
-  float4 ks4[4], vs4[4];
+  const uint8_t* sc = blk + 2 * cb;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int t = 16 * (m >> 2) + 4 * mt + (m & 3);
-    kr[mt][0] = gld<uint4>(kb + t * MD + 16 * q);
-    kr[mt][1] = gld<uint4>(kb + t * MD + 64 + 16 * q);
+    const uint4 k0 = gld<uint4>(kb + t * MD + 32 * q);
+    const uint4 k1 = gld<uint4>(kb + t * MD + 32 * q + 16);
+    pr.ka[mt] = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ks4[i] = gld<float4>(reinterpret_cast<const uint8_t*>(ksc + 16 * q + 4 * i));
+  for (int dt = 0; dt < 8; ++dt) pr.vr[dt] = gld<uint4>(vb + (16 * dt + m) * MPS + 16 * q);
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) vr[dt] = gld<uint4>(vb + (16 * dt + m) * MPS + 16 * q);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) vs4[i] = gld<float4>(reinterpret_cast<const uint8_t*>(ksc + MPS + 16 * q + 4 * i));
+  for (int i = 0; i < 4; ++i) {
+    pr.ks4[i] = gld<float4>(sc + 4 * (16 * q + 4 * i));
+    pr.vs4[i] = gld<float4>(sc + 4 * MPS + 4 * (16 * q + 4 * i));
+  }
+}
 
-  // S^T tiles
+// Fold one loaded page (nt >= 1 visible tokens) into the wave's running state.
+__device__ __forceinline__ void fold_page(const PageRegs& pr, int nt, int lane, const QOp& qo, float qscale,
+                                          WaveAttn& st) {
+  const int q = lane >> 4;
+  // S^T tiles: two fp8 products per 16 keys (query hi and lo parts)
   f32x4 s[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    bf16x8 a0, a1, a2, a3;
-    fp8x16_to_bf16(kr[mt][0], a0, a1);
-    fp8x16_to_bf16(kr[mt][1], a2, a3);
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qop[0], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qop[1], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, qop[2], z, 0, 0, 0);
-    z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, qop[3], z, 0, 0, 0);
+    z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pr.ka[mt], qo.hi, z, 0, 0, 0, 127, 0, qo.scale);
+    z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pr.ka[mt], qo.lo, z, 0, 0, 0, 127, 0, qo.scale);
     s[mt] = z;
   }
   // logits in the exp2 domain, masked past the visible tokens (a full page,
@@ -120,7 +204,7 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
   const bool full = nt >= MPS;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const float kv4[4] = {ks4[mt].x, ks4[mt].y, ks4[mt].z, ks4[mt].w};
+    const float kv4[4] = {pr.ks4[mt].x, pr.ks4[mt].y, pr.ks4[mt].z, pr.ks4[mt].w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float x = s[mt][v] * (kv4[v] * qscale);
@@ -150,7 +234,7 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
   f32x8 pv[2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const float vv4[4] = {vs4[mt].x, vs4[mt].y, vs4[mt].z, vs4[mt].w};
+    const float vv4[4] = {pr.vs4[mt].x, pr.vs4[mt].y, pr.vs4[mt].z, pr.vs4[mt].w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float p = __builtin_amdgcn_exp2f(s[mt][v] - m_ref);
@@ -166,7 +250,7 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     bf16x8 v0, v1;
-    fp8x16_to_bf16(vr[dt], v0, v1);
+    fp8x16_to_bf16(pr.vr[dt], v0, v1);
     f32x4 o = st.acc[dt];
     o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb0, o, 0, 0, 0);
     o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pb1, o, 0, 0, 0);
@@ -174,10 +258,117 @@ __device__ __forceinline__ void wave_page(const uint8_t* blk, size_t cb, int g, 
   }
 }
 
+// Fold the pages flagged in `mask` (wave-uniform; bit j = lane j's page:
+// row pointer rows_lo/hi, visible tokens nt) in ascending lane order,
+// loading each page straight into registers (decode: about one page per
+// wave).
+__device__ __forceinline__ void fold_pages(uint64_t mask, uint32_t rows_lo, uint32_t rows_hi, int nt,
+                                           size_t layer_off, size_t cb, int g, int lane, QOp& qo, bool& have_q,
+                                           const uint4 (&qraw)[4], float qscale, WaveAttn& st) {
+  while (mask) {
+    const int j = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)rows_hi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)rows_lo, j);
+    PageRegs cur;
+    load_page(reinterpret_cast<const uint8_t*>(pv) + layer_off, cb, g, lane, cur);
+    if (!have_q) {                 // built while the first page's loads are in flight
+      make_qop(qraw, qo);
+      have_q = true;
+    }
+    fold_page(cur, __builtin_amdgcn_readlane(nt, j), lane, qo, qscale, st);
+  }
+}
+
+// ---- LDS-staged page pipeline (many pages per wave) ----------------------
+// Each wave owns a 17 KiB LDS buffer.  While a page is folded from
+// registers, the next page is already streaming into the buffer with
+// direct global->LDS 16-byte loads (lane L's bytes land at base + 16 L), so
+// a wave keeps a page in flight without registers for it.  The buffer
+// holds the page XOR-swizzled so that the operand reads are free of bank
+// conflicts: K row t's 16-byte chunk c sits at granule 8t + (c ^ fK(t));
+// V^T row r's chunk c at granule 512 + 4r + (c ^ fV(r)); then the K and V
+// scales (granules 1024..1055, K then V; lanes 32..63 load a duplicate copy).
+constexpr int PBUF = 17408;
+__device__ __forceinline__ int fK(int t) { return ((t >> 4) & 3) | ((t & 2) << 1); }
+__device__ __forceinline__ int fV(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void stage_page(const uint8_t* blk, size_t cb, int g, int lane, uint8_t* buf) {
+  const uint8_t* kb = blk + (size_t)g * MPS * MD;
+  const uint8_t* vb = blk + cb + (size_t)g * MPS * MD;
+  const uint8_t* sc = blk + 2 * cb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int G = 64 * i + lane, t = G >> 3, ch = (G & 7) ^ fK(t);
+    __builtin_amdgcn_global_load_lds((const void*)(kb + t * MD + 16 * ch), buf + 1024 * i, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int G = 64 * i + lane, r = G >> 2, ch = (G & 3) ^ fV(r);
+    __builtin_amdgcn_global_load_lds((const void*)(vb + r * MPS + 16 * ch), buf + 8192 + 1024 * i, 16, 0, 0);
+  }
+  __builtin_amdgcn_global_load_lds((const void*)(sc + 16 * (lane & 31)), buf + 16384, 16, 0, 0);
+}
+
+__device__ __forceinline__ void read_page(const uint8_t* buf, int lane, PageRegs& pr) {
+  const int m = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int t = 16 * (m >> 2) + 4 * mt + (m & 3), f = fK(t);
+    const uint4 k0 = *reinterpret_cast<const uint4*>(buf + 16 * (8 * t + ((2 * q) ^ f)));
+    const uint4 k1 = *reinterpret_cast<const uint4*>(buf + 16 * (8 * t + ((2 * q + 1) ^ f)));
+    pr.ka[mt] = i32x8{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int r = 16 * dt + m;
+    pr.vr[dt] = *reinterpret_cast<const uint4*>(buf + 8192 + 16 * (4 * r + (q ^ fV(r))));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr.ks4[i] = *reinterpret_cast<const float4*>(buf + 16384 + 4 * (16 * q + 4 * i));
+    pr.vs4[i] = *reinterpret_cast<const float4*>(buf + 16384 + 4 * MPS + 4 * (16 * q + 4 * i));
+  }
+}
+
+// As fold_pages, with the next page staged through the wave's LDS buffer.
+__device__ __forceinline__ void fold_pages_lds(uint64_t mask, uint32_t rows_lo, uint32_t rows_hi, int nt,
+                                               size_t layer_off, size_t cb, int g, int lane, const QOp& qo,
+                                               float qscale, WaveAttn& st, uint8_t* buf) {
+  if (!mask) return;
+  auto row_of = [&](int jj) {
+    const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)rows_hi, jj) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)rows_lo, jj);
+    return reinterpret_cast<const uint8_t*>(pv) + layer_off;
+  };
+  int j = __builtin_ctzll(mask);
+  mask &= mask - 1;
+  stage_page(row_of(j), cb, g, lane, buf);
+  while (true) {
+    __builtin_amdgcn_s_waitcnt(0);          // the staged page has landed
+    PageRegs cur;
+    read_page(buf, lane, cur);
+    __builtin_amdgcn_s_waitcnt(0);          // reads done before the buffer is refilled
+    const int n = __builtin_amdgcn_readlane(nt, j);
+    const bool more = mask != 0;
+    if (more) {
+      j = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      stage_page(row_of(j), cb, g, lane, buf);
+    }
+    fold_page(cur, n, lane, qo, qscale, st);
+    if (!more) break;
+  }
+}
+
 // Pages j = jbeg, jbeg + jstep, ... < jend of row r (request b), KV head g.
+// The query operand: ready (STAGED) or built by the register path from the
+// raw query once the first page's loads are in flight.
+template <bool STAGED>
 __device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, int r, int b, int g,
                                            int jbeg, int jend, int jstep, int lane,
-                                           const bf16x8 (&qop)[4], WaveAttn& st) {
+                                           QOp& qop, bool& have_q, const uint4 (&qraw)[4], WaveAttn& st,
+                                           uint8_t* lds) {
   int limit = a.ctx_len[b];
   if (a.row_pos) limit = min(limit, a.row_pos[r] + 1);
   const float qscale = 1.4426950408889634f / sqrtf((float)MD);
@@ -208,31 +399,13 @@ __device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, i
       if (!row) nt = 0;
     }
     const uint64_t rowv = reinterpret_cast<uint64_t>(row);
-    const uint32_t row_lo = (uint32_t)rowv, row_hi = (uint32_t)(rowv >> 32);
-    const int cnt = min(64, (jend - base + jstep - 1) / jstep);
-    for (int i = 0; i < cnt; ++i) {
-      const int n = __builtin_amdgcn_readlane(nt, i);
-      if (n <= 0) continue;
-      const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, i) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)row_lo, i);
-      wave_page(reinterpret_cast<const uint8_t*>(pv) + (size_t)a.layer * c.layer_bytes, cb, g, n, lane, qop,
-                qscale, st);
-    }
-  }
-}
-
-__device__ __forceinline__ void load_query(const AttnArgs& a, const DevCtx& c, int r, int g, int lane,
-                                           bf16x8 (&qop)[4]) {
-  const int h = lane & 15, q = lane >> 4;
-  if (h < MG) {
-    const uint16_t* qh = a.q + ((size_t)r * c.Hq + g * MG + h) * MD + 16 * q;
-    qop[0] = ld_q8(qh);
-    qop[1] = ld_q8(qh + 8);
-    qop[2] = ld_q8(qh + 64);
-    qop[3] = ld_q8(qh + 72);
-  } else {
-    const bf16x8 z = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    qop[0] = z; qop[1] = z; qop[2] = z; qop[3] = z;
+    const uint64_t mask = __ballot(nt > 0);
+    if constexpr (STAGED)
+      fold_pages_lds(mask, (uint32_t)rowv, (uint32_t)(rowv >> 32), nt, (size_t)a.layer * c.layer_bytes, cb, g,
+                     lane, qop, qscale, st, lds);
+    else
+      fold_pages(mask, (uint32_t)rowv, (uint32_t)(rowv >> 32), nt, (size_t)a.layer * c.layer_bytes, cb, g, lane,
+                 qop, have_q, qraw, qscale, st);
   }
 }
 
@@ -254,7 +427,8 @@ constexpr int NXCD = 8;
 __host__ __device__ __forceinline__ bool attn_rows_by_xcd(int Hkv) { return Hkv <= NXCD && NXCD % Hkv == 0; }
 
 // one wave per (row, KV head), all of the row's pages
-__global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
+__global__ __launch_bounds__(TKV_BLOCK, 2) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
+  __shared__ __align__(16) uint8_t pbuf[MWAVES][PBUF];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int r, g;
   if (attn_rows_by_xcd(c.Hkv)) {
@@ -269,11 +443,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs
   }
   if (r >= a.rows) return;
   const int b = attn_row_request(a, r);
-  bf16x8 qop[4];
+  QOp qop;
   load_query(a, c, r, g, lane, qop);
   WaveAttn st;
   init_state(st);
-  wave_pages(c, a, r, b, g, 0, a.topk, 1, lane, qop, st);
+  bool have_q = true;
+  const uint4 no_raw[4] = {};
+  wave_pages<true>(c, a, r, b, g, 0, a.topk, 1, lane, qop, have_q, no_raw, st, pbuf[wave]);
   const int h = lane & 15, q = lane >> 4;
   if (h >= MG) return;
   const float inv = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
@@ -302,7 +478,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_rows(DevCtx c, AttnArgs
 constexpr int ST_FLOATS = ATTN_STATE_FLOATS;   // O^T tiles of the 32 live lanes, then (m, l) per head
 static_assert(ST_FLOATS == 8 * 32 * 4 + MG * 2, "record layout");
 
-__global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_range(DevCtx c, AttnArgs a, int r, int RP) {
+__global__ __launch_bounds__(TKV_BLOCK, 2) void k_attn_mfma_range(DevCtx c, AttnArgs a, int r, int RP) {
+  __shared__ __align__(16) uint8_t pbuf[MWAVES][PBUF];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int row, g;
   if (attn_rows_by_xcd(c.Hkv)) {
@@ -356,7 +533,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_range(DevCtx c, AttnArg
   if (r < first || r > last) return;
   uint64_t mine = __ballot(rg == r);
   if (!mine) return;                                    // nothing in this range: the record stays
-  bf16x8 qop[4];
+  QOp qop;
   load_query(a, c, row, g, lane, qop);
   float* rec = c.attn_state + ((size_t)row * c.Hkv + g) * ST_FLOATS;
   WaveAttn st;
@@ -376,16 +553,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_range(DevCtx c, AttnArg
   const float qscale = 1.4426950408889634f / sqrtf((float)MD);
   const size_t cb = (size_t)c.code_bytes;
   const uint64_t bv = reinterpret_cast<uint64_t>(base);
-  const uint32_t b_lo = (uint32_t)bv, b_hi = (uint32_t)(bv >> 32);
-  while (mine) {
-    const int j = __builtin_ctzll(mine);
-    mine &= mine - 1;
-    const int n = __builtin_amdgcn_readlane(nt, j);
-    const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)b_hi, j) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)b_lo, j);
-    wave_page(reinterpret_cast<const uint8_t*>(pv) + (size_t)a.layer * c.layer_bytes, cb, g, n, lane, qop, qscale,
-              st);
-  }
+  fold_pages_lds(mine, (uint32_t)bv, (uint32_t)(bv >> 32), nt, (size_t)a.layer * c.layer_bytes, cb, g, lane, qop,
+                 qscale, st, pbuf[wave]);
   if (h >= MG) return;
   if (r == last) {
     const float inv = st.l_run > 0.f ? 1.f / st.l_run : 0.f;
@@ -415,11 +584,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_split(DevCtx c, AttnArg
   const int j0 = split * a.pages_per_split;
   const int j1 = min(a.topk, j0 + a.pages_per_split);
   const int b = attn_row_request(a, r);
-  bf16x8 qop[4];
-  load_query(a, c, r, g, lane, qop);
+  uint4 qraw[4];
+  load_query_raw(a, c, r, g, lane, qraw);
+  QOp qop;
+  bool have_q = false;
   WaveAttn st;
   init_state(st);
-  wave_pages(c, a, r, b, g, j0 + wave, j1, MWAVES, lane, qop, st);
+  wave_pages<false>(c, a, r, b, g, j0 + wave, j1, MWAVES, lane, qop, have_q, qraw, st, nullptr);
   const int h = lane & 15, q = lane >> 4;
   if (h < MG) {
 #pragma unroll
