@@ -269,6 +269,64 @@ __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, 
   }
 }
 
+// Wave count of a per-lane count below 2^7: one ballot per bit.
+__device__ __forceinline__ int wave_count7(int cnt) {
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) tot += __popcll(__ballot((cnt >> j) & 1)) << j;
+  return tot;
+}
+
+// Top-k (k <= 64) of a row from its chunks' candidate lists (each sorted
+// descending), by one wave: only the first k entries of a list can be
+// selected, so lane L holds entry L (L < k) of every list.  The k-th largest
+// key is found by the radix descent used for prefill rows; the selected
+// page indices are gathered through LDS and sorted ascending.
+template <int NC>
+__device__ void row_topk_lists_wave(const uint64_t* cand, int n_lists, int k, int32_t* out, int* sm_idx) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NC];
+  const int last = n_lists > 0 ? n_lists - 1 : 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint64_t v = cand[(size_t)min(i, last) * 64 + lane];
+    key[i] = (i < n_lists && lane < k) ? v : 0ull;      // empty entries are 0
+  }
+  int cnt0 = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) cnt0 += key[i] != 0ull ? 1 : 0;
+  const int total = wave_count7(cnt0);
+  uint64_t thr = 1;
+  if (total > k) {
+    uint64_t t = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t c2 = t | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) cnt += key[i] >= c2 ? 1 : 0;
+      const int tot = wave_count7(cnt);
+      if (tot >= k) {
+        t = c2;
+        if (tot == k) break;
+      }
+    }
+    thr = t;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const bool sel = key[i] >= thr;
+    const uint64_t m = __ballot(sel);
+    if (sel) sm_idx[base + __popcll(m & below)] = sel_key_index(key[i]);
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  int idx = (lane < base) ? sm_idx[lane] : 0x7FFFFFFF;
+  idx = wave_sort_asc_i32(idx);
+  if (lane < k) out[lane] = idx == 0x7FFFFFFF ? -1 : idx;
+}
+
 template <int E8>
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) {
   extern __shared__ __align__(16) uint32_t dyn[];
@@ -372,14 +430,25 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     }
   }
   if (!last_block_arrive(&c.row_done[r], a.n_chunks, &sm_misc[4])) return;
-  if (a.topk <= 64) {
-    row_topk64_block(a.n_chunks, a.topk, a.sel_local + (size_t)r * a.topk, reinterpret_cast<uint64_t*>(dyn),
+  int32_t* out_r = a.sel_local + (size_t)r * a.topk;
+  if (a.topk <= 64 && a.n_chunks <= 16) {
+    // few lists (up to 1,024 pages): one wave, radix descent over the first
+    // k entries of every list; more lists merge faster across 4 waves
+    if (wave == 0) {
+      int* sm_idx = reinterpret_cast<int*>(&sm_keys[0][0]);
+      if (a.n_chunks <= 8) row_topk_lists_wave<8>(cand, a.n_chunks, a.topk, out_r, sm_idx);
+      else row_topk_lists_wave<16>(cand, a.n_chunks, a.topk, out_r, sm_idx);
+    }
+    __syncthreads();
+  } else if (a.topk <= 64) {
+    row_topk64_block(a.n_chunks, a.topk, out_r, reinterpret_cast<uint64_t*>(dyn),
                      [&](int ch) { return cand[(size_t)ch * 64 + lane]; });
   } else {
-    row_topk_block(sc, visible, a.topk, a.sel_local + (size_t)r * a.topk, dyn, hist, sm_scan, sm_misc);
+    row_topk_block(sc, visible, a.topk, out_r, dyn, hist, sm_scan, sm_misc);
   }
   mark_row_pages(c, a, b, r);
-  if (!last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
+  // a single row's last workgroup is the last workgroup of the launch
+  if (a.rows > 1 && !last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
   select_finish(c, a, dyn, sm_scan);
 }
 
