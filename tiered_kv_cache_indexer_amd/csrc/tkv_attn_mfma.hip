@@ -4,15 +4,18 @@
 // FreeToken PR #499, "Design": after the ensure, attention reads only the
 // selected pages through the logical->physical translation; vLLM RFC #33980,
 // "Proposed Change": attention over the top-k KV.  The arithmetic is the
-// same softmax as the vector kernel; only the products move to
-// v_mfma_f32_16x16x32_bf16 (e4m3 codes are exact in bf16).
+// same softmax as the vector kernel; the products move to the matrix cores:
+// S = Q.K^T on the fp8 instruction v_mfma_scale_f32_16x16x128_f8f6f4 (K codes
+// as stored; the query scaled by a power of two and split into two e4m3
+// parts, exact for bf16 queries with up to 8 significant bits), and P.V on
+// v_mfma_f32_16x16x32_bf16 (e4m3 V codes are exact in bf16).
 //
 // One wave processes one selected page of one (row, KV head) at a time.
 //  * S^T = K . Q^T: the 64 keys of the page are four 16-row A tiles, the
 //    8 query heads are B columns 0..7 (columns 8..15 zero).  The
 //    contraction over d runs in an order in which a lane's A slice is two
-//    16-byte loads of its key row; the query operand (loaded once) uses the
-//    same order.  Row m of A tile `mt` is token 16*(m/4) + 4*mt + m%4, so
+//    16-byte loads of its key row (32 fp8 codes); the query operand (built
+//    once per (row, KV head)) uses the same order.  Row m of A tile `mt` is token 16*(m/4) + 4*mt + m%4, so
 //    the output fragment of lane (q = lane/16, h = lane%16) holds tokens
 //    16q .. 16q+15 of head h: the online softmax is per lane plus two
 //    cross-lane reductions.
