@@ -181,6 +181,19 @@ int tkv_lru_ensure(tkv_ctx* ctx, const int32_t* needed, int32_t width, const uin
 int tkv_fetch_pages(tkv_ctx* ctx, const int32_t* miss, const int32_t* miss_count, int32_t width,
                     void* stream);
 
+/* The copy of tkv_fetch_pages in two parts, the parts tkv_decode_layer_split
+ * issues.  tkv_fetch_pages_layer copies, for every miss, only layer
+ * `layer`'s slice of the row (its K and V codes and scales) and keeps a copy
+ * of the miss list and count in the ctx; it adds the whole rows to
+ * bytes_fetched.  tkv_fetch_pages_rest copies the rest of the rows of the
+ * list the last tkv_fetch_pages_layer kept, for the same `layer`; it must
+ * follow that call in stream order (or by an event) and come before the next
+ * one.  Both parts together write exactly what tkv_fetch_pages writes.
+ * width <= max_width; miss, miss_count as for tkv_fetch_pages. */
+int tkv_fetch_pages_layer(tkv_ctx* ctx, const int32_t* miss, const int32_t* miss_count, int32_t width,
+                          int32_t layer, void* stream);
+int tkv_fetch_pages_rest(tkv_ctx* ctx, int32_t width, int32_t layer, void* stream);
+
 /* Sparse paged attention over the selected pages (PR #499 "Design": after
  * ensure the block table is translated logical->physical; the page ids are
  * translated here through the LRU's page->slot map).  For row r of request b
@@ -223,6 +236,34 @@ int tkv_decode_layer(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
                      const int32_t* ctx_len, const float* page_bias, int32_t topk,
                      int32_t* sel_local, int32_t* needed, int32_t* out_slots, int32_t* miss,
                      int32_t* miss_count, uint16_t* out, void* stream);
+
+/* tkv_decode_layer with the fused row copy (FreeToken PR #499, "Design":
+ * one copy per miss carries the page for every layer) issued in two parts:
+ * on `stream`, for every miss, the slices of `layer` (what this layer's
+ * attention reads) and of the next layer ((layer+1) mod num_layers); then on
+ * `copy_stream` the rest of the rows, overlapping this layer's attention and
+ * the next call's selection and ensure.  A call for the layer after the
+ * previous call's, with num_slots >= W_prev + 2*W (W = B * the compaction
+ * width), chains: no slot the previous call filled can be rebound by this
+ * call's ensure, so this call's slice copy waits only for the rest copy of
+ * the call two back, and its attention for nothing on `copy_stream`.  Any
+ * other call waits for every earlier copy; so does every other call of this
+ * library that touches the pool or the state (select_pages and lru_ensure
+ * end a chain).
+ * Results (sel, needed, slots, misses, attention, LRU state, counters) and,
+ * once the copy stream is done, pool contents are those of tkv_decode_layer.
+ * Ordering the caller owns: work of its own that reads the pool, and the
+ * end of a graph capture, must first wait for `copy_stream` (one wait at
+ * the end of a step suffices).  Inside a capture the first call does not
+ * wait for copies issued outside it: order graph replays after eager work,
+ * as for any capture.  `copy_stream` may equal `stream` (the parts then run
+ * in order on it).  One layer (num_layers == 1): same as tkv_decode_layer.
+ * Calls on one ctx must not overlap. */
+int tkv_decode_layer_split(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
+                           const int32_t* ctx_len, const float* page_bias, int32_t topk,
+                           int32_t* sel_local, int32_t* needed, int32_t* out_slots, int32_t* miss,
+                           int32_t* miss_count, uint16_t* out, void* stream, void* copy_stream);
 
 /* tkv_decode_layer preceded by a preload of a predicted page list (vLLM RFC
  * #33980, "Topk KV preload": an earlier top-k index, e.g. the next layer's

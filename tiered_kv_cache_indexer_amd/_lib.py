@@ -71,6 +71,9 @@ SIGNATURES = {
     "tkv_sparse_paged_attn_host_tail": (C.c_int, [P, I32, P, I32, P, P, P, I32, P, P, I32, I32, P, P]),
     "tkv_decode_layer": (C.c_int, [P, I32, P, I32, P, I32, P, P, P, I32, P, P, P, P, P, P, P]),
     "tkv_decode_layer_prefetch": (C.c_int, [P, I32, P, I32, P, I32, P, P, P, I32, P, P, P, P, P, P, P, I32, P, P]),
+    "tkv_fetch_pages_layer": (C.c_int, [P, P, P, I32, I32, P]),
+    "tkv_fetch_pages_rest": (C.c_int, [P, I32, I32, P]),
+    "tkv_decode_layer_split": (C.c_int, [P, I32, P, I32, P, I32, P, P, P, I32, P, P, P, P, P, P, P, P]),
     "tkv_ensure_write_pages": (C.c_int, [P, I32, P, P, P, I32, P, I32, P, P]),
     "tkv_store_kv_mirror": (C.c_int, [P, I32, P, P, I32, P, P, P, P, I32, P, I32, P]),
     "tkv_read_counters": (C.c_int, [P, C.POINTER(Counters), P]),

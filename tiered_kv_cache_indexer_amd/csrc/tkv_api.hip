@@ -22,6 +22,16 @@ struct tkv_ctx {
   DevCtx dev{};
   int C = 0;            // compaction width (set_select_width)
   hipEvent_t ev_pre = nullptr, ev_copy = nullptr;   // preload ordering (created on first use)
+  // Split decode copies (tkv_decode_layer_split).  Call k of a chain copies
+  // its layer's and the next layer's slices on the caller's stream (ev_slice
+  // after them), then the rest of the rows on the copy stream (ev_rest[k & 1]
+  // after it), from miss-list copy k & 1.  rest_last indexes the latest
+  // ev_rest; rest_cap is the capture sequence it was recorded in (0: none);
+  // last_split is cleared by every other call.
+  hipEvent_t ev_slice = nullptr, ev_rest[2] = {nullptr, nullptr};
+  bool rest_pending = false, last_split = false;
+  unsigned long long rest_cap = 0;
+  int rest_last = 0, chain_len = 0, prev_layer = -1, prev_width = 0;
 };
 
 static thread_local std::string g_err;
@@ -56,7 +66,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_attn_state, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_attn_state, ws_total;
 };
 
 static int validate(const tkv_config* c) {
@@ -134,6 +144,7 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_pout = o; o = align256(o + W * 4);
   L.ws_pmiss = o; o = align256(o + W * 8);
   L.ws_pmiss_count = o; o = align256(o + 4);
+  L.ws_bg_miss = o; o = align256(o + 2 * (1 + 2 * W) * 4);
   // records of the page-range prefill attention: only configs with more rows than requests
   L.ws_attn_state = o;
   if (c->max_rows > c->max_batch) o = align256(o + R * (size_t)H * ATTN_STATE_FLOATS * 4);
@@ -196,6 +207,10 @@ void tkv_destroy(tkv_ctx* c) {
   if (!c) return;
   if (c->ev_pre) hipEventDestroy(c->ev_pre);
   if (c->ev_copy) hipEventDestroy(c->ev_copy);
+  for (hipEvent_t e : c->ev_rest)
+    if (e) hipEventSynchronize(e);
+  for (hipEvent_t e : {c->ev_slice, c->ev_rest[0], c->ev_rest[1]})
+    if (e) hipEventDestroy(e);
   if (c->mirror_host) hipHostFree(c->mirror_host);
   delete c;
 }
@@ -250,6 +265,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.pout = (int32_t*)(ws + L.ws_pout);
   d.pmiss = (int32_t*)(ws + L.ws_pmiss);
   d.pmiss_count = (int32_t*)(ws + L.ws_pmiss_count);
+  d.bg_miss = (int32_t*)(ws + L.ws_bg_miss);
   d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;
   d.attn_range_pages = ATTN_RANGE_PAGES_DEFAULT;
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
@@ -284,9 +300,81 @@ static int need_attached(tkv_ctx* c) {
   return TKV_OK;
 }
 
+// Capture sequence `s` records into (0 when it is not capturing).
+static unsigned long long capture_id(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  if (hipStreamGetCaptureInfo(s, &st, &id) != hipSuccess || st != hipStreamCaptureStatusActive) return 0;
+  return id;
+}
+
+// Orders `s` after the last rest-of-rows copy of a split decode call.  A copy
+// recorded in another capture sequence (or outside the one `s` records into)
+// is not waited for: a graph holds only its own work, and the caller orders
+// graphs against eager work.
+static int wait_rest(tkv_ctx* c, hipStream_t s) {
+  c->last_split = false;
+  if (!c->rest_pending || capture_id(s) != c->rest_cap) return TKV_OK;
+  HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last], 0), "hipStreamWaitEvent(rest copy)");
+  return TKV_OK;
+}
+
+// The copies of a split decode call, issued after its selection and ensure
+// (which ran beside earlier copies: they touch no pool bytes and no kept
+// miss list).  W is the call's ensure width.  On `s`: the slices of this
+// layer and of the next one, for every miss; on `cs`: the rest of the rows.
+//
+// A call chains on the previous one when that was the ctx's last call, for
+// the layer before, and num_slots >= W_prev + 2*W: then no slot the previous
+// call filled is rebound by this call's ensure (at least num_slots - W_prev
+// - W slots outside both calls are older and the misses take at most W of
+// them).  Its slice copy then waits only for the rest copy of the call two
+// back (whose slots this call may rebind, and whose kept list it reuses).
+// Its attention reads this layer's slice of pages missed here (copied just
+// before), by the previous call (copied there as that call's next slice) or
+// earlier (rest copies two or more back: done).  Anything else waits for
+// every earlier copy.
+static int split_copies(tkv_ctx* c, int layer, const int32_t* miss, const int32_t* miss_count, int W,
+                        hipStream_t s, hipStream_t cs) {
+  const unsigned long long cap = capture_id(s);
+  const int L = c->cfg.num_layers;
+  const bool same = c->rest_pending && cap == c->rest_cap;
+  const bool chained = same && c->last_split && layer == (c->prev_layer + 1) % L &&
+                       (int64_t)c->cfg.num_slots >= (int64_t)c->prev_width + 2 * (int64_t)W;
+  if (!chained) {
+    if (same) HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last], 0), "hipStreamWaitEvent(rest copy)");
+    c->chain_len = 0;
+  } else if (c->chain_len >= 2) {
+    HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last ^ 1], 0), "hipStreamWaitEvent(rest copy, two back)");
+  }
+  const int k = c->chain_len & 1;
+  int32_t* keep = c->dev.bg_miss + (size_t)k * (1 + 2 * (size_t)c->cfg.max_width);
+  const int nxt = (layer + 1) % L;
+  HIPCHECK(launch_fetch_slice(c->dev, miss, miss_count, W, layer, nxt, keep, s), "decode slice fetch launch");
+  HIPCHECK(hipEventRecord(c->ev_slice, s), "hipEventRecord");
+  HIPCHECK(hipStreamWaitEvent(cs, c->ev_slice, 0), "hipStreamWaitEvent");
+  HIPCHECK(launch_fetch_rest(c->dev, keep, W, layer, nxt, cs), "rest-of-rows fetch launch");
+  HIPCHECK(hipEventRecord(c->ev_rest[k], cs), "hipEventRecord");
+  c->rest_last = k;
+  c->rest_pending = true;
+  c->rest_cap = cap;
+  c->chain_len += 1;
+  c->prev_layer = layer;
+  c->prev_width = W;
+  c->last_split = true;
+  return TKV_OK;
+}
+
+#define WAIT_REST(c, s)                                \
+  do {                                                 \
+    int rc_ = wait_rest((c), (hipStream_t)(s));        \
+    if (rc_) return rc_;                               \
+  } while (0)
+
 int tkv_reset_residency(tkv_ctx* c, void* stream) {
   int rc = need_attached(c);
   if (rc) return rc;
+  WAIT_REST(c, stream);
   HIPCHECK(launch_reset(c->dev, 0, (hipStream_t)stream), "reset residency");
   return TKV_OK;
 }
@@ -326,6 +414,7 @@ int tkv_select_pages(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   SelArgs a = make_sel(c, layer, q, rows, row_start, row_pos, block_table, max_pages, n_pages, B,
                        page_bias, topk, sel_local, needed);
   a.do_ensure = 0;
+  c->last_split = false;
   if (row_pos && B == 1 && rows >= 64) {
     // a chunk of query rows of one request: indexer scores as a matrix product
     HIPCHECK(launch_prefill_scores(c->dev, a, (hipStream_t)stream), "select_pages (prefill) launch");
@@ -343,6 +432,7 @@ int tkv_lru_ensure(tkv_ctx* c, const int32_t* needed, int32_t width, const uint8
     return fail(TKV_E_INVALID_ARG, "width=%d out of [1, max_width=%d]", width, c->cfg.max_width);
   if (!needed || !miss || !miss_count)
     return fail(TKV_E_INVALID_ARG, "needed, miss and miss_count must not be NULL");
+  c->last_split = false;   // an ensure between split calls voids their no-rebind argument
   HIPCHECK(launch_ensure(c->dev, needed, width, no_fetch, out_slots, miss, miss_count, (hipStream_t)stream),
            "lru_ensure launch");
   return TKV_OK;
@@ -352,7 +442,34 @@ int tkv_fetch_pages(tkv_ctx* c, const int32_t* miss, const int32_t* miss_count, 
   int rc = need_attached(c);
   if (rc) return rc;
   if (width < 1 || !miss || !miss_count) return fail(TKV_E_INVALID_ARG, "miss, miss_count or width invalid");
+  WAIT_REST(c, stream);
   HIPCHECK(launch_fetch(c->dev, miss, miss_count, width, (hipStream_t)stream), "fetch_pages launch");
+  return TKV_OK;
+}
+
+int tkv_fetch_pages_layer(tkv_ctx* c, const int32_t* miss, const int32_t* miss_count, int32_t width, int32_t layer,
+                          void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (width < 1 || width > c->cfg.max_width || !miss || !miss_count)
+    return fail(TKV_E_INVALID_ARG, "miss, miss_count or width (must be in [1, max_width=%d]) invalid",
+                c->cfg.max_width);
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
+  WAIT_REST(c, stream);
+  HIPCHECK(launch_fetch_slice(c->dev, miss, miss_count, width, layer, layer, c->dev.bg_miss, (hipStream_t)stream),
+           "fetch_pages_layer launch");
+  return TKV_OK;
+}
+
+int tkv_fetch_pages_rest(tkv_ctx* c, int32_t width, int32_t layer, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  if (width < 1 || width > c->cfg.max_width)
+    return fail(TKV_E_INVALID_ARG, "width=%d out of [1, max_width=%d]", width, c->cfg.max_width);
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
+  WAIT_REST(c, stream);
+  HIPCHECK(launch_fetch_rest(c->dev, c->dev.bg_miss, width, layer, layer, (hipStream_t)stream),
+           "fetch_pages_rest launch");
   return TKV_OK;
 }
 
@@ -371,6 +488,7 @@ static int attn_call(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
   a.ctx_len = ctx_len; a.sel = sel_local; a.bt = block_table; a.max_pages = max_pages; a.topk = topk;
   a.B = B; a.out = out; a.host_tail = host_tail;
+  WAIT_REST(c, stream);
   HIPCHECK(launch_attn(c->dev, a, (hipStream_t)stream), "sparse_paged_attn launch");
   return TKV_OK;
 }
@@ -396,7 +514,7 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
                              const int32_t* ctx_len, const float* page_bias, int32_t topk, int32_t* sel_local,
                              int32_t* needed, int32_t* out_slots, int32_t* miss, int32_t* miss_count,
                              uint16_t* out, const int32_t* pred, int32_t pred_width, void* stream,
-                             void* copy_stream) {
+                             void* copy_stream, bool split) {
   int rc = need_attached(c);
   if (rc) return rc;
   if ((rc = check_rows(c, layer, B, B, max_pages, topk))) return rc;
@@ -408,7 +526,13 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   hipStream_t s = (hipStream_t)stream;
   hipStream_t cs = (hipStream_t)copy_stream;
   const bool overlap = pred && cs && cs != s;
+  split = split && c->cfg.num_layers > 1;   // one layer: the slice is the row
+  if (split && !c->ev_slice) {
+    for (hipEvent_t* e : {&c->ev_slice, &c->ev_rest[0], &c->ev_rest[1]})
+      HIPCHECK(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreate");
+  }
   if (pred) {
+    WAIT_REST(c, s);
     if (pred_width < 1 || pred_width > c->cfg.max_width || pred_width > c->cfg.num_slots)
       return fail(TKV_E_INVALID_ARG, "pred_width=%d out of [1, min(max_width=%d, num_slots=%d)]", pred_width,
                   c->cfg.max_width, c->cfg.num_slots);
@@ -438,7 +562,14 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   // the layer's ensure may have rebound a slot the preload copy still writes:
   // its own fetch (and the attention) wait for that copy
   if (overlap) HIPCHECK(hipStreamWaitEvent(s, c->ev_copy, 0), "hipStreamWaitEvent");
-  HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
+  if (split) {
+    if ((rc = split_copies(c, layer, miss, miss_count, B * c->C, s, cs))) return rc;
+  } else {
+    // the selection and ensure ran beside a split call's copies (they touch
+    // no pool bytes and no kept miss list); the copy waits for them
+    WAIT_REST(c, s);
+    HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
+  }
   AttnArgs t{};
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
   t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
@@ -453,7 +584,16 @@ int tkv_decode_layer(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, co
                      const float* page_bias, int32_t topk, int32_t* sel_local, int32_t* needed,
                      int32_t* out_slots, int32_t* miss, int32_t* miss_count, uint16_t* out, void* stream) {
   return decode_layer_impl(c, layer, q, B, block_table, max_pages, n_pages, ctx_len, page_bias, topk, sel_local,
-                           needed, out_slots, miss, miss_count, out, nullptr, 0, stream, nullptr);
+                           needed, out_slots, miss, miss_count, out, nullptr, 0, stream, nullptr, false);
+}
+
+int tkv_decode_layer_split(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B, const int32_t* block_table,
+                           int32_t max_pages, const int32_t* n_pages, const int32_t* ctx_len,
+                           const float* page_bias, int32_t topk, int32_t* sel_local, int32_t* needed,
+                           int32_t* out_slots, int32_t* miss, int32_t* miss_count, uint16_t* out, void* stream,
+                           void* copy_stream) {
+  return decode_layer_impl(c, layer, q, B, block_table, max_pages, n_pages, ctx_len, page_bias, topk, sel_local,
+                           needed, out_slots, miss, miss_count, out, nullptr, 0, stream, copy_stream, true);
 }
 
 int tkv_decode_layer_prefetch(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t B,
@@ -464,7 +604,8 @@ int tkv_decode_layer_prefetch(tkv_ctx* c, int32_t layer, const uint16_t* q, int3
                               void* copy_stream) {
   if (!pred) return fail(TKV_E_INVALID_ARG, "pred is NULL");
   return decode_layer_impl(c, layer, q, B, block_table, max_pages, n_pages, ctx_len, page_bias, topk, sel_local,
-                           needed, out_slots, miss, miss_count, out, pred, pred_width, stream, copy_stream);
+                           needed, out_slots, miss, miss_count, out, pred, pred_width, stream, copy_stream,
+                           false);
 }
 
 int tkv_ensure_write_pages(tkv_ctx* c, int32_t n_runs, const int32_t* run_req, const int32_t* run_start,
@@ -480,6 +621,7 @@ int tkv_ensure_write_pages(tkv_ctx* c, int32_t n_runs, const int32_t* run_req, c
   if ((int64_t)n_runs * spr > c->cfg.max_width)
     return fail(TKV_E_CAPACITY, "n_runs*(max_run_len/page_size+1)=%lld samples > max_width=%d",
                 (long long)n_runs * spr, c->cfg.max_width);
+  WAIT_REST(c, stream);
   HIPCHECK(launch_write_ensure(c->dev, n_runs, run_req, run_start, run_len, spr, block_table, max_pages,
                                old_len, (hipStream_t)stream), "ensure_write_pages launch");
   return TKV_OK;
@@ -499,6 +641,7 @@ int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint
   StoreArgs a{};
   a.layer = layer; a.k = k; a.v = v; a.n_runs = n_runs; a.run_req = run_req; a.run_start = run_start;
   a.run_len = run_len; a.run_tok_off = run_tok_off; a.bt = block_table; a.max_pages = max_pages;
+  WAIT_REST(c, stream);
   HIPCHECK(launch_store(c->dev, a, max_run_len, (hipStream_t)stream), "store_kv_mirror launch");
   return TKV_OK;
 }
@@ -509,6 +652,7 @@ int tkv_read_counters(tkv_ctx* c, tkv_counters* out, void* stream) {
   if (!out) return fail(TKV_E_INVALID_ARG, "out is NULL");
   StateHdr h;
   hipStream_t s = (hipStream_t)stream;
+  WAIT_REST(c, s);
   HIPCHECK(hipMemcpyAsync(&h, c->dev.hdr, sizeof h, hipMemcpyDeviceToHost, s), "read counters");
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
   out->ensure_calls = h.counters[CNT_ENSURE];
@@ -530,6 +674,7 @@ int tkv_debug_read_state(tkv_ctx* c, int32_t* page_to_slot, int32_t* slot_to_pag
   int rc = need_attached(c);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
+  WAIT_REST(c, s);
   const DevCtx& d = c->dev;
   if (page_to_slot) HIPCHECK(hipMemcpyAsync(page_to_slot, d.page_to_slot, (size_t)d.N * 4, hipMemcpyDeviceToHost, s), "read page_to_slot");
   if (slot_to_page) HIPCHECK(hipMemcpyAsync(slot_to_page, d.slot_to_page, (size_t)d.S * 4, hipMemcpyDeviceToHost, s), "read slot_to_page");
@@ -618,6 +763,7 @@ int tkv_prefix_save(tkv_ctx* c, const int32_t* pages, int32_t n, void* records, 
   if (rc) return rc;
   if (!records) return fail(TKV_E_INVALID_ARG, "records is NULL");
   hipStream_t s = (hipStream_t)stream;
+  WAIT_REST(c, s);
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // stores to the mirror have landed
   const size_t rec = (size_t)tkv_prefix_record_bytes(c);
   prefix_copy_rows((uint8_t*)records, rec, c->mirror_host, c->row_bytes, c->row_bytes, pages, n, false);
@@ -629,6 +775,7 @@ int tkv_prefix_restore(tkv_ctx* c, const int32_t* pages, int32_t n, const void* 
   if (rc) return rc;
   if (!records) return fail(TKV_E_INVALID_ARG, "records is NULL");
   hipStream_t s = (hipStream_t)stream;
+  WAIT_REST(c, s);
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // no copy still reads these rows
   const size_t rec = (size_t)tkv_prefix_record_bytes(c);
   prefix_copy_rows(c->mirror_host, c->row_bytes, (const uint8_t*)records, rec, c->row_bytes, pages, n, true);

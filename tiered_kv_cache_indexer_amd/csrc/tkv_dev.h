@@ -65,9 +65,10 @@ struct DevCtx {
   int32_t* pmiss;           // [max_width][2] preload ensure: misses
   int32_t* pmiss_count;     // [1]
   float* attn_state;        // [max_rows][Hkv][ATTN_STATE_FLOATS] page-range attention records (or null)
+  int32_t* bg_miss;         // [2][1 + 2*max_width] miss count and list kept for the split copy's later parts
   int max_rows, max_pages, max_topk, max_batch, max_width;
-  int attn_impl;
-  int attn_range_pages;     // pages per range of the multi-pass prefill attention (0 = one pass)            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
+  int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
+  int attn_range_pages;     // pages per range of the multi-pass prefill attention (0 = one pass)
 };
 
 enum { ATTN_AUTO = 0, ATTN_VECTOR = 1, ATTN_MATRIX = 2 };

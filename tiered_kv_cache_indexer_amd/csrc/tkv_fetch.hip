@@ -13,6 +13,8 @@
 // Measured on MI355X over PCIe Gen5 x16: one vector in flight per thread with
 // 64 KiB items reads host memory at ~56 GB/s (the contiguous hipMemcpy rate),
 // four vectors per thread with 16 KiB items at ~49 GB/s.
+#include <utility>
+
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
@@ -49,6 +51,106 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch(DevCtx c, const int32_t* mi
 hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width,
                         hipStream_t st) {
   hipLaunchKernelGGL(k_fetch, dim3(FETCH_GRID), dim3(TKV_BLOCK), 0, st, c, miss, miss_count, width);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- split row copy ----
+// The same copy in parts, for decode steps whose link time should hide the
+// compute around it: one part moves, for every miss, one or two layers'
+// slices of the row (the layer being decoded, whose attention reads it, and
+// the next one); the other moves the rest of the rows, skipping those
+// slices.  The parts together move the bytes of k_fetch and leave the same
+// pool rows.
+
+// Slices `s0` and `s1` of every missed row (equal: one slice): a flat
+// grid-stride walk over the 16-byte vectors of all of them, so a few dozen
+// misses put every thread's load in flight.  With `keep` set, block 0 also
+// stores the miss count and list there ([0] = count, then the pairs) for the
+// part that follows.
+__global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32_t* miss, const int32_t* miss_count,
+                                                           int width, int s0, int s1, int32_t* keep) {
+  int m = *miss_count;
+  if (m > width) m = width;
+  if (keep && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < 2 * m; i += TKV_BLOCK) keep[1 + i] = miss[i];
+    if (threadIdx.x == 0) keep[0] = m;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && m > 0) c.hdr->counters[CNT_BYTES_FETCHED] += (int64_t)m * c.row_bytes;
+  // 32-bit indices: max_width < 2^16 and two layer slices are at most 2^15 vectors
+  const uint32_t nvl = (uint32_t)(c.layer_bytes / 16);
+  const uint32_t per = (s0 == s1 ? 1u : 2u) * nvl;
+  const uint32_t total = (uint32_t)m * per;
+  for (uint32_t v = blockIdx.x * TKV_BLOCK + threadIdx.x; v < total; v += gridDim.x * TKV_BLOCK) {
+    const int mi = (int)(v / per);
+    const uint32_t e = v - (uint32_t)mi * per;
+    const int64_t r = e < nvl ? (int64_t)s0 * nvl + e : (int64_t)s1 * nvl + (e - nvl);
+    const int slot = miss[2 * mi], page = miss[2 * mi + 1];
+    if (slot < 0 || slot >= c.S || page < 0 || (int64_t)page >= c.N) {
+      set_error(c.hdr, DERR_BAD_MISS);
+      continue;
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
+    dst[r] = __builtin_nontemporal_load(src + r);
+  }
+}
+
+// Every slice of the kept rows but slices `sa` <= `sb` (equal: one skipped).
+// (miss, 64 KiB item) work items as in k_fetch, on a small grid with eight
+// loads in flight per thread: the copy runs beside the decode's kernels, and
+// a grid spread over every CU holds enough host reads in flight to stall
+// their memory accesses (measured: attention 10 -> 200+ us), while 16
+// workgroups still keep the link busy.
+#define REST_GRID 16
+#define REST_UNROLL 8
+__global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_t* keep, int width, int sa, int sb) {
+  int m = keep[0];
+  if (m > width) m = width;
+  const int32_t* miss = keep + 1;
+  const int64_t nvl = c.layer_bytes / 16;
+  const int64_t a = (int64_t)sa * nvl, b = (int64_t)sb * nvl;
+  const int64_t nvec = c.row_bytes / 16 - (sa == sb ? 1 : 2) * nvl;
+  const int cpr = (int)((nvec + FETCH_CHUNK / 16 - 1) / (FETCH_CHUNK / 16));
+  const int64_t items = (int64_t)m * cpr;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int mi = (int)(it / cpr), ch = (int)(it - (int64_t)mi * cpr);
+    const int slot = miss[2 * mi], page = miss[2 * mi + 1];
+    if (slot < 0 || slot >= c.S || page < 0 || (int64_t)page >= c.N) {
+      if (threadIdx.x == 0) set_error(c.hdr, DERR_BAD_MISS);
+      continue;
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
+    const int64_t v_end = min(nvec, (int64_t)(ch + 1) * (FETCH_CHUNK / 16));
+    for (int64_t v0 = (int64_t)ch * (FETCH_CHUNK / 16) + threadIdx.x; v0 < v_end; v0 += TKV_BLOCK * REST_UNROLL) {
+      u32x4 t[REST_UNROLL];
+      int64_t r[REST_UNROLL];
+#pragma unroll
+      for (int u = 0; u < REST_UNROLL; ++u) {
+        // row vector of the u-th rest vector: step over slice sa, then sb
+        int64_t x = v0 + u * TKV_BLOCK;
+        if (x >= a) x += nvl;
+        if (sb != sa && x >= b) x += nvl;
+        r[u] = x;
+        if (v0 + u * TKV_BLOCK < v_end) t[u] = __builtin_nontemporal_load(src + x);
+      }
+#pragma unroll
+      for (int u = 0; u < REST_UNROLL; ++u)
+        if (v0 + u * TKV_BLOCK < v_end) dst[r[u]] = t[u];
+    }
+  }
+}
+
+hipError_t launch_fetch_slice(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width, int s0,
+                              int s1, int32_t* keep, hipStream_t st) {
+  hipLaunchKernelGGL(k_fetch_slice, dim3(FETCH_GRID), dim3(TKV_BLOCK), 0, st, c, miss, miss_count, width, s0, s1,
+                     keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_fetch_rest(const DevCtx& c, const int32_t* keep, int width, int sa, int sb, hipStream_t st) {
+  if (sa > sb) std::swap(sa, sb);
+  hipLaunchKernelGGL(k_fetch_rest, dim3(REST_GRID), dim3(TKV_BLOCK), 0, st, c, keep, width, sa, sb);
   return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@ hipError_t launch_ensure(const DevCtx& c, const int32_t* needed, int W, const ui
                          int32_t* out_slots, int32_t* miss, int32_t* miss_count, hipStream_t st);
 hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width,
                         hipStream_t st);
+hipError_t launch_fetch_slice(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width, int s0,
+                              int s1, int32_t* keep, hipStream_t st);
+hipError_t launch_fetch_rest(const DevCtx& c, const int32_t* keep, int width, int sa, int sb, hipStream_t st);
 hipError_t launch_write_ensure(const DevCtx& c, int n_runs, const int32_t* run_req,
                                const int32_t* run_start, const int32_t* run_len, int spr,
                                const int32_t* bt, int max_pages, const int32_t* old_len,

@@ -122,6 +122,15 @@ class TieredKV:
         check(self.lib.tkv_fetch_pages(self.ctx, _ptr(miss, torch.int32, "miss"),
                                        _ptr(miss_count, torch.int32, "miss_count"), width, _stream(stream)))
 
+    def fetch_pages_layer(self, miss, miss_count, layer, width=None, stream=None):
+        width = width or miss.shape[0]
+        check(self.lib.tkv_fetch_pages_layer(self.ctx, _ptr(miss, torch.int32, "miss"),
+                                             _ptr(miss_count, torch.int32, "miss_count"), width, layer,
+                                             _stream(stream)))
+
+    def fetch_pages_rest(self, width, layer, stream=None):
+        check(self.lib.tkv_fetch_pages_rest(self.ctx, width, layer, _stream(stream)))
+
     def sparse_paged_attn(self, layer, q, row_start, ctx_len, sel_local, block_table, out,
                           row_pos=None, stream=None, host_tail=False):
         fn = self.lib.tkv_sparse_paged_attn_host_tail if host_tail else self.lib.tkv_sparse_paged_attn
@@ -142,6 +151,19 @@ class TieredKV:
             _ptr(needed, torch.int32, "needed"), _ptr(out_slots, torch.int32, "out_slots"),
             _ptr(miss, torch.int32, "miss"), _ptr(miss_count, torch.int32, "miss_count"),
             _ptr(out, torch.bfloat16, "out"), _stream(stream)))
+
+    def decode_layer_split(self, layer, q, block_table, n_pages, ctx_len, topk, sel_local, needed, out_slots,
+                           miss, miss_count, out, copy_stream, page_bias=None, stream=None):
+        """decode_layer with the missed rows' other layers copied on copy_stream;
+        the caller waits for copy_stream before reading the pool itself."""
+        check(self.lib.tkv_decode_layer_split(
+            self.ctx, layer, _ptr(q, torch.bfloat16, "q"), q.shape[0],
+            _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+            _ptr(n_pages, torch.int32, "n_pages"), _ptr(ctx_len, torch.int32, "ctx_len"),
+            _ptr(page_bias, torch.float32, "page_bias"), topk, _ptr(sel_local, torch.int32, "sel_local"),
+            _ptr(needed, torch.int32, "needed"), _ptr(out_slots, torch.int32, "out_slots"),
+            _ptr(miss, torch.int32, "miss"), _ptr(miss_count, torch.int32, "miss_count"),
+            _ptr(out, torch.bfloat16, "out"), _stream(stream), _stream(copy_stream)))
 
     def decode_layer_prefetch(self, layer, q, block_table, n_pages, ctx_len, topk, sel_local, needed, out_slots,
                               miss, miss_count, out, pred, page_bias=None, stream=None, copy_stream=None):

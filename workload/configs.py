@@ -108,6 +108,11 @@ WORKLOADS.update({
                    num_layers=4, steps=8, setup_chunk=1024, topk=8),
     "c4s": replace(WORKLOADS["c4"], name="c4_small_mixed", contexts=(2048, 4096, 6432, 8192),
                    num_slots=160, num_layers=2, steps=5, setup_chunk=2048, topk=8),
+    # pools of 3x the batch width: a split decode call's copies chain on the previous call's
+    "c3sc": replace(WORKLOADS["c3"], name="c3_small_thrash_chain", contexts=(16384,), num_slots=72,
+                    num_layers=5, steps=8, setup_chunk=2048, topk=8, query="iid"),
+    "c4sc": replace(WORKLOADS["c4"], name="c4_small_mixed_chain", contexts=(2048, 4096, 6432, 8192),
+                    num_slots=288, num_layers=3, steps=5, setup_chunk=2048, topk=8, query="iid"),
     "c5s": replace(WORKLOADS["c5"], name="c5_small_prefill", contexts=(4096,), prefill_tokens=512,
                    num_slots=160, num_layers=2, setup_chunk=2048, topk=8),
 })

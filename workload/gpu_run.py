@@ -95,6 +95,21 @@ class GpuWorkload:
                                    self.miss[layer], self.miss_count[layer], self.out[layer],
                                    page_bias=self.bias, stream=stream)
 
+    def decode_step_split(self, s, copy_stream, q=None, stream=None, join=True):
+        """One decode step through decode_layer_split: each layer's missed rows
+        copy their other layers on `copy_stream`, beside that layer's attention
+        and the next layer's selection.  With `join`, `stream` waits for the
+        copy stream at the end of the step (pool complete in stream order)."""
+        wl = self.wl
+        q = self.q if q is None else q
+        for layer in range(wl.num_layers):
+            self.tier.decode_layer_split(layer, q[s, layer], self.bt, self.n_pages, self.ctx_len, wl.topk,
+                                         self.sel[layer], self.needed[layer], self.out_slots[layer],
+                                         self.miss[layer], self.miss_count[layer], self.out[layer],
+                                         copy_stream, page_bias=self.bias, stream=stream)
+        if join:
+            (stream or torch.cuda.current_stream()).wait_stream(copy_stream)
+
     def decode_step_prefetch(self, s, copy_stream, q=None, stream=None):
         """One decode step where layer l first preloads the page list layer
         l+1 needed last time (the next step's layer 0 for the last layer),
