@@ -4,15 +4,20 @@ Workload c3 (synthetic): 12 sparse-attention layers, batch 1, 32 query heads
 / 4 KV heads, head_dim 128, 64-token pages, context 196,608 tokens (3,072
 pages per layer), top-32 pages (2,048 tokens), fp8 e4m3 KV with per-token
 fp32 scales, a 256-slot GPU pool over a pinned host mirror, log-Zipf(1.1)
-page bias, AR(1) queries.  One step = decode_layer for all 12 layers
-(indexer + compact + LRU ensure, fused host->device fetch of the missed pages
-across all layers, sparse paged attention).
+page bias, AR(1) queries.  One step = one decode call for each of the 12
+layers (indexer + compact + LRU ensure, fused host->device copy of the missed
+pages across all layers, sparse paged attention).  When the warmup steps miss
+pages, the calls are decode_layer_split: each miss's slices of the decoded
+layer and the next one are copied on the decode stream, the rest of its row
+on a second stream, beside the attention and the next layer's selection;
+otherwise decode_layer (one stream).
 
 Timing: W untimed steps, then K steps bracketed by synchronize + HIP events
-on the stream the kernels run on.  A separate measurement pass then times
-the fetch and attention kernels one launch at a time with HIP events for the
-roofline figures.  The oracle (CPU) is timed on a bounded sample of the same
-workload as the cpu_baseline.
+on the decode stream (the copy stream joined before the closing event).
+Separate passes then time, with HIP events, every rest-of-rows copy on the
+copy stream (the roofline figure), and select+ensure, the whole-row copy and
+the attention one launch at a time.  The oracle (CPU) is timed on a bounded
+sample of the same workload as the cpu_baseline.
 """
 from __future__ import annotations
 
@@ -65,6 +70,25 @@ def pmc_traffic(summary, kernel, source):
                  * 1024)
 
 
+def split_traffic(misses_per_call):
+    """HBM-side bytes of one split copy (k_fetch_slice + k_fetch_rest) from the
+    committed PMC summary, scaled to `misses_per_call` misses, or None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "c3_pmc_traffic.json")
+    src = os.path.join(ROOT, "tiered_kv_cache_indexer_amd", "csrc", "tkv_fetch.hip")
+    try:
+        doc = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        parts = [doc["k_fetch_slice"], doc["k_fetch_rest"]]
+    except Exception:
+        return None
+    if any(p.get("source_sha256_16") != sha or not p.get("misses_per_launch") for p in parts):
+        return None
+    b = sum((p["fetch_KiB"] * doc["fetch_scale"] + p["write_KiB"] * doc["write_scale"]) * 1024
+            / p["misses_per_launch"] for p in parts)
+    return round(b * misses_per_call)
+
+
 def prefill_attn_traffic():
     return pmc_traffic("c5_pmc_traffic.json", "k_attn_mfma_rows", "tkv_attn_mfma.hip")
 
@@ -83,6 +107,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--graph", action="store_true", help="replay each decode step as a captured HIP graph")
+    ap.add_argument("--decode", choices=["auto", "split", "plain"], default="auto",
+                    help="split: decode_layer_split (each miss's other layers copied on a second stream); "
+                         "plain: decode_layer; auto: split when the warmup steps missed pages")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the preload, host-tail, prefix and append figures (profiling runs)")
     return ap.parse_args()
@@ -497,7 +524,7 @@ def main():
         torch.cuda.set_device(0)
         print(json.dumps(bench_prefill(args, torch)), flush=True)
         return
-    total = args.warmup + args.steps + args.measure_steps
+    total = args.warmup + args.steps + 2 * args.measure_steps
     wl = dataclasses.replace(base, steps=max(base.steps, total))
     torch.cuda.set_device(0)
     calib = calibrate(torch)
@@ -509,32 +536,97 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t0:.1f}s ({wl.name})")
     stream = torch.cuda.current_stream()
+    cw = g.tier.read_counters()
     for s in range(args.warmup):
         g.decode_step(s)
     torch.cuda.synchronize()
+    warm_misses = g.tier.read_counters()["misses"] - cw["misses"]
+    split = args.decode == "split" or (args.decode == "auto" and warm_misses > 0)
+    side = torch.cuda.Stream() if split else None
+    log(f"[bench] decode path: {'split' if split else 'plain'} ({warm_misses} misses in {args.warmup} warmup steps)")
     graphs = {}
     if args.graph:
         for s in range(args.warmup, args.warmup + args.steps):
             cg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(cg):
-                g.decode_step(s)
+                if split:
+                    g.decode_step_split(s, side)
+                else:
+                    g.decode_step(s)
             graphs[s] = cg
         torch.cuda.synchronize()
+    L = wl.num_layers
     c0 = g.tier.read_counters()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for s in range(args.warmup, args.warmup + args.steps):
+    for i, s in enumerate(range(args.warmup, args.warmup + args.steps)):
         if args.graph:
             graphs[s].replay()
+        elif split:
+            g.decode_step_split(s, side, join=False)
         else:
             g.decode_step(s)
+    if split:
+        stream.wait_stream(side)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     c1 = g.tier.read_counters()
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step")
-    k = measure_kernels(torch, g, args.warmup + args.steps, args.measure_steps)
+    s_next = args.warmup + args.steps
+    snap = {k_: getattr(g, k_).clone() for k_ in ("sel", "out_slots", "miss_count", "out")}
+    rest = None
+    if split:
+        # HIP events on the copy stream around each call's rest-of-rows copy, in
+        # steps of their own (markers between the copies add gaps to the timed
+        # steps).  The marker before a call runs when the copy stream reaches it,
+        # after the previous call's copy: the span is the copy plus any wait for
+        # its own slice copy.
+        ev = []
+        cr0 = g.tier.read_counters()
+        for s in range(s_next, s_next + args.measure_steps):
+            for layer in range(L):
+                ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ea.record(side)
+                g.tier.decode_layer_split(layer, g.q[s, layer], g.bt, g.n_pages, g.ctx_len, wl.topk, g.sel[layer],
+                                          g.needed[layer], g.out_slots[layer], g.miss[layer], g.miss_count[layer],
+                                          g.out[layer], side, page_bias=g.bias)
+                eb.record(side)
+                ev.append((ea, eb))
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        cr1 = g.tier.read_counters()
+        s_next += args.measure_steps
+        rest_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        rest_bytes = (cr1["bytes_fetched"] - cr0["bytes_fetched"]) * (L - 2) / L / len(ev)
+        rest = dict(us=rest_us, bytes=rest_bytes, GBps=rest_bytes / (rest_us * 1e-6) / 1e9, launches=len(ev))
+        log(f"[bench] rest copy {rest}")
+    plain = None
+    if split and not args.no_extras:
+        # the same steps from the same state through decode_layer, on a second tier
+        g2 = GpuWorkload(wl)
+        g2.setup()
+        g2.upload_queries()
+        for s in range(args.warmup):
+            g2.decode_step(s)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(args.warmup, args.warmup + args.steps):
+            g2.decode_step(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / args.steps
+        same = all(torch.equal(snap[k_], getattr(g2, k_)) for k_ in snap)
+        plain = {"ms_per_step": round(pms, 4), "steps_per_s": round(1e3 / pms, 2),
+                 "split_speedup": round(pms / ms, 4),
+                 "note": "decode_layer (one stream: select+ensure, whole-row copy, attention) over the same "
+                         "steps from the same state, on a second tier; last step's selections, slot maps, misses and "
+                         "attention outputs " + ("equal" if same else "DIFFER")}
+        log(f"[bench] plain decode {plain}")
+        del g2
+        torch.cuda.empty_cache()
+    k = measure_kernels(torch, g, s_next, args.measure_steps)
     log(f"[bench] kernels {k}")
     misses_step = (c1["misses"] - c0["misses"]) / args.steps
     link_bytes_step = (c1["bytes_fetched"] - c0["bytes_fetched"]) / args.steps
@@ -559,12 +651,38 @@ def main():
                    "budget_tokens": wl.topk * wl.page_size, "page_size": wl.page_size,
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "pool_slots": wl.num_slots, "kv_format": wl.kv_format},
-        "roofline": {"kernel": "k_fetch (fused host->device page copy)", "bound": "host_link",
-                     "achieved": round(k["fetch_GBps"], 2), "peak": LINK_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k["fetch_GBps"] / LINK_PEAK_GBPS, 4), "traffic": t_read,
-                     "traffic_hbm_write": t_write,
-                     "bytes_per_launch": round(k["fetch_bytes_per_launch"]),
-                     "avg_launch_us": round(k["fetch_us"], 2), "step_time_share": round(fetch_share, 3)},
+        "roofline": ({"kernel": "k_fetch_slice + k_fetch_rest (each call's missed rows: the decoded and next "
+                                "layers' slices on the decode stream, the rest on the copy stream; the two share the "
+                                "host link, so the figure is the link's over the timed steps)",
+                      "bound": "host_link",
+                      "achieved": round(link_bytes_step / (ms * 1e-3) / 1e9, 2), "peak": LINK_PEAK_GBPS,
+                      "unit": "GB/s", "frac": round(link_bytes_step / (ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4),
+                      "traffic": split_traffic(misses_step / wl.num_layers) if args.config == "c3" else None,
+                      "bytes_per_launch": round(link_bytes_step / wl.num_layers),
+                      "avg_launch_us": round(ms * 1e3 / wl.num_layers, 2),
+                      "launch": "one decode_layer_split call (a slice copy and a rest copy); avg = step time / layers"}
+                     if rest else
+                     {"kernel": "k_fetch (fused host->device page copy)", "bound": "host_link",
+                      "achieved": round(k["fetch_GBps"], 2), "peak": LINK_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(k["fetch_GBps"] / LINK_PEAK_GBPS, 4), "traffic": t_read,
+                      "traffic_hbm_write": t_write,
+                      "bytes_per_launch": round(k["fetch_bytes_per_launch"]),
+                      "avg_launch_us": round(k["fetch_us"], 2), "step_time_share": round(fetch_share, 3)}),
+        "rest_copy": ({"kernel": "k_fetch_rest", "achieved_GBps": round(rest["GBps"], 2),
+                       "bytes_per_launch": round(rest["bytes"]), "avg_launch_us": round(rest["us"], 2),
+                       "launches": rest["launches"],
+                       "traffic": pmc_traffic("c3_pmc_traffic.json", "k_fetch_rest", "tkv_fetch.hip")
+                       if args.config == "c3" else None,
+                       "note": "HIP events on the copy stream around each call, in steps of their own: there "
+                               "the copies do not overlap the next call's slice copy, as they do in the timed "
+                               "steps"} if rest else None),
+        "whole_row_copy": {"kernel": "k_fetch (decode_layer's one-launch copy, timed one launch at a time)",
+                           "achieved_GBps": round(k["fetch_GBps"], 2),
+                           "bytes_per_launch": round(k["fetch_bytes_per_launch"]),
+                           "avg_launch_us": round(k["fetch_us"], 2), "traffic": t_read,
+                           "traffic_hbm_write": t_write},
+        "decode_path": "split" if split else "plain",
+        "plain_decode": plain,
         "roofline_hbm": {"kernel": "k_attn_mfma_split (sparse paged attention, split pages + merge)",
                          "bound": "hbm",
                          "achieved": round(k["attn_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -578,7 +696,9 @@ def main():
                  "bytes_per_step": round(link_bytes_step),
                  "step_GBps": round(link_bytes_step / (ms * 1e-3) / 1e9, 2)},
         "calibration": calib,
-        "launch": "hip graph per step" if args.graph else "eager, one C call per layer",
+        "launch": ("hip graph per step" if args.graph else "eager, one C call per layer")
+                  + (" (decode_layer_split: copy stream joined once, after the timed steps; rest-copy "
+                     "events in %d steps of their own)" % args.measure_steps if split else ""),
         "error_word": err,
     }
     if args.no_extras:
