@@ -1,0 +1,182 @@
+"""GPU parity on the edges of the decode path, against the oracle.
+
+* contexts shorter than the top-k (a one-token request, contexts ending
+  mid-page): selections padded with -1, masked tails;
+* top-k above 64 pages (the block top-k and unsplit attention paths);
+* bf16 KV with 16-token pages and a ragged batch of three;
+* a compaction width below the top-k (FreeToken PR #499, "Design": pages
+  past the cap are counted as drops, not silently lost);
+* the device error word (FreeToken PR #499, "Design": fixed-shape calls
+  report anomalies instead of faulting): an ensure needing more distinct
+  pages than slots changes nothing; page ids out of range are skipped;
+  fetch entries outside the pool or the page space are skipped; a store to a
+  page with no slot writes the mirror and the slab only.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import run
+from oracle.lru import ERR_CAPACITY, ERR_PAGE_RANGE, LRUState
+from workload import gen, get_workload
+
+from tests.gpu_compare import compare_layer, compare_state, say
+
+pytestmark = pytest.mark.gpu
+
+TKV_ERR_PAGE_RANGE, TKV_ERR_CAPACITY, TKV_ERR_NOT_RESIDENT, TKV_ERR_BAD_MISS = 1, 2, 4, 8
+
+EDGE = {
+    "short": replace(get_workload("c4s"), name="edge_short_contexts", contexts=(1, 100, 130, 1000),
+                     num_slots=128, num_layers=2, steps=4, topk=8, query="iid", setup_chunk=1024),
+    "wide": replace(get_workload("c2s"), name="edge_topk_128", contexts=(16384,), topk=128, num_slots=512,
+                    num_layers=2, steps=3, query="iid", setup_chunk=4096),
+    "bf16": replace(get_workload("c1"), name="edge_bf16_batch", contexts=(700, 4096, 33), num_slots=160,
+                    steps=4),
+}
+
+
+def _pair(wl):
+    from workload.gpu_run import GpuWorkload
+    g = GpuWorkload(wl)
+    g.setup()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    return g, o
+
+
+def _chain(wl, g, o, C=None):
+    g.upload_queries()
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, C or 0)
+    for s in range(wl.steps):
+        say(f"[edges] {wl.name} step {s}")
+        g.decode_step(s)
+        torch.cuda.synchronize()
+        for layer in range(wl.num_layers):
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+            compare_layer(g, rec, layer, f"{wl.name} step {s} layer {layer}")
+        compare_state(g, o, f"{wl.name} step {s}", check_rows=(s == wl.steps - 1))
+
+
+@pytest.mark.parametrize("key", sorted(EDGE))
+def test_decode_edges_bit_exact(key):
+    wl = EDGE[key]
+    say(f"[edges] {key}: {wl.name}")
+    g, o = _pair(wl)
+    compare_state(g, o, f"{wl.name} after setup")
+    _chain(wl, g, o)
+    if key == "short":
+        sel = g.sel.cpu().numpy()
+        assert (sel[:, 0, 1:] == -1).all(), "the one-page request pads its selection with -1"
+    assert g.tier.read_counters()["error_word"] == 0
+
+
+def test_decode_drops_when_the_cap_is_below_topk():
+    wl = replace(get_workload("c3s"), name="edge_cap_5", num_layers=2, steps=3, query="iid")
+    say("[edges] compaction width 5 < top-8")
+    g, o = _pair(wl)
+    C = 5
+    B, L = wl.batch, wl.num_layers
+    g.C = g.tier.set_select_width(B, wl.topk, C)
+    g.needed = torch.full((L, B, C), -1, dtype=torch.int32, device="cuda")
+    g.out_slots = torch.full((L, B * C), -1, dtype=torch.int32, device="cuda")
+    g.miss = torch.zeros((L, B * C, 2), dtype=torch.int32, device="cuda")
+    _chain(wl, g, o, C=C)
+    c = g.tier.read_counters()
+    assert c["drops"] == (wl.topk - C) * B * L * wl.steps, c["drops"]
+
+
+def _small_tier(num_slots, max_width, layers=2):
+    from tiered_kv_cache_indexer_amd import TieredKV
+    return TieredKV(num_layers=layers, num_q_heads=32, num_kv_heads=4, head_dim=128, page_size=64,
+                    kv_format="fp8", num_logical_pages=64, num_slots=num_slots, max_batch=1,
+                    max_topk=8, max_pages_per_req=64, max_width=max_width)
+
+
+def _ensure_both(t, lru, needed):
+    W = len(needed)
+    nd = torch.tensor(needed, dtype=torch.int32, device="cuda")
+    out = torch.full((W,), -7, dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W, 2), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t.lru_ensure(nd, out, miss, cnt)
+    torch.cuda.synchronize()
+    o_out, o_miss = lru.ensure(np.array(needed, dtype=np.int64))
+    m = int(cnt.item())
+    assert np.array_equal(out.cpu().numpy(), o_out), "out_slots"
+    assert m == len(o_miss) and np.array_equal(miss[:m].cpu().numpy(), np.asarray(o_miss).reshape(-1, 2)), "misses"
+    st = t.read_state()
+    assert np.array_equal(st["page_to_slot"], lru.page_to_slot)
+    assert np.array_equal(st["slot_to_page"], lru.slot_to_page)
+    assert np.array_equal(st["stamp"], lru.stamp) and st["clock"] == lru.clock
+
+
+def test_ensure_capacity_and_page_range_errors_match_oracle():
+    say("[edges] ensure error words")
+    S, N = 6, 64
+    t = _small_tier(S, 16)
+    lru = LRUState(N, S)
+    _ensure_both(t, lru, [3, 4, 5])
+    # seven distinct pages for six slots: nothing changes, every slot -1, error bit
+    _ensure_both(t, lru, [10, 11, 12, 13, 14, 15, 16, 10])
+    assert t.read_counters()["error_word"] == TKV_ERR_CAPACITY and lru.error_word == ERR_CAPACITY
+    # ids out of range are skipped and flagged; the rest is served
+    _ensure_both(t, lru, [4, N, -5, 20, -1, 21, 4])
+    assert t.read_counters()["error_word"] == TKV_ERR_CAPACITY | TKV_ERR_PAGE_RANGE
+    assert lru.error_word == ERR_CAPACITY | ERR_PAGE_RANGE
+    _ensure_both(t, lru, [30, 31, 3, 20])
+
+
+def test_fetch_skips_entries_outside_the_pool_or_page_space():
+    say("[edges] fetch with bad miss entries")
+    S, N = 6, 64
+    t = _small_tier(S, 16)
+    rb = t.row_bytes
+    # give every mirror row distinct bytes through the write path's layout-free
+    # view: the mirror is the library's pinned memory, written here directly
+    import ctypes
+    ptr = t.lib.tkv_mirror_host_ptr(t.ctx)
+    mir = np.ctypeslib.as_array((ctypes.c_uint8 * (N * rb)).from_address(ptr)).reshape(N, rb)
+    rng = np.random.default_rng(5)
+    mir[:] = rng.integers(0, 256, size=mir.shape, dtype=np.uint8)
+    before = t.pool_rows().clone()
+    miss = torch.tensor([[2, 9], [S, 1], [1, N], [-1, 3], [4, 17]], dtype=torch.int32, device="cuda")
+    cnt = torch.tensor([5], dtype=torch.int32, device="cuda")
+    t.fetch_pages(miss, cnt)
+    torch.cuda.synchronize()
+    pool = t.pool_rows().cpu().numpy()
+    assert np.array_equal(pool[2], mir[9]) and np.array_equal(pool[4], mir[17])
+    for s in (0, 1, 3, 5):
+        assert np.array_equal(pool[s], before[s].cpu().numpy()), f"slot {s} was written"
+    assert t.read_counters()["error_word"] == TKV_ERR_BAD_MISS
+
+
+def test_store_to_a_page_without_slot():
+    """A full-page store to a page that is not resident: mirror row and slab
+    take the new bytes (as the oracle's store does), the pool does not, and
+    the error word says so."""
+    from workload.gpu_run import GpuWorkload
+    wl = replace(get_workload("c3s"), name="edge_store_nonresident", num_layers=2, steps=1)
+    say("[edges] store to a page without a slot")
+    g, o = _pair(wl)
+    bt, _ = gen.block_tables(wl)
+    st = g.tier.read_state()
+    page0 = int(bt[0][0])
+    assert st["page_to_slot"][page0] < 0 and o.lru.page_to_slot[page0] < 0
+    layer, n = 1, wl.page_size
+    k = gen.kv_tokens(wl, gen.KIND_K, 0, 0, 64 * wl.page_size, n)     # other on-grid values
+    v = gen.kv_tokens(wl, gen.KIND_V, 0, 0, 70 * wl.page_size, n)
+    kt = torch.from_numpy(gen.to_bf16_bits(k).view(np.int16)).cuda().view(torch.bfloat16)
+    vt = torch.from_numpy(gen.to_bf16_bits(v).view(np.int16)).cuda().view(torch.bfloat16)
+    one = lambda x: torch.tensor([x], dtype=torch.int32, device="cuda")
+    g.tier.store_kv_mirror(layer, kt, vt, one(0), one(0), one(n), one(0), n, g.bt)
+    o.store(layer, [(0, 0, n)], k, v, bt)
+    compare_state(g, o, "after the store", check_rows=True)
+    assert g.tier.read_counters()["error_word"] == TKV_ERR_NOT_RESIDENT
