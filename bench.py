@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+ATTN_MFMA_PEAK = 3333.3  # TFLOP/s: fp8 Q.K^T (5.0 PFLOP/s) and bf16 P.V (2.5) in equal parts
 LINK_PEAK_GBPS = 63.0   # PCIe Gen5 x16: 32 GT/s * 16 lanes * 128/130 / 8, per direction
 
 
@@ -486,16 +487,20 @@ def bench_prefill(args, torch):
                    "topk_pages": wl.topk, "pool_slots": wl.num_slots},
         "split_ms": {k: round(v, 3) for k, v in ms.items()},
         "roofline": {"kernel": "k_attn_mfma_rows (causal sparse attention, one wave per row and KV head)",
-                     "bound": "hbm",
-                     "achieved": round(attn_bytes_layer * L / (ms["attn"] * 1e-3) / 1e9, 1),
-                     "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(attn_bytes_layer * L / (ms["attn"] * 1e-3) / 1e9 / 8000.0, 4),
+                     "bound": "mfma",
+                     "achieved": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12, 2),
+                     "peak": ATTN_MFMA_PEAK, "unit": "TFLOP/s",
+                     "frac": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12 / ATTN_MFMA_PEAK, 4),
                      "traffic": attn_traffic,
-                     "bytes_per_launch": attn_bytes_layer,
                      "flop_per_launch": attn_flop_layer,
-                     "TFLOPs": round(attn_flop_layer * L / (ms["attn"] * 1e-3) / 1e12, 2),
-                     "note": "bytes = K+V codes and scales of every (row, KV head, selected page) read; "
-                             "most are served by the Infinity Cache, so HBM 8 TB/s is the reference peak"},
+                     "peak_note": "half the flops are S = Q.K^T on fp8 (5.0 PFLOP/s), half P.V on bf16 "
+                                  "(2.5 PFLOP/s): 3.33 PFLOP/s for the mix",
+                     "cache_bytes_per_launch": attn_bytes_layer,
+                     "cache_GBps": round(attn_bytes_layer * L / (ms["attn"] * 1e-3) / 1e9, 1),
+                     "note": "the kernel reads K+V codes and scales of every (row, KV head, selected page): "
+                             "cache_bytes per launch, 123x the layer's unique KV; most come from the L2s and "
+                             "the Infinity Cache (traffic: what passed the L2s), and one page in flight per "
+                             "wave leaves it bound by that path's latency, not by the matrix cores"},
         "roofline_mfma": {"kernel": "k_prefill_scores (+ per-row top-k, compaction)", "bound": "mfma",
                           "achieved": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12, 2),
                           "peak": 2500.0, "unit": "TFLOP/s",
