@@ -663,6 +663,9 @@ def main():
                       "achieved": round(link_bytes_step / (ms * 1e-3) / 1e9, 2), "peak": LINK_PEAK_GBPS,
                       "unit": "GB/s", "frac": round(link_bytes_step / (ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4),
                       "traffic": split_traffic(misses_step / wl.num_layers) if args.config == "c3" else None,
+                      "traffic_note": "FETCH_SIZE (the host reads, which pass the L2s) + WRITE_SIZE (the HBM "
+                                      "writes): every copied byte counts twice, so 2 x bytes_per_launch is the "
+                                      "floor",
                       "bytes_per_launch": round(link_bytes_step / wl.num_layers),
                       "avg_launch_us": round(ms * 1e3 / wl.num_layers, 2),
                       "launch": "one decode_layer_split call (a slice copy and a rest copy); avg = step time / layers"}
