@@ -19,9 +19,12 @@
  *    allocates device memory).  The pinned host mirror is owned by the ctx.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    calls except tkv_create/tkv_attach_device/tkv_read_counters/
- *    tkv_debug_read_state are asynchronous, launch a fixed number of kernels
- *    whose shapes depend only on the arguments' sizes, never synchronise and
- *    never allocate, so they can be captured in a HIP graph.
+ *    tkv_debug_read_state and the cold-prefix calls (tkv_prefix_save/
+ *    tkv_prefix_restore: host-side copies, a staging buffer) are
+ *    asynchronous, launch a fixed number of kernels whose shapes depend only
+ *    on the arguments' sizes, never synchronise and never allocate, so they
+ *    can be captured in a HIP graph (tkv_decode_layer_split: see its
+ *    ordering notes).
  *  - Return value: TKV_OK (0) or a negative TKV_E_* code; tkv_last_error()
  *    returns a thread-local message naming the offending argument or knob.
  *  - Anomalies found on the device (page id out of range, a selection that
@@ -29,7 +32,9 @@
  *    sticky error word returned by tkv_read_counters.  Pages cut by the
  *    selection cap are not errors: they are counted in `drops`.
  *  - One ctx is used from one stream at a time; calls on one ctx that
- *    overlap on different streams race.
+ *    overlap on different streams race.  (tkv_decode_layer_split and
+ *    tkv_decode_layer_prefetch also use the `copy_stream` they are given,
+ *    ordered by events the ctx owns.)
  *
  * Page row layout (identical in a pool slot and a mirror row; one row holds
  * one logical page for ALL layers): for layer l at l*layer_bytes,
