@@ -185,8 +185,22 @@ __device__ __forceinline__ uint64_t sel_key(float score, int idx) {
 }
 __device__ __forceinline__ int sel_key_index(uint64_t k) { return (int)(~(uint32_t)k); }
 
+// The value of lane (lane ^ m) for the constant distances of the wave sort
+// networks (m folds to a constant once the networks are unrolled): DPP moves
+// for 1, 2 (quad permutes) and 8 (row rotate by 8), a ds_swizzle in bit-mask
+// mode for 4 and 16 (within 32 lanes), a lane permute for 32.
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int m) {
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    default: return (uint32_t)__shfl_xor((int)v, m, 64);
+  }
+}
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  const uint32_t lo = xor_lane_u32((uint32_t)v, m), hi = xor_lane_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
@@ -232,7 +246,7 @@ __device__ __forceinline__ int wave_sort_asc_i32(int v) {
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int o = __shfl_xor(v, stride, 64);
+      const int o = (int)xor_lane_u32((uint32_t)v, stride);
       const bool lower = (lane & stride) == 0;
       const bool asc = (lane & size) == 0;
       const bool keep_min = (lower == asc);
