@@ -87,7 +87,7 @@ typedef struct tkv_config {
   int32_t page_size;        /* 16 or 64 tokens */
   int32_t kv_format;        /* TKV_KV_* */
   int64_t num_logical_pages;/* mirror rows (cf. --kv-host-pages + --num-pages) */
-  int32_t num_slots;        /* GPU pool slots (cf. --num-pages) */
+  int32_t num_slots;        /* GPU pool slots (cf. --num-pages), 1 .. 524288 */
   int32_t max_batch;        /* requests per call */
   int32_t max_rows;         /* query rows per call (decode: requests; prefill: chunk tokens) */
   int32_t max_topk;         /* pages selected per row */

@@ -63,7 +63,7 @@ struct Layout {
   size_t row, layer, code;
   size_t pool, slab, mirror;
   // state offsets
-  size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_touched, st_acc, st_total;
+  size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
       ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_attn_state, ws_total;
@@ -89,7 +89,9 @@ static int validate(const tkv_config* c) {
     return fail(TKV_E_INVALID_ARG, "page_size=%d: 16 or 64 tokens are supported", c->page_size);
   if (c->num_logical_pages < 1 || c->num_logical_pages > 0x7FFFFFFF)
     return fail(TKV_E_INVALID_ARG, "num_logical_pages=%lld out of range", (long long)c->num_logical_pages);
-  if (c->num_slots < 1) return fail(TKV_E_INVALID_ARG, "num_slots=%d must be >= 1", c->num_slots);
+  if (c->num_slots < 1 || c->num_slots > (1 << 19))
+    return fail(TKV_E_INVALID_ARG, "num_slots=%d out of [1, 524288] (the ensure keeps one LDS bit per slot)",
+                c->num_slots);
   if (c->max_batch < 1 || c->max_rows < c->max_batch)
     return fail(TKV_E_INVALID_ARG, "max_batch=%d, max_rows=%d: need 1 <= max_batch <= max_rows",
                 c->max_batch, c->max_rows);
@@ -120,7 +122,6 @@ static Layout make_layout(const tkv_config* c) {
   L.st_s2p = o; o = align256(o + S * 4);
   L.st_stamp = o; o = align256(o + S * 8);
   L.st_order = o; o = align256(o + 2 * S * 4);
-  L.st_touched = o; o = align256(o + S * 4);
   L.st_acc = o; o = align256(o + NL * N * H * D * 4);
   L.st_total = o;
   const size_t W = c->max_width, R = c->max_rows, P = c->max_pages_per_req;
@@ -243,7 +244,6 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.slot_to_page = (int32_t*)(st + L.st_s2p);
   d.stamp = (int64_t*)(st + L.st_stamp);
   d.order = (int32_t*)(st + L.st_order);
-  d.touched = (int32_t*)(st + L.st_touched);
   d.slab_acc = (float*)(st + L.st_acc);
   uint8_t* ws = (uint8_t*)b->workspace;
   d.scores = (float*)(ws + L.ws_scores);

@@ -42,7 +42,6 @@ struct DevCtx {
   int32_t* slot_to_page;    // [S]
   int64_t* stamp;           // [S]
   int32_t* order;           // [2][S] slots in ascending (stamp, slot)
-  int32_t* touched;         // [S]
   // workspace
   float* scores;            // [max_rows][max_pages rounded to 64] x 8 bytes: float scores or 64-bit keys
   int32_t* sel_slots;       // [max_rows][max_topk] slots of the selected pages (fused decode)

@@ -246,7 +246,6 @@ hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st) {
   if ((e = fill_i32(c.page_mark, c.N, 0x7FFFFFFF, st)) != hipSuccess) return e;
   if ((e = fill_i32(c.slot_to_page, c.S, -1, st)) != hipSuccess) return e;
   if ((e = launch_fill_bytes(c.stamp, (int64_t)c.S * 8, 0, st)) != hipSuccess) return e;
-  if ((e = fill_i32(c.touched, c.S, 0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_iota_i32, dim3((c.S + 255) / 256), dim3(256), 0, st, c.order, (int64_t)c.S);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_reset_hdr, dim3(1), dim3(64), 0, st, c.hdr);

@@ -27,10 +27,16 @@ struct EnsureOut {
 
 __device__ __forceinline__ bool page_ok(const DevCtx& c, int p) { return p >= 0 && (int64_t)p < c.N; }
 
+// `tb`: LDS bitset of the slots touched by this call (hit or bound), at
+// least (S + 31) / 32 words; it lives only for the call.
+__device__ __forceinline__ bool slot_touched(const uint32_t* tb, int s) { return (tb[s >> 5] >> (s & 31)) & 1u; }
+__device__ __forceinline__ void touch_slot(uint32_t* tb, int s) { atomicOr(&tb[s >> 5], 1u << (s & 31)); }
+
 __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
-                                 const uint8_t* no_fetch, EnsureOut o, int* sm_scan) {
+                                 const uint8_t* no_fetch, EnsureOut o, int* sm_scan, uint32_t* tb) {
   const int tid = threadIdx.x;
   const int32_t INTMAX = 0x7FFFFFFF;
+  for (int w = tid; w < (c.S + 31) >> 5; w += TKV_BLOCK) tb[w] = 0u;
 
   // A: first occurrence of every valid page id (atomicMin of the index)
   int bad = 0;
@@ -77,7 +83,7 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
       if (page_ok(c, p) && ld_acquire_i32(&c.page_mark[p]) == j) {
         int s = c.page_to_slot[p];
         if (s >= 0) {
-          c.touched[s] = 1;
+          touch_slot(tb, s);
           c.stamp[s] = clock_new;
           c.slot_of_j[j] = s;
           ++n_hits;
@@ -110,7 +116,7 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
       int cnt = 0;
 #pragma unroll
       for (int u = 0; u < LRU_CH; ++u) {
-        cand[u] = (u < ch && i0 + u < c.S) && !c.touched[sl[u]];
+        cand[u] = (u < ch && i0 + u < c.S) && !slot_touched(tb, sl[u]);
         cnt += cand[u];
       }
       int tot;
@@ -140,7 +146,7 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
     c.page_to_slot[p] = s;
     c.slot_to_page[s] = p;
     c.stamp[s] = clock_new;
-    c.touched[s] = 1;
+    touch_slot(tb, s);
     c.slot_of_j[j] = s;
   }
   __syncthreads();
@@ -191,7 +197,7 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
       int cnt = 0;
 #pragma unroll
       for (int u = 0; u < LRU_CH; ++u) {
-        keep[u] = (u < ch && i0 + u < c.S) && !c.touched[sl[u]];
+        keep[u] = (u < ch && i0 + u < c.S) && !slot_touched(tb, sl[u]);
         cnt += keep[u];
       }
       int tot;
@@ -208,17 +214,14 @@ __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
       int cnt = 0;
 #pragma unroll
       for (int u = 0; u < LRU_CH; ++u) {
-        t[u] = (u < ch && s0 + u < c.S) ? c.touched[s0 + u] : 0;
+        t[u] = (u < ch && s0 + u < c.S) ? (int)slot_touched(tb, s0 + u) : 0;
         cnt += t[u];
       }
       int tot;
       int r = run + block_excl_scan(cnt, &tot, sm_scan);
 #pragma unroll
       for (int u = 0; u < LRU_CH; ++u)
-        if (t[u]) {
-          nxt[r++] = s0 + u;
-          c.touched[s0 + u] = 0;
-        }
+        if (t[u]) nxt[r++] = s0 + u;
       run += tot;
     }
   }

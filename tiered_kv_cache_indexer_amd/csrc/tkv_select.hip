@@ -263,7 +263,7 @@ __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, 
   }
   if (a.do_ensure) {
     EnsureOut o{a.out_slots, a.miss, a.miss_count};
-    lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan);
+    lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan, dyn);   // dyn is free after the compaction
     __syncthreads();
     if (a.sel_slots) write_sel_slots(c, a);
   }
@@ -559,17 +559,21 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_finish(DevCtx c, SelArgs a
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* needed, int W,
                                                       const uint8_t* no_fetch, EnsureOut o) {
+  extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ int sm_scan[8];
-  lru_ensure_block(c, needed, W, no_fetch, o, sm_scan);
+  lru_ensure_block(c, needed, W, no_fetch, o, sm_scan, dyn);
 }
 
 // ------------------------------------------------------------------ launchers --
+static size_t ensure_dyn_lds(const DevCtx& c) { return (size_t)((c.S + 31) / 32) * 4; }
+
 size_t select_dyn_lds(const DevCtx& c) {
   size_t keys = (size_t)c.max_pages * 4;
   size_t bm = (size_t)((c.max_pages + 31) / 32) * 4;
   size_t lists = 4 * 64 * 8;
   size_t m = keys > bm ? keys : bm;
-  return m > lists ? m : lists;
+  m = m > lists ? m : lists;
+  return m > ensure_dyn_lds(c) ? m : ensure_dyn_lds(c);
 }
 
 hipError_t launch_select_scan(const DevCtx& c, const SelArgs& a, hipStream_t st) {
@@ -599,6 +603,6 @@ hipError_t launch_select_rows(const DevCtx& c, const SelArgs& a, hipStream_t st)
 hipError_t launch_ensure(const DevCtx& c, const int32_t* needed, int W, const uint8_t* no_fetch,
                          int32_t* out_slots, int32_t* miss, int32_t* miss_count, hipStream_t st) {
   EnsureOut o{out_slots, miss, miss_count};
-  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(TKV_BLOCK), 0, st, c, needed, W, no_fetch, o);
+  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(TKV_BLOCK), ensure_dyn_lds(c), st, c, needed, W, no_fetch, o);
   return hipGetLastError();
 }
