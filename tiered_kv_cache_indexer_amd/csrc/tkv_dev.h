@@ -256,26 +256,29 @@ __device__ __forceinline__ int wave_sort_asc_i32(int v) {
 }
 
 // ------------------------------------------------------------------ block ops --
+// Inclusive prefix sum across the wave by DPP: row shifts right by 1, 2, 4
+// and 8 (a lane whose source lies outside its 16-lane row adds 0), then lane
+// 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
+// Sum / max over the wave, every lane gets the result (xor butterflies).
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 32; o > 0; o >>= 1) v += __uint_as_float(xor_lane_u32(__float_as_uint(v), o));
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __uint_as_float(xor_lane_u32(__float_as_uint(v), o)));
   return v;
 }
 

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
       }
     }
 #pragma unroll
-    for (int o = LANES / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    for (int o = LANES / 2; o > 0; o >>= 1) part += __uint_as_float(xor_lane_u32(__float_as_uint(part), o));
     const int lg = logical[it];
     float key = part;
     if (lg < 0) key = -INFINITY;
