@@ -63,10 +63,15 @@ hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* mis
 // pool rows.
 
 // Slices `s0` and `s1` of every missed row (equal: one slice): a flat
-// grid-stride walk over the 16-byte vectors of all of them, so a few dozen
-// misses put every thread's load in flight.  With `keep` set, block 0 also
-// stores the miss count and list there ([0] = count, then the pairs) for the
-// part that follows.
+// grid-stride walk over the 16-byte vectors of all of them on SLICE_GRID
+// workgroups.  With `keep` set, block 0 also stores the miss count and list
+// there ([0] = count, then the pairs) for the part that follows.  The grid
+// is a quarter of k_fetch's: this copy shares the link with the previous
+// call's rest copy, and with 1,024 workgroups (every vector of a few dozen
+// misses in flight at once) the two together moved 52.3 GB/s on MI355X; with
+// 64-384 workgroups 53.7-54.4 GB/s (+3.5% decode steps at 196k context, with
+// 16 or 12 rest workgroups alike); more loads per thread gained nothing.
+#define SLICE_GRID 256
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32_t* miss, const int32_t* miss_count,
                                                            int width, int s0, int s1, int32_t* keep) {
   int m = *miss_count;
@@ -100,7 +105,9 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 // loads in flight per thread: the copy runs beside the decode's kernels, and
 // a grid spread over every CU holds enough host reads in flight to stall
 // their memory accesses (measured: attention 10 -> 200+ us), while 16
-// workgroups still keep the link busy.
+// workgroups still keep the link busy.  Timed call by call on MI355X: 8-16
+// workgroups with 4-12 loads per thread move 51-53 GB/s, 32 workgroups 48,
+// 48-64 workgroups 43: more host reads in flight slow the link down.
 #define REST_GRID 16
 #define REST_UNROLL 8
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_t* keep, int width, int sa, int sb) {
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
 
 hipError_t launch_fetch_slice(const DevCtx& c, const int32_t* miss, const int32_t* miss_count, int width, int s0,
                               int s1, int32_t* keep, hipStream_t st) {
-  hipLaunchKernelGGL(k_fetch_slice, dim3(FETCH_GRID), dim3(TKV_BLOCK), 0, st, c, miss, miss_count, width, s0, s1,
+  hipLaunchKernelGGL(k_fetch_slice, dim3(SLICE_GRID), dim3(TKV_BLOCK), 0, st, c, miss, miss_count, width, s0, s1,
                      keep);
   return hipGetLastError();
 }
