@@ -107,8 +107,12 @@ __device__ void row_topk_block(const float* scores, int visible, int k, int32_t*
 }
 
 // Row top-k for k <= 64 (wave bitonic): each wave folds a share of the
-// row's sorted 64-key lists into its running top-64 list, the four wave lists
-// are merged through LDS, and wave 0 writes the first k indices ascending.
+// row's sorted 64-key lists into its running top-64 list (a merge per list
+// that exists: 16 lists take 3 merges per wave, then 3 in wave 0), the four
+// wave lists are merged through LDS, and wave 0 writes the first k indices
+// ascending.  Measured on MI355X at 16 lists: 2.7 us from the last
+// workgroup's arrival, where a one-wave radix descent over the lists' keys
+// (up to 64 dependent ballot rounds) took 6.4 us.
 // `load_list(c)` returns chunk c's sorted list in this lane.
 template <typename LoadList>
 __device__ void row_topk64_block(int n_lists, int k, int32_t* out, uint64_t* lds64, LoadList load_list) {
@@ -123,13 +127,15 @@ __device__ void row_topk64_block(int n_lists, int k, int32_t* out, uint64_t* lds
       v[u] = c < n_lists ? load_list(c) : 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < BATCH; ++u) run = (base == wave && u == 0) ? v[u] : wave_merge_desc(run, v[u]);
+    for (int u = 0; u < BATCH; ++u) {
+      if (base + 4 * u >= n_lists) break;           // wave-uniform: no merges with empty lists
+      run = (base == wave && u == 0) ? v[u] : wave_merge_desc(run, v[u]);
+    }
   }
   lds64[wave * 64 + lane] = run;
   __syncthreads();
   if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < 4; ++w) run = wave_merge_desc(run, lds64[w * 64 + lane]);
+    for (int w = 1; w < 4 && w < n_lists; ++w) run = wave_merge_desc(run, lds64[w * 64 + lane]);
     int idx = (lane < k && run != 0) ? sel_key_index(run) : 0x7FFFFFFF;
     idx = wave_sort_asc_i32(idx);
     if (lane < k) out[lane] = idx == 0x7FFFFFFF ? -1 : idx;
@@ -269,64 +275,6 @@ __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, 
   }
 }
 
-// Wave count of a per-lane count below 2^7: one ballot per bit.
-__device__ __forceinline__ int wave_count7(int cnt) {
-  int tot = 0;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) tot += __popcll(__ballot((cnt >> j) & 1)) << j;
-  return tot;
-}
-
-// Top-k (k <= 64) of a row from its chunks' candidate lists (each sorted
-// descending), by one wave: only the first k entries of a list can be
-// selected, so lane L holds entry L (L < k) of every list.  The k-th largest
-// key is found by the radix descent used for prefill rows; the selected
-// page indices are gathered through LDS and sorted ascending.
-template <int NC>
-__device__ void row_topk_lists_wave(const uint64_t* cand, int n_lists, int k, int32_t* out, int* sm_idx) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[NC];
-  const int last = n_lists > 0 ? n_lists - 1 : 0;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const uint64_t v = cand[(size_t)min(i, last) * 64 + lane];
-    key[i] = (i < n_lists && lane < k) ? v : 0ull;      // empty entries are 0
-  }
-  int cnt0 = 0;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) cnt0 += key[i] != 0ull ? 1 : 0;
-  const int total = wave_count7(cnt0);
-  uint64_t thr = 1;
-  if (total > k) {
-    uint64_t t = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t c2 = t | (1ull << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < NC; ++i) cnt += key[i] >= c2 ? 1 : 0;
-      const int tot = wave_count7(cnt);
-      if (tot >= k) {
-        t = c2;
-        if (tot == k) break;
-      }
-    }
-    thr = t;
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
-  int base = 0;
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const bool sel = key[i] >= thr;
-    const uint64_t m = __ballot(sel);
-    if (sel) sm_idx[base + __popcll(m & below)] = sel_key_index(key[i]);
-    base += __popcll(m);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  int idx = (lane < base) ? sm_idx[lane] : 0x7FFFFFFF;
-  idx = wave_sort_asc_i32(idx);
-  if (lane < k) out[lane] = idx == 0x7FFFFFFF ? -1 : idx;
-}
-
 template <int E8>
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) {
   extern __shared__ __align__(16) uint32_t dyn[];
@@ -334,8 +282,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   __shared__ int sm_scan[8];
   __shared__ int sm_misc[8];
   __shared__ int sm_b;
-  __shared__ float sm_qg[E8 * 8];
-  __shared__ uint64_t sm_keys[4][64];
+  __shared__ uint64_t sm_keys[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.y, chunk = blockIdx.x;
   constexpr int G = 8;                                // query heads per KV head (validated on the host)
@@ -347,40 +294,41 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   if (tid == 0) sm_b = request_of_row(a.row_start, a.B, r);
   __syncthreads();
   const int b = sm_b;
-  const int visible = visible_pages(a, c.PS, b, r);
   const int p_begin = chunk * SEL_CHUNK;
-  const int p_end = min(visible, p_begin + SEL_CHUNK);
   const int32_t* btb = a.bt + (size_t)b * a.max_pages;
   const int sub = lane / LANES, seg0 = lane % LANES;
 
-  // block-table entries first: independent of the query sums
+  // block-table entries first, up to the row's end (not the visible count,
+  // whose load they would otherwise wait for): independent of the query sums
+  const int p_lim = min(a.max_pages, p_begin + SEL_CHUNK);
   int logical[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
     const int p = p_begin + (it * 4 + wave) * PPW + sub;
     int lg = -1;
-    if (p < p_end) lg = btb[p];
-    logical[it] = ((int64_t)lg >= 0 && (int64_t)lg < c.N) ? lg : -1;
+    if (p < p_lim) lg = btb[p];
+    logical[it] = lg;
   }
-  // per-group query sum: exact (fp64) sum of the group's 8 bf16 heads -> fp32 -> bf16
-  for (int e = tid; e < E; e += TKV_BLOCK) {
-    const int g = e / c.D, dd = e - g * c.D;
-    const uint16_t* qp = a.q + ((size_t)r * c.Hq + g * G) * c.D + dd;
-    float v[G];
+  // the query rows of the lane's 8-element segments (element e0 = 8 * segment:
+  // group e0 / d, dims e0 % d .. +7), one 16-byte load per group head; each
+  // wave forms its own group sums, so nothing waits at a barrier and the
+  // slab loads below are in flight while they are summed
+  uint4 qraw[SPL][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) v[h] = bf16_to_f32(qp[(size_t)h * c.D]);
-    double acc = 0.0;
+  for (int s = 0; s < SPL; ++s) {
+    const int e0 = (seg0 + s * 64) * 8, g = e0 / c.D;
+    const uint16_t* qp = a.q + ((size_t)r * c.Hq + g * G) * c.D + (e0 - g * c.D);
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc += (double)v[h];
-    sm_qg[e] = bf16_to_f32(f32_to_bf16((float)acc));
+    for (int h = 0; h < G; ++h) qraw[s][h] = *reinterpret_cast<const uint4*>(qp + (size_t)h * c.D);
   }
-  __syncthreads();
-  float qg[SPL][8];
+  const int visible = visible_pages(a, c.PS, b, r);
+  const int p_end = min(visible, p_begin + SEL_CHUNK);
 #pragma unroll
-  for (int s = 0; s < SPL; ++s)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qg[s][t] = sm_qg[(seg0 + s * 64) * 8 + t];
-
+  for (int it = 0; it < PASSES; ++it) {
+    const int p = p_begin + (it * 4 + wave) * PPW + sub;
+    const int lg = logical[it];
+    logical[it] = (p < p_end && (int64_t)lg >= 0 && (int64_t)lg < c.N) ? lg : -1;
+  }
   const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
   uint4 v[PASSES][SPL];
 #pragma unroll
@@ -390,6 +338,21 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
       v[it][s] = logical[it] >= 0
                      ? reinterpret_cast<const uint4*>(slab_l + (size_t)logical[it] * E)[seg0 + s * 64]
                      : make_uint4(0, 0, 0, 0);
+  // per-group query sum: exact (fp64) sum of the group's 8 bf16 heads -> fp32 -> bf16
+  float qg[SPL][8];
+#pragma unroll
+  for (int s = 0; s < SPL; ++s) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      double acc = 0.0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t w = (&qraw[s][h].x)[t >> 1];
+        acc += (double)__uint_as_float((t & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      }
+      qg[s][t] = bf16_to_f32(f32_to_bf16((float)acc));
+    }
+  }
   float keys[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
@@ -418,10 +381,10 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int p = p_begin + (it * 4 + wave) * PPW + sub;
-      if (seg0 == 0) sm_keys[0][p - p_begin] = (p < p_end) ? sel_key(keys[it], p) : 0ull;
+      if (seg0 == 0) sm_keys[p - p_begin] = (p < p_end) ? sel_key(keys[it], p) : 0ull;
     }
     __syncthreads();
-    if (wave == 0) cand[(size_t)chunk * 64 + lane] = wave_sort_desc(sm_keys[0][lane]);
+    if (wave == 0) cand[(size_t)chunk * 64 + lane] = wave_sort_desc(sm_keys[lane]);
   } else {
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
@@ -431,16 +394,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   }
   if (!last_block_arrive(&c.row_done[r], a.n_chunks, &sm_misc[4])) return;
   int32_t* out_r = a.sel_local + (size_t)r * a.topk;
-  if (a.topk <= 64 && a.n_chunks <= 16) {
-    // few lists (up to 1,024 pages): one wave, radix descent over the first
-    // k entries of every list; more lists merge faster across 4 waves
-    if (wave == 0) {
-      int* sm_idx = reinterpret_cast<int*>(&sm_keys[0][0]);
-      if (a.n_chunks <= 8) row_topk_lists_wave<8>(cand, a.n_chunks, a.topk, out_r, sm_idx);
-      else row_topk_lists_wave<16>(cand, a.n_chunks, a.topk, out_r, sm_idx);
-    }
-    __syncthreads();
-  } else if (a.topk <= 64) {
+  if (a.topk <= 64) {
     row_topk64_block(a.n_chunks, a.topk, out_r, reinterpret_cast<uint64_t*>(dyn),
                      [&](int ch) { return cand[(size_t)ch * 64 + lane]; });
   } else {
