@@ -10,7 +10,12 @@
   report anomalies instead of faulting): an ensure needing more distinct
   pages than slots changes nothing; page ids out of range are skipped;
   fetch entries outside the pool or the page space are skipped; a store to a
-  page with no slot writes the mirror and the slab only.
+  page with no slot writes the mirror and the slab only;
+* random ensure traces (duplicates, padding, ids out of range, no-fetch
+  flags, capacity overruns) through both ensure paths: widths up to 512 on
+  pools up to 2,048 slots (state reads up front, first occurrences from an
+  LDS hash table) and wider calls or larger pools (global first-occurrence
+  marks).
 """
 from dataclasses import replace
 
@@ -100,15 +105,16 @@ def _small_tier(num_slots, max_width, layers=2):
                     max_topk=8, max_pages_per_req=64, max_width=max_width)
 
 
-def _ensure_both(t, lru, needed):
+def _ensure_both(t, lru, needed, no_fetch=None):
     W = len(needed)
     nd = torch.tensor(needed, dtype=torch.int32, device="cuda")
     out = torch.full((W,), -7, dtype=torch.int32, device="cuda")
     miss = torch.zeros((W, 2), dtype=torch.int32, device="cuda")
     cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
-    t.lru_ensure(nd, out, miss, cnt)
+    nf = None if no_fetch is None else torch.tensor(no_fetch, dtype=torch.uint8, device="cuda")
+    t.lru_ensure(nd, out, miss, cnt, no_fetch=nf)
     torch.cuda.synchronize()
-    o_out, o_miss = lru.ensure(np.array(needed, dtype=np.int64))
+    o_out, o_miss = lru.ensure(np.array(needed, dtype=np.int64), no_fetch)
     m = int(cnt.item())
     assert np.array_equal(out.cpu().numpy(), o_out), "out_slots"
     assert m == len(o_miss) and np.array_equal(miss[:m].cpu().numpy(), np.asarray(o_miss).reshape(-1, 2)), "misses"
@@ -132,6 +138,30 @@ def test_ensure_capacity_and_page_range_errors_match_oracle():
     assert t.read_counters()["error_word"] == TKV_ERR_CAPACITY | TKV_ERR_PAGE_RANGE
     assert lru.error_word == ERR_CAPACITY | ERR_PAGE_RANGE
     _ensure_both(t, lru, [30, 31, 3, 20])
+
+
+@pytest.mark.parametrize("S,N,widths", [(48, 160, (1, 130)), (200, 400, (300, 512)), (48, 160, (513, 700)),
+                                         (2300, 2600, (40, 300))])
+def test_ensure_random_traces_match_oracle(S, N, widths):
+    from tiered_kv_cache_indexer_amd import TieredKV
+    say(f"[edges] random ensure trace: {S} slots, {N} pages, widths {widths}")
+    t = TieredKV(num_layers=1, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=16, kv_format="bf16",
+                 num_logical_pages=N, num_slots=S, max_batch=1, max_topk=8, max_pages_per_req=64,
+                 max_width=widths[1])
+    lru = LRUState(N, S)
+    rng = np.random.default_rng([S, N, widths[1]])
+    for call in range(40):
+        W = int(rng.integers(widths[0], widths[1] + 1))
+        # mostly a working set that fits the pool, sometimes one that does not
+        ws = int(rng.integers(1, S + 1)) if call % 7 else int(rng.integers(S + 1, N + 1))
+        base = rng.choice(N, size=min(ws, N), replace=False)
+        needed = rng.choice(base, size=W).astype(np.int64)          # duplicates
+        needed[rng.random(W) < 0.1] = -1                             # padding
+        if call % 5 == 3:
+            needed[int(rng.integers(W))] = N + int(rng.integers(3))  # out of range
+        no_fetch = (rng.random(W) < 0.3).astype(np.uint8) if call % 2 else None
+        _ensure_both(t, lru, needed.tolist(), no_fetch)
+        assert t.read_counters()["error_word"] == lru.error_word, f"error word at call {call}"
 
 
 def test_fetch_skips_entries_outside_the_pool_or_page_space():

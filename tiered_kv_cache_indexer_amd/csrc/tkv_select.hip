@@ -519,7 +519,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* n
 }
 
 // ------------------------------------------------------------------ launchers --
-static size_t ensure_dyn_lds(const DevCtx& c) { return (size_t)((c.S + 31) / 32) * 4; }
+static size_t ensure_dyn_lds(const DevCtx& c) { return lru_lds_words(c.S) * 4; }
 
 size_t select_dyn_lds(const DevCtx& c) {
   size_t keys = (size_t)c.max_pages * 4;
