@@ -5,8 +5,9 @@
 // PR #525 commit summary (mirror_store_quant): the mirror takes the e4m3
 // codes and fp32 scales AFTER quantisation -- the pool is the source of truth.
 //
-// One workgroup per (run, page of the run).  A wave quantises one token at a
-// time: each lane holds 8 of the token's Hkv*d bf16 values (one 16-byte
+// One workgroup per (run, page of the run).  A wave takes groups of four page
+// positions, loads the group's K and V rows at once and quantises one token
+// at a time: each lane holds 8 of the token's Hkv*d bf16 values (one 16-byte
 // load), the wave reduces |x| to the token's amax, scale = amax/448 (1 if
 // amax is 0), code = e4m3(x / scale) with a correctly rounded fp32 division.
 // K codes go straight to the pool slot (HBM) and the mirror row (posted
@@ -71,13 +72,30 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
     for (int s = 0; s < SPL; ++s)
 #pragma unroll
       for (int t = 0; t < 8; ++t) vpack[s][t] = 0u;
+    // the group's K and V rows (4 positions) in flight together: one load
+    // latency per group instead of one per token and tensor
+    uint4 rawg[4][2][SPL];
+#pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int pos = pbase + u;
-      if (pos < off || pos >= off + n) continue;         // wave-uniform
+      const bool in = pos >= off && pos < off + n;
       const int tok = tok_first + (pos - off);
 #pragma unroll
       for (int kv = 0; kv < 2; ++kv) {
-        const uint16_t* src = (kv == 0 ? a.k : a.v) + (size_t)tok * E;
+        const uint16_t* src = (kv == 0 ? a.k : a.v) + (size_t)(in ? tok : 0) * E;
+#pragma unroll
+        for (int s = 0; s < SPL; ++s) {
+          const int seg = lane + s * 64;
+          rawg[u][kv][s] = (in && seg < E8) ? reinterpret_cast<const uint4*>(src)[seg] : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pos = pbase + u;
+      if (pos < off || pos >= off + n) continue;         // wave-uniform
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
         float x[SPL][8];
         bool act[SPL];
         uint4 raw[SPL];
@@ -86,7 +104,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
         for (int s = 0; s < SPL; ++s) {
           const int seg = lane + s * 64;
           act[s] = seg < E8;
-          raw[s] = act[s] ? reinterpret_cast<const uint4*>(src)[seg] : make_uint4(0, 0, 0, 0);
+          raw[s] = rawg[u][kv][s];
           const uint32_t ww[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
