@@ -26,8 +26,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   constexpr int E = E8 * 8;
   constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;
   constexpr int VT_WORDS = FP8 ? E * (64 / 4 + 1) : 1;   // transposed V block, rows padded by one word
+  // fp8 K codes and both scale vectors staged too (up to Hkv*d = 512), so
+  // every byte leaves in 16-byte vectors, a wave's store one contiguous KiB
+  constexpr bool STAGE_K = FP8 && E8 <= 64;
   __shared__ float ksum_w[4][E];
   __shared__ uint32_t vt[VT_WORDS];
+  __shared__ __align__(16) uint8_t kt[STAGE_K ? E * 64 : 16];
+  __shared__ __align__(16) float sct[STAGE_K ? 2 * 64 : 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x, j = blockIdx.y;
   const int PS = c.PS, D = c.D;
@@ -134,8 +139,12 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
               const uint2 val = make_uint2(code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24,
                                            code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24);
               const size_t o = ((size_t)h * PS + pos) * D + dd;
-              *reinterpret_cast<uint2*>(mblk + o) = val;
-              if (pblk) *reinterpret_cast<uint2*>(pblk + o) = val;
+              if (STAGE_K) {
+                *reinterpret_cast<uint2*>(kt + o) = val;
+              } else {
+                *reinterpret_cast<uint2*>(mblk + o) = val;
+                if (pblk) *reinterpret_cast<uint2*>(pblk + o) = val;
+              }
             } else {
               // V codes transposed [h][d][pos]: byte u of the group's word in each of 8 rows
 #pragma unroll
@@ -143,9 +152,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
             }
           }
           if (lane == 0) {
-            const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
-            *reinterpret_cast<float*>(mir + so) = scale;
-            if (pol) *reinterpret_cast<float*>(pol + so) = scale;
+            if (STAGE_K) {
+              sct[kv * 64 + pos] = scale;
+            } else {
+              const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
+              *reinterpret_cast<float*>(mir + so) = scale;
+              if (pol) *reinterpret_cast<float*>(pol + so) = scale;
+            }
           }
         } else {
 #pragma unroll
@@ -202,6 +215,37 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
     uint8_t* mv = mir + cb;
     uint8_t* pv = pol ? pol + cb : nullptr;
     const int wpr = PS / 4;
+    if (STAGE_K) {
+      // K codes [h][pos][d]: positions [off, off+n) of each head, 16 bytes a thread
+      const int per_h = n * D / 16;
+      for (int g16 = tid; g16 < c.Hkv * per_h; g16 += TKV_BLOCK) {
+        const int h = g16 / per_h;
+        const size_t o = ((size_t)h * PS + off) * D + (size_t)(g16 - h * per_h) * 16;
+        const uint4 w = *reinterpret_cast<const uint4*>(kt + o);
+        *reinterpret_cast<uint4*>(mir + o) = w;
+        if (pol) *reinterpret_cast<uint4*>(pol + o) = w;
+      }
+      // scales of positions [off, off+n), K then V
+      for (int i = tid; i < 2 * n; i += TKV_BLOCK) {
+        const int kv = i / n, pos = off + (i - kv * n);
+        const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
+        const float sc = sct[kv * 64 + pos];
+        *reinterpret_cast<float*>(mir + so) = sc;
+        if (pol) *reinterpret_cast<float*>(pol + so) = sc;
+      }
+    }
+    if (STAGE_K && lo == 0 && hi == PS) {
+      // whole V rows: 16 bytes (four staged words) a thread, rows back to back
+      const int gpr = PS / 16;
+      for (int g16 = tid; g16 < E * gpr; g16 += TKV_BLOCK) {
+        const int e = g16 / gpr, part = g16 - e * gpr;
+        const uint32_t* src = vt + e * VROW + part * 4;
+        const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
+        const size_t o = (size_t)e * PS + part * 16;
+        *reinterpret_cast<uint4*>(mv + o) = w;
+        if (pv) *reinterpret_cast<uint4*>(pv + o) = w;
+      }
+    } else {
     for (int idx = tid; idx < E * wpr; idx += TKV_BLOCK) {
       const int e = idx / wpr, w = idx - e * wpr;
       const int p0 = 4 * w;
@@ -218,6 +262,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
           if (pv) pv[o + b] = (uint8_t)(word >> (8 * b));
         }
       }
+    }
     }
   }
 
