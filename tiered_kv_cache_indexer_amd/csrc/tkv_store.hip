@@ -19,17 +19,28 @@
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
+// 16 waves: one group of four positions each on a 64-token page, so the
+// quantisation of a page is done in a quarter of the time it took 4 waves
+// and the mirror writes that follow start sooner (the writes run at the
+// link's rate; measured on MI355X, a 4,096-token store of 12 layers took
+// 1.5 ms, 0.7 ms of it with the host writes taken out)
+// (Hkv*d = 1024 keeps 4 waves: its registers would not fit 16)
+template <int E8>
+__host__ __device__ constexpr int store_block() { return E8 >= 128 ? 256 : 1024; }
+
 
 
 template <int E8, bool FP8>
-__global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
+__global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs a) {
   constexpr int E = E8 * 8;
   constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;
   constexpr int VT_WORDS = FP8 ? E * (64 / 4 + 1) : 1;   // transposed V block, rows padded by one word
   // fp8 K codes and both scale vectors staged too (up to Hkv*d = 512), so
   // every byte leaves in 16-byte vectors, a wave's store one contiguous KiB
   constexpr bool STAGE_K = FP8 && E8 <= 64;
-  __shared__ float ksum_w[4][E];
+  constexpr int STORE_BLOCK = store_block<E8>();
+  constexpr int NW = STORE_BLOCK / 64;
+  __shared__ float ksum_w[NW][E];
   __shared__ uint32_t vt[VT_WORDS];
   __shared__ __align__(16) uint8_t kt[STAGE_K ? E * 64 : 16];
   __shared__ __align__(16) float sct[STAGE_K ? 2 * 64 : 4];
@@ -59,7 +70,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   const int tok_first = a.run_tok_off[r] + (t0 - start);  // input row of page position `off`
   const int VROW = PS / 4 + 1;                             // words per staged V row (fp8)
   if (FP8)
-    for (int w = tid; w < E * VROW; w += TKV_BLOCK) vt[w] = 0u;
+    for (int w = tid; w < E * VROW; w += STORE_BLOCK) vt[w] = 0u;
 
   float ksum[SPL][8];
 #pragma unroll
@@ -69,7 +80,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   if (FP8) __syncthreads();
 
   // a wave handles groups of 4 consecutive page positions
-  for (int grp = wave; grp * 4 < PS; grp += 4) {
+  for (int grp = wave; grp * 4 < PS; grp += NW) {
     const int pbase = grp * 4;
     if (pbase + 3 < off || pbase >= off + n) continue;   // wave-uniform
     uint32_t vpack[SPL][8];
@@ -191,13 +202,13 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
     for (int kv = 0; kv < (FP8 ? 1 : 2); ++kv)
       for (int h = 0; h < H; ++h) {
         const size_t base = (size_t)kv * cb + ((size_t)h * PS + n) * D * elt;
-        for (int i = tid * 4; i < tail; i += TKV_BLOCK * 4) {
+        for (int i = tid * 4; i < tail; i += STORE_BLOCK * 4) {
           *reinterpret_cast<uint32_t*>(mir + base + i) = 0u;
           if (pol) *reinterpret_cast<uint32_t*>(pol + base + i) = 0u;
         }
       }
     if (FP8) {
-      for (int i = n + tid; i < PS; i += TKV_BLOCK) {
+      for (int i = n + tid; i < PS; i += STORE_BLOCK) {
         reinterpret_cast<float*>(mir + 2 * cb)[i] = 0.f;
         reinterpret_cast<float*>(mir + 2 * cb + PS * 4)[i] = 0.f;
         if (pol) {
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
     if (STAGE_K) {
       // K codes [h][pos][d]: positions [off, off+n) of each head, 16 bytes a thread
       const int per_h = n * D / 16;
-      for (int g16 = tid; g16 < c.Hkv * per_h; g16 += TKV_BLOCK) {
+      for (int g16 = tid; g16 < c.Hkv * per_h; g16 += STORE_BLOCK) {
         const int h = g16 / per_h;
         const size_t o = ((size_t)h * PS + off) * D + (size_t)(g16 - h * per_h) * 16;
         const uint4 w = *reinterpret_cast<const uint4*>(kt + o);
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
         if (pol) *reinterpret_cast<uint4*>(pol + o) = w;
       }
       // scales of positions [off, off+n), K then V
-      for (int i = tid; i < 2 * n; i += TKV_BLOCK) {
+      for (int i = tid; i < 2 * n; i += STORE_BLOCK) {
         const int kv = i / n, pos = off + (i - kv * n);
         const size_t so = 2 * cb + (size_t)kv * PS * 4 + (size_t)pos * 4;
         const float sc = sct[kv * 64 + pos];
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
     if (STAGE_K && lo == 0 && hi == PS) {
       // whole V rows: 16 bytes (four staged words) a thread, rows back to back
       const int gpr = PS / 16;
-      for (int g16 = tid; g16 < E * gpr; g16 += TKV_BLOCK) {
+      for (int g16 = tid; g16 < E * gpr; g16 += STORE_BLOCK) {
         const int e = g16 / gpr, part = g16 - e * gpr;
         const uint32_t* src = vt + e * VROW + part * 4;
         const uint4 w = make_uint4(src[0], src[1], src[2], src[3]);
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
         if (pv) *reinterpret_cast<uint4*>(pv + o) = w;
       }
     } else {
-    for (int idx = tid; idx < E * wpr; idx += TKV_BLOCK) {
+    for (int idx = tid; idx < E * wpr; idx += STORE_BLOCK) {
       const int e = idx / wpr, w = idx - e * wpr;
       const int p0 = 4 * w;
       if (p0 + 4 <= lo || p0 >= hi) continue;
@@ -277,8 +288,10 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_store(DevCtx c, StoreArgs a) {
   __syncthreads();
   const size_t sbase = ((size_t)a.layer * c.N + page) * E;
   const int cnt = off + n;
-  for (int e = tid; e < E; e += TKV_BLOCK) {
-    float sum = (ksum_w[0][e] + ksum_w[1][e]) + (ksum_w[2][e] + ksum_w[3][e]);
+  for (int e = tid; e < E; e += STORE_BLOCK) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; w += 4) sum += (ksum_w[w][e] + ksum_w[w + 1][e]) + (ksum_w[w + 2][e] + ksum_w[w + 3][e]);
     if (off > 0) sum += c.slab_acc[sbase + e];
     c.slab_acc[sbase + e] = sum;
     c.slab[sbase + e] = f32_to_bf16(sum / (float)cnt);
@@ -295,16 +308,16 @@ hipError_t launch_store(const DevCtx& c, const StoreArgs& a, int max_run_len, hi
   dim3 grid(a.n_runs, ppr);
   const int E8 = c.Hkv * c.D / 8;
   if (c.fp8) {
-    if (E8 == 64) hipLaunchKernelGGL((k_store<64, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, true>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    if (E8 == 64) hipLaunchKernelGGL((k_store<64, true>), grid, dim3(store_block<64>()), 0, st, c, a);
+    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, true>), grid, dim3(store_block<16>()), 0, st, c, a);
+    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, true>), grid, dim3(store_block<32>()), 0, st, c, a);
+    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, true>), grid, dim3(store_block<128>()), 0, st, c, a);
     else return hipErrorInvalidValue;
   } else {
-    if (E8 == 64) hipLaunchKernelGGL((k_store<64, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
-    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, false>), grid, dim3(TKV_BLOCK), 0, st, c, a);
+    if (E8 == 64) hipLaunchKernelGGL((k_store<64, false>), grid, dim3(store_block<64>()), 0, st, c, a);
+    else if (E8 == 16) hipLaunchKernelGGL((k_store<16, false>), grid, dim3(store_block<16>()), 0, st, c, a);
+    else if (E8 == 32) hipLaunchKernelGGL((k_store<32, false>), grid, dim3(store_block<32>()), 0, st, c, a);
+    else if (E8 == 128) hipLaunchKernelGGL((k_store<128, false>), grid, dim3(store_block<128>()), 0, st, c, a);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();
