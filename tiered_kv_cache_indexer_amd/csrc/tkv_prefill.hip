@@ -86,38 +86,60 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_prefill_scores(DevCtx c, SelArgs 
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-#pragma unroll 4
-  for (int k0 = 0; k0 < E; k0 += 32) {
-    bf16x8 av[2], bv[2];
+  // operands of KB contraction steps in flight at once (every load of a
+  // batch issued before the first product; a page outside the request reads
+  // slab row 0 and its column is set to -inf below)
+  constexpr int KS = E / 32, KB = KS < 8 ? KS : 8;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      av[t] = ld_bf16x8(arow[t] + k0);
-      bv[t] = bok[t] ? ld_bf16x8(brow[t] + k0) : zero;
-    }
+  for (int kb = 0; kb < KS; kb += KB) {
+    bf16x8 av[KB][2], bv[KB][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < KB; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      for (int t = 0; t < 2; ++t) {
+        av[u][t] = ld_bf16x8(arow[t] + (kb + u) * 32);
+        bv[u][t] = ld_bf16x8(brow[t] + (kb + u) * 32);
+      }
+    __builtin_amdgcn_sched_barrier(0);   // keep the batch's loads ahead of its products
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][i], bv[u][j], acc[i][j], 0, 0, 0);
   }
   // output tile (i, j): lane holds rows 4*(lane/16) + v, page column lane % 16
+  float bias[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = p0 + j * 16 + m;
-    if (p >= npg) continue;
-    float bias = 0.f;
-    if (a.bias && bok[j]) bias = a.bias[logical[j]];
+  for (int j = 0; j < 2; ++j) bias[j] = (a.bias && bok[j]) ? a.bias[logical[j]] : 0.f;
+  float* __restrict__ sc = c.scores;
+  // interior tiles (a wave-uniform test) store without per-lane conditions,
+  // so the 16 stores issue back to back
+  float key[2][2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = row0 + i * 16 + kq * 4 + v;
-        if (r >= a.rows) continue;
-        float key = acc[i][j][v];
-        key = bok[j] ? (a.bias ? key + bias : key) : -INFINITY;
-        c.scores[(size_t)r * c.max_pages + p] = key;
-      }
+      for (int v = 0; v < 4; ++v) key[j][i][v] = bok[j] ? acc[i][j][v] + bias[j] : -INFINITY;
+  float* base = sc + (size_t)(row0 + kq * 4) * c.max_pages + p0 + m;
+  if (p0 + 32 <= npg && row0 + 32 <= a.rows) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) base[(size_t)(i * 16 + v) * c.max_pages + j * 16] = key[j][i][v];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (p0 + j * 16 + m < npg && row0 + i * 16 + kq * 4 + v < a.rows)
+            base[(size_t)(i * 16 + v) * c.max_pages + j * 16] = key[j][i][v];
   }
 }
 
