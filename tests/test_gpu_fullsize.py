@@ -1,5 +1,8 @@
-"""Parity at the full workload sizes, in the launch configuration bench.py
-times (fused decode_layer per layer, eager launches on one stream).
+"""Parity at the full workload sizes, in the launch configurations bench.py
+times: fused decode_layer per layer (eager launches on one stream), and for
+the workloads whose steps miss pages (196k-context thrash, batch 4) the split
+decode the bench times there (decode_layer_split: slice copies on the decode
+stream, the rest of the rows on a copy stream).
 
 Exact for every layer of the steps run: selections, compaction, slot maps,
 miss lists, LRU state and counters; the slab of every page; attention on
@@ -19,7 +22,7 @@ from tests.gpu_compare import assert_close, bf16_to_f64, compare_state, say
 pytestmark = pytest.mark.gpu
 
 
-def _decode_fullsize(key, steps, attn_layers):
+def _decode_fullsize(key, steps, attn_layers, split=False):
     from workload.gpu_run import GpuWorkload
     wl = get_workload(key)
     say(f"[fullsize] {key}: {wl.description}")
@@ -39,8 +42,12 @@ def _decode_fullsize(key, steps, attn_layers):
     bias = gen.page_bias(wl)
     rs = np.arange(wl.batch + 1)
     o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    side = torch.cuda.Stream() if split else None
     for s in range(steps):
-        g.decode_step(s)
+        if split:
+            g.decode_step_split(s, side)
+        else:
+            g.decode_step(s)
         torch.cuda.synchronize()
         for layer in range(wl.num_layers):
             where = f"{key} step {s} layer {layer}"
@@ -56,6 +63,11 @@ def _decode_fullsize(key, steps, attn_layers):
                 assert_close(bf16_to_f64(g.out[layer]), rec["out"], f"{where}: attention")
         say(f"[fullsize] {key}: step {s} ok")
         compare_state(g, o, f"{key} step {s}", sample_pages=sample_pages)
+        if split:
+            # pool rows of pages the step's copies brought in (resident now)
+            resident = [int(p) for p in o.lru.slot_to_page if p >= 0]
+            picked = sorted(rng.choice(resident, size=min(4, len(resident)), replace=False).tolist())
+            compare_state(g, o, f"{key} step {s} (copied rows)", sample_pages=picked)
     c = g.tier.read_counters()
     assert c["error_word"] == 0 and c["drops"] == 0
     return wl, g, o
@@ -73,6 +85,16 @@ def test_c3_fullsize():
 
 def test_c4_fullsize():
     _decode_fullsize("c4", steps=2, attn_layers={5})
+
+
+def test_c3_fullsize_split():
+    wl, g, o = _decode_fullsize("c3", steps=3, attn_layers={1, 6, 11}, split=True)
+    c = g.tier.read_counters()
+    assert c["misses"] > 0 and c["evictions"] > 0
+
+
+def test_c4_fullsize_split():
+    _decode_fullsize("c4", steps=2, attn_layers={2, 9}, split=True)
 
 
 def test_c5_fullsize_prefill():
