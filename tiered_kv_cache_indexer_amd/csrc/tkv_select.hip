@@ -445,16 +445,44 @@ __device__ __forceinline__ int wave_count6(int cnt) {
 }
 
 // One wave per row, keys of up to 64*NPL visible pages in registers.  The
-// k-th largest key T is found by a radix descent from the top bit: a bit is
-// kept when at least k keys are >= the prefix with it set, and the descent
-// stops early once exactly k keys are >= the prefix.  Keys are unique (the
+// k-th largest key T is the k-th of the few keys at or above a bound taken
+// from the lanes' maxima (below); where those are more than 64, T is found by
+// a radix descent from the top bit: a bit is kept when at least k keys are
+// >= the prefix with it set, and the descent stops early once exactly k keys
+// are >= the prefix.  Keys are unique (the
 // low word is ~page), so exactly min(k, visible) keys are >= T; they are
 // written in ascending page order by ballot prefix counts.
+// Workgroup size of the per-row top-k: 4 rows (16 measured the same).
+#define RW_BLOCK TKV_BLOCK
+
+// Nonzero words of the LDS group bitmap into the global one (the group of
+// the workgroup's first wave).
+template <int NW_WORDS>
+__device__ __forceinline__ void rows_wave_flush_n(const DevCtx& c, const uint32_t* wbm, const int* wgrp, int words) {
+  const int g0 = wgrp[0];
+  if (g0 < 0) return;
+  for (int w = threadIdx.x; w < NW_WORDS && w < words; w += RW_BLOCK)
+    if (wbm[w]) atomicOr(&c.sel_bm[(size_t)g0 * words + w], wbm[w]);
+}
+#define rows_wave_flush(c, wbm, wgrp, words) rows_wave_flush_n<2 * NPL>((c), (wbm), (wgrp), (words))
+
 template <int NPL>
-__global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * (TKV_BLOCK / 64) + (threadIdx.x >> 6);
-  if (r >= a.rows) return;
+__global__ __launch_bounds__(RW_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs a) {
+  constexpr int NW = RW_BLOCK / 64;
+  __shared__ uint64_t cbuf[NW][64];
+  __shared__ uint32_t wbm[2 * NPL];   // the first wave's group bitmap (64 * NPL pages)
+  __shared__ int wgrp[NW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.x * NW + wave;
+  for (int w = threadIdx.x; w < 2 * NPL; w += RW_BLOCK) wbm[w] = 0u;
+  const int words = (a.max_pages + 31) >> 5;   // <= 2 * NPL (max_pages <= 64 * NPL)
+  if (r >= a.rows) {
+    if (lane == 0) wgrp[wave] = -1;
+    __syncthreads();
+    __syncthreads();
+    rows_wave_flush(c, wbm, wgrp, words);
+    return;
+  }
   const int b = request_of_row(a.row_start, a.B, r);
   const int visible = visible_pages(a, c.PS, b, r);
   const float* sc = c.scores + (size_t)r * c.max_pages;
@@ -470,8 +498,39 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
     key[i] = p < visible ? sel_key(v, p) : 0ull;   // valid keys are nonzero
   }
   const int k = a.topk;
+  const uint64_t below = (1ull << lane) - 1ull;
   uint64_t thr = 1;
-  if (visible > k) {
+  bool found = visible <= k;
+  if (!found && k <= 64) {
+    // A bound from the lanes' maxima: the k-th largest of them, T, has at
+    // least k keys at or above it, so the k-th largest key is >= T.  The keys
+    // >= T (about 43 of 1,088 random keys for k = 32, more than 64 in about
+    // 1 of 20,000 rows) are gathered and sorted in one wave; the k-th of
+    // them is the threshold.  With more than 64 the radix descent decides.
+    uint64_t lm = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) lm = key[i] > lm ? key[i] : lm;
+    const uint64_t T = shfl_u64(wave_sort_desc(lm), k - 1);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) cnt += key[i] >= T ? 1 : 0;
+    if (wave_count6(cnt) <= 64) {
+      uint64_t* cb = cbuf[threadIdx.x >> 6];
+      int base = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const bool s = key[i] >= T;
+        const uint64_t m = __ballot(s);
+        if (s) cb[base + __popcll(m & below)] = key[i];
+        base += __popcll(m);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint64_t cv = lane < base ? cb[lane] : 0ull;
+      thr = shfl_u64(wave_sort_desc(cv), k - 1);
+      found = true;
+    }
+  }
+  if (!found) {
     uint64_t t = 0;
     for (int bit = 63; bit >= 0; --bit) {
       const uint64_t cand = t | (1ull << bit);
@@ -487,9 +546,16 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
     thr = t;
   }
   int32_t* out = a.sel_local + (size_t)r * k;
+  // a request with several rows marks the row's pages in its group's bitmap:
+  // the waves whose group is the first wave's OR into LDS (the workgroup's
+  // rows are consecutive, so normally all of them) and the workgroup flushes
+  // each nonzero word with one atomic; other waves mark the global bitmap
   const bool multi = a.row_start[b + 1] - a.row_start[b] > 1;
-  uint32_t* bm = multi ? c.sel_bm + (size_t)sel_bm_group(a, b, r) * ((a.max_pages + 31) >> 5) : nullptr;
-  const uint64_t below = (1ull << lane) - 1ull;
+  const int grp = multi ? sel_bm_group(a, b, r) : -1;
+  if (lane == 0) wgrp[wave] = grp;
+  __syncthreads();
+  const bool to_lds = grp >= 0 && grp == wgrp[0];
+  uint32_t* bm = (grp >= 0 && !to_lds) ? c.sel_bm + (size_t)grp * words : nullptr;
   int base = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -498,11 +564,14 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_rows_wave(DevCtx c, SelArg
     if (s) {
       const int p = i * 64 + lane;
       out[base + __popcll(m & below)] = p;
-      if (bm) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      if (to_lds) atomicOr(&wbm[p >> 5], 1u << (p & 31));
+      else if (bm) atomicOr(&bm[p >> 5], 1u << (p & 31));
     }
     base += __popcll(m);
   }
   for (int j = base + lane; j < k; j += 64) out[j] = -1;
+  __syncthreads();
+  rows_wave_flush(c, wbm, wgrp, words);
 }
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_finish(DevCtx c, SelArgs a) {
@@ -543,10 +612,11 @@ hipError_t launch_select_scan(const DevCtx& c, const SelArgs& a, hipStream_t st)
 }
 
 hipError_t launch_select_rows(const DevCtx& c, const SelArgs& a, hipStream_t st) {
-  const dim3 wgrid((a.rows + 3) / 4);
-  if (a.max_pages <= 512) hipLaunchKernelGGL(k_select_rows_wave<8>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
-  else if (a.max_pages <= 1024) hipLaunchKernelGGL(k_select_rows_wave<16>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
-  else if (a.max_pages <= 2048) hipLaunchKernelGGL(k_select_rows_wave<32>, wgrid, dim3(TKV_BLOCK), 0, st, c, a);
+  const dim3 wgrid((a.rows + RW_BLOCK / 64 - 1) / (RW_BLOCK / 64));
+  if (a.max_pages <= 512) hipLaunchKernelGGL(k_select_rows_wave<8>, wgrid, dim3(RW_BLOCK), 0, st, c, a);
+  else if (a.max_pages <= 1024) hipLaunchKernelGGL(k_select_rows_wave<16>, wgrid, dim3(RW_BLOCK), 0, st, c, a);
+  else if (a.max_pages <= 1536) hipLaunchKernelGGL(k_select_rows_wave<24>, wgrid, dim3(RW_BLOCK), 0, st, c, a);
+  else if (a.max_pages <= 2048) hipLaunchKernelGGL(k_select_rows_wave<32>, wgrid, dim3(RW_BLOCK), 0, st, c, a);
   else hipLaunchKernelGGL(k_select_rows, dim3(a.rows), dim3(TKV_BLOCK), select_dyn_lds(c), st, c, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
