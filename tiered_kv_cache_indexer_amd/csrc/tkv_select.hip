@@ -458,13 +458,12 @@ __device__ __forceinline__ int wave_count6(int cnt) {
 // Nonzero words of the LDS group bitmap into the global one (the group of
 // the workgroup's first wave).
 template <int NW_WORDS>
-__device__ __forceinline__ void rows_wave_flush_n(const DevCtx& c, const uint32_t* wbm, const int* wgrp, int words) {
+__device__ __forceinline__ void rows_wave_flush(const DevCtx& c, const uint32_t* wbm, const int* wgrp, int words) {
   const int g0 = wgrp[0];
   if (g0 < 0) return;
   for (int w = threadIdx.x; w < NW_WORDS && w < words; w += RW_BLOCK)
     if (wbm[w]) atomicOr(&c.sel_bm[(size_t)g0 * words + w], wbm[w]);
 }
-#define rows_wave_flush(c, wbm, wgrp, words) rows_wave_flush_n<2 * NPL>((c), (wbm), (wgrp), (words))
 
 template <int NPL>
 __global__ __launch_bounds__(RW_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs a) {
@@ -480,7 +479,7 @@ __global__ __launch_bounds__(RW_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs
     if (lane == 0) wgrp[wave] = -1;
     __syncthreads();
     __syncthreads();
-    rows_wave_flush(c, wbm, wgrp, words);
+    rows_wave_flush<2 * NPL>(c, wbm, wgrp, words);
     return;
   }
   const int b = request_of_row(a.row_start, a.B, r);
@@ -571,7 +570,7 @@ __global__ __launch_bounds__(RW_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs
   }
   for (int j = base + lane; j < k; j += 64) out[j] = -1;
   __syncthreads();
-  rows_wave_flush(c, wbm, wgrp, words);
+  rows_wave_flush<2 * NPL>(c, wbm, wgrp, words);
 }
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_finish(DevCtx c, SelArgs a) {
