@@ -11,10 +11,10 @@
 // on the query grid, so the bf16 rounding is the only one.
 // k_prefill_scores: one 256-thread workgroup per 64 rows x 64 pages; each wave
 // owns 32 x 32 outputs as 2 x 2 tiles of v_mfma_f32_16x16x32_bf16.  Lane i of
-// a wave loads row (i % 16) of a 16 x 32 A tile and page (i % 16) of the
-// 32 x 16 B tile, 8 consecutive features (16 bytes) at feature offset
-// 8 * (i / 16): A and B use the same feature slicing, so the product is the
-// dot product over all features.  Accumulation is fp32; with the inputs on
+// a wave reads row (i % 16) of a 16 x 32 A tile and page (i % 16) of the
+// 32 x 16 B tile from LDS, 8 consecutive features (16 bytes) at feature
+// offset 8 * (i / 16): A and B use the same feature slicing, so the product
+// is the dot product over all features.  Accumulation is fp32; with the inputs on
 // the indexer grids (qg on 2^-5, slab on 2^-10, sum |qg*slab| < 2^9) every
 // partial sum is exact, so the scores equal the decode scan's bit for bit.
 #include "tkv_dev.h"
@@ -57,57 +57,97 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
 
 template <int E>
 __global__ __launch_bounds__(TKV_BLOCK) void k_prefill_scores(DevCtx c, SelArgs a, const uint16_t* qg) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The workgroup's 64 query rows and 64 pages pass through LDS in chunks of
+  // 64 features (128 bytes of a row): a load instruction moves whole 128-byte
+  // row pieces (8 rows a wave), each row is read from the caches once per
+  // workgroup instead of once per wave, and the next chunk's loads are in
+  // flight while the current one is multiplied.  Rows are padded to 144
+  // bytes, so the fragment reads (16 rows, 16 bytes each) hit distinct banks.
+  constexpr int KC = 64, NCH = E / KC, RS = KC * 2 + 16;
+  __shared__ __align__(16) uint8_t lds[2][2][64 * RS];   // [buffer][query rows | pages]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int row0 = blockIdx.y * 64 + wr * 32;
-  const int p0 = blockIdx.x * 64 + wc * 32;
+  const int rowb = blockIdx.y * 64, pb = blockIdx.x * 64;
+  const int row0 = rowb + wr * 32;
+  const int p0 = pb + wc * 32;
   const int m = lane & 15, kq = lane >> 4;
   const int npg = min(a.n_pages[0], a.max_pages);
   const uint16_t* slab_l = c.slab + (size_t)a.layer * c.N * E;
 
-  // operand rows of this lane: 2 query rows, 2 pages
-  const uint16_t* arow[2];
-  const uint16_t* brow[2];
+  // loader: thread t moves 16-byte piece t % 8 of rows t / 8 and t / 8 + 32
+  // (a page outside the request loads slab row 0; its column is set to -inf)
+  const int lp = tid & 7, lr = tid >> 3;
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = min(rowb + lr + 32 * h, a.rows - 1);
+    asrc[h] = qg + (size_t)r * E + lp * 8;
+    const int p = pb + lr + 32 * h;
+    int lg = p < npg ? a.bt[p] : -1;
+    if (!(lg >= 0 && (int64_t)lg < c.N)) lg = 0;
+    bsrc[h] = slab_l + (size_t)lg * E + lp * 8;
+  }
+  // this lane's output pages
   int logical[2];
   bool bok[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int r = min(row0 + t * 16 + m, a.rows - 1);
-    arow[t] = qg + (size_t)r * E + kq * 8;
     const int p = p0 + t * 16 + m;
     int lg = -1;
     if (p < npg) lg = a.bt[p];
     bok[t] = lg >= 0 && (int64_t)lg < c.N;
     logical[t] = bok[t] ? lg : 0;
-    brow[t] = slab_l + (size_t)logical[t] * E + kq * 8;
   }
+  const uint4* a0 = reinterpret_cast<const uint4*>(asrc[0]);
+  const uint4* a1 = reinterpret_cast<const uint4*>(asrc[1]);
+  const uint4* b0 = reinterpret_cast<const uint4*>(bsrc[0]);
+  const uint4* b1 = reinterpret_cast<const uint4*>(bsrc[1]);
+  const int so0 = lr * RS + lp * 16, so1 = (lr + 32) * RS + lp * 16;
+  constexpr int CV = KC / 8;   // 16-byte vectors per chunk of a row
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // operands of KB contraction steps in flight at once (every load of a
-  // batch issued before the first product; a page outside the request reads
-  // slab row 0 and its column is set to -inf below)
-  constexpr int KS = E / 32, KB = KS < 8 ? KS : 8;
+  uint4 ra0 = a0[0], ra1 = a1[0], rb0 = b0[0], rb1 = b1[0];
+  *reinterpret_cast<uint4*>(&lds[0][0][so0]) = ra0;
+  *reinterpret_cast<uint4*>(&lds[0][0][so1]) = ra1;
+  *reinterpret_cast<uint4*>(&lds[0][1][so0]) = rb0;
+  *reinterpret_cast<uint4*>(&lds[0][1][so1]) = rb1;
+  __syncthreads();
+#pragma unroll 2
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < NCH) {
+      ra0 = a0[(ch + 1) * CV];
+      ra1 = a1[(ch + 1) * CV];
+      rb0 = b0[(ch + 1) * CV];
+      rb1 = b1[(ch + 1) * CV];
+    }
 #pragma unroll
-  for (int kb = 0; kb < KS; kb += KB) {
-    bf16x8 av[KB][2], bv[KB][2];
-#pragma unroll
-    for (int u = 0; u < KB; ++u)
+    for (int s = 0; s < KC / 32; ++s) {
+      bf16x8 av[2], bv[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        av[u][t] = ld_bf16x8(arow[t] + (kb + u) * 32);
-        bv[u][t] = ld_bf16x8(brow[t] + (kb + u) * 32);
+        av[t] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&lds[buf][0][(wr * 32 + t * 16 + m) * RS + s * 64 + kq * 16]));
+        bv[t] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&lds[buf][1][(wc * 32 + t * 16 + m) * RS + s * 64 + kq * 16]));
       }
-    __builtin_amdgcn_sched_barrier(0);   // keep the batch's loads ahead of its products
-#pragma unroll
-    for (int u = 0; u < KB; ++u)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][i], bv[u][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (ch + 1 < NCH) {   // nobody reads buffer buf ^ 1 until the barrier below
+      *reinterpret_cast<uint4*>(&lds[buf ^ 1][0][so0]) = ra0;
+      *reinterpret_cast<uint4*>(&lds[buf ^ 1][0][so1]) = ra1;
+      *reinterpret_cast<uint4*>(&lds[buf ^ 1][1][so0]) = rb0;
+      *reinterpret_cast<uint4*>(&lds[buf ^ 1][1][so1]) = rb1;
+    }
+    __syncthreads();
   }
   // output tile (i, j): lane holds rows 4*(lane/16) + v, page column lane % 16
   float bias[2];
