@@ -27,6 +27,9 @@
  *    ordering notes).
  *  - Return value: TKV_OK (0) or a negative TKV_E_* code; tkv_last_error()
  *    returns a thread-local message naming the offending argument or knob.
+ *  - bf16 row buffers (queries, attention outputs, new keys and values) are
+ *    read and written in 16-byte vectors and must be 16-byte aligned
+ *    (TKV_E_INVALID_ARG otherwise, before anything is launched).
  *  - Anomalies found on the device (page id out of range, a selection that
  *    does not fit the pool, a store to a non-resident page) set bits of a
  *    sticky error word returned by tkv_read_counters.  Pages cut by the

@@ -164,6 +164,33 @@ def test_ensure_random_traces_match_oracle(S, N, widths):
         assert t.read_counters()["error_word"] == lru.error_word, f"error word at call {call}"
 
 
+def test_misaligned_rows_are_refused_before_any_launch():
+    """bf16 rows are read in 16-byte vectors: a query or key buffer that is not
+    16-byte aligned is an argument error, reported before anything runs."""
+    from tiered_kv_cache_indexer_amd import TkvError
+    say("[edges] misaligned q / k")
+    t = _small_tier(16, 16)
+    t.set_select_width(1, 4, 0)
+    Hq, Hkv, d = 32, 4, 128
+    qbuf = torch.zeros(1 + Hq * d, dtype=torch.bfloat16, device="cuda")
+    q = qbuf[1:].view(1, Hq, d)                       # 2 bytes past an aligned address
+    rs = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    bt = torch.arange(64, dtype=torch.int32, device="cuda").view(1, 64)
+    npg = torch.tensor([8], dtype=torch.int32, device="cuda")
+    sel = torch.full((1, 4), -1, dtype=torch.int32, device="cuda")
+    needed = torch.full((1, t.C), -1, dtype=torch.int32, device="cuda")
+    with pytest.raises(TkvError, match="16-byte"):
+        t.select_pages(0, q, rs, bt, npg, 4, sel, needed)
+    kbuf = torch.zeros(1 + Hkv * d, dtype=torch.bfloat16, device="cuda")
+    k = kbuf[1:].view(1, Hkv, d)
+    v = torch.zeros(1, Hkv, d, dtype=torch.bfloat16, device="cuda")
+    one = torch.tensor([0], dtype=torch.int32, device="cuda")
+    with pytest.raises(TkvError, match="16-byte"):
+        t.store_kv_mirror(0, k, v, one, one, torch.tensor([1], dtype=torch.int32, device="cuda"), one, 1, bt)
+    torch.cuda.synchronize()
+    assert t.read_counters()["error_word"] == 0
+
+
 def test_fetch_skips_entries_outside_the_pool_or_page_space():
     say("[edges] fetch with bad miss entries")
     S, N = 6, 64

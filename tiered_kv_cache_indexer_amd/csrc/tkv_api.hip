@@ -390,6 +390,13 @@ static int check_rows(tkv_ctx* c, int layer, int rows, int B, int max_pages, int
   return TKV_OK;
 }
 
+// bf16 rows (queries, new keys and values) are read in 16-byte vectors
+static int check_vec16(const void* p, const char* name) {
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0)
+    return fail(TKV_E_INVALID_ARG, "%s=%p is not 16-byte aligned", name, p);
+  return TKV_OK;
+}
+
 static SelArgs make_sel(tkv_ctx* c, int layer, const uint16_t* q, int rows, const int32_t* row_start,
                         const int32_t* row_pos, const int32_t* bt, int max_pages, const int32_t* n_pages,
                         int B, const float* bias, int topk, int32_t* sel, int32_t* needed) {
@@ -411,6 +418,7 @@ int tkv_select_pages(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   if (!c->C) return fail(TKV_E_STATE, "select width not set (tkv_set_select_width)");
   if (!q || !row_start || !block_table || !n_pages || !sel_local || !needed)
     return fail(TKV_E_INVALID_ARG, "a required pointer is NULL (q, row_start, block_table, n_pages, sel_local, needed)");
+  if ((rc = check_vec16(q, "q"))) return rc;
   SelArgs a = make_sel(c, layer, q, rows, row_start, row_pos, block_table, max_pages, n_pages, B,
                        page_bias, topk, sel_local, needed);
   a.do_ensure = 0;
@@ -482,6 +490,7 @@ static int attn_call(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   if ((rc = check_rows(c, layer, rows, B, max_pages, topk))) return rc;
   if (!q || !row_start || !ctx_len || !sel_local || !block_table || !out)
     return fail(TKV_E_INVALID_ARG, "a required pointer is NULL (q, row_start, ctx_len, sel_local, block_table, out)");
+  if ((rc = check_vec16(q, "q")) || (rc = check_vec16(out, "out"))) return rc;
   if (rows > c->cfg.max_batch && topk > 64)
     return fail(TKV_E_INVALID_ARG, "topk=%d > 64 with rows=%d > max_batch: such rows are not split", topk, rows);
   AttnArgs a{};
@@ -521,6 +530,7 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   if (!c->C) return fail(TKV_E_STATE, "select width not set (tkv_set_select_width)");
   if (!q || !block_table || !n_pages || !ctx_len || !sel_local || !needed || !out_slots || !miss || !miss_count || !out)
     return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
+  if ((rc = check_vec16(q, "q")) || (rc = check_vec16(out, "out"))) return rc;
   if ((int64_t)B * c->C > c->cfg.max_width || (int64_t)B * c->C > c->cfg.num_slots)
     return fail(TKV_E_CAPACITY, "B*max_sel_pages=%lld exceeds num_slots or max_width", (long long)B * c->C);
   hipStream_t s = (hipStream_t)stream;
@@ -637,6 +647,7 @@ int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint
   if (n_runs < 1 || max_run_len < 1) return fail(TKV_E_INVALID_ARG, "n_runs=%d, max_run_len=%d must be >= 1", n_runs, max_run_len);
   if (!k || !v || !run_req || !run_start || !run_len || !run_tok_off || !block_table)
     return fail(TKV_E_INVALID_ARG, "a required pointer is NULL");
+  if ((rc = check_vec16(k, "k")) || (rc = check_vec16(v, "v"))) return rc;
   if (max_pages < 1 || max_pages > c->cfg.max_pages_per_req) return fail(TKV_E_INVALID_ARG, "max_pages out of range");
   StoreArgs a{};
   a.layer = layer; a.k = k; a.v = v; a.n_runs = n_runs; a.run_req = run_req; a.run_start = run_start;
