@@ -25,37 +25,40 @@ __device__ __forceinline__ void attn_merge_splits(const DevCtx& c, const AttnArg
   const int h = tid / 32, d0 = (tid % 32) * 4;
   const float* base = c.attn_part + ((size_t)r * c.Hq + g * G + h) * a.splits * REC;
   const int S = a.splits;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 16) {
-    float mv[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) mv[u] = (s0 + u < S) ? base[(size_t)(s0 + u) * REC + D] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) M = fmaxf(M, mv[u]);
-  }
-  float L = 0.f;
+  // one pass: a batch of up to 16 records (output slice, max, sum) is loaded
+  // at once and folded into a running max; up to 16 splits take one round
+  // trip to memory and the same arithmetic as a max pass followed by a sum
+  float M = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      float4 ov[16];
-      float2 ml[16];
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float4 ov[16];
+    float2 ml[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (s0 + u < S) {
-          const float* rec = base + (size_t)(s0 + u) * REC;
-          ov[u] = *reinterpret_cast<const float4*>(rec + d0);
-          ml[u] = *reinterpret_cast<const float2*>(rec + D);
-        } else {
-          ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-          ml[u] = make_float2(-INFINITY, 0.f);
-        }
+    for (int u = 0; u < 16; ++u) {
+      if (s0 + u < S) {
+        const float* rec = base + (size_t)(s0 + u) * REC;
+        ov[u] = *reinterpret_cast<const float4*>(rec + d0);
+        ml[u] = *reinterpret_cast<const float2*>(rec + D);
+      } else {
+        ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ml[u] = make_float2(-INFINITY, 0.f);
       }
+    }
+    float Mb = M;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float w = (ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
-        L += ml[u].y * w;
-        o.x += ov[u].x * w; o.y += ov[u].y * w; o.z += ov[u].z * w; o.w += ov[u].w * w;
-      }
+    for (int u = 0; u < 16; ++u) Mb = fmaxf(Mb, ml[u].x);
+    if (Mb == -INFINITY) continue;
+    if (M != -INFINITY && M != Mb) {
+      const float sc = exp2f(M - Mb);
+      L *= sc;
+      o.x *= sc; o.y *= sc; o.z *= sc; o.w *= sc;
+    }
+    M = Mb;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float w = (ml[u].x == -INFINITY) ? 0.f : exp2f(ml[u].x - M);
+      L += ml[u].y * w;
+      o.x += ov[u].x * w; o.y += ov[u].y * w; o.z += ov[u].z * w; o.w += ov[u].w * w;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
