@@ -14,7 +14,7 @@ per-page written-token counts are kept; the bytes of a page are rebuilt on
 demand by ``row_builder(page)`` -- the same ``write_tokens`` arithmetic
 applied to the page's tokens -- and a resident slot reads its page's mirror
 row, which is what the write-through mirror guarantees (PR #499 "Design":
-every GPU slot is drop-clean).
+a slot never holds bytes the mirror lacks, so dropping it loses nothing).
 """
 from __future__ import annotations
 
@@ -23,7 +23,8 @@ import numpy as np
 from .attention import attend
 from .layout import RowLayout
 from .lru import LRUState
-from .select import compact_request, select_row, select_rows
+from .select import (NO_BITS, ScoreCertificateError, compact_request, lowest_bit_exponent, select_row,
+                     select_rows)
 from .store import read_kv, slab_entry, write_tokens
 
 ERR_NOT_RESIDENT = 4      # store to a page that is not resident (pool not written)
@@ -31,6 +32,10 @@ ERR_NOT_RESIDENT = 4      # store to a page that is not resident (pool not writt
 
 class CapacityError(ValueError):
     pass
+
+
+class SlabCertificateError(ArithmeticError):
+    """A page's key sums cannot be proven exact in fp64."""
 
 
 class OracleTier:
@@ -46,19 +51,31 @@ class OracleTier:
                      if materialize else None)
         self._lazy_pool = {}                  # slot -> (page, row copied by the fetch)
         self.slab = np.zeros((self.L, self.N, self.Hkv, self.d), dtype=np.float32)
-        self._partial_sums = {}               # (layer, page) -> fp64 key sum of a partly written page
+        # (layer, page) -> (fp64 key sum, fp64 sum of |key|, lowest-bit exponent)
+        # of a partly written page; the last two certify the sum exact
+        self._partial_sums = {}
         self.written = np.zeros(self.N, dtype=np.int64)   # tokens written per page (layer 0)
         self.lru = LRUState(self.N, self.S)
         self.drops = 0
         self.bytes_fetched = 0
         self.bytes_mirrored = 0
         self.max_sel_pages = None
-        self.max_certificate = 0.0
+        self.max_certificate = 0.0            # largest sum |qg * slab| seen by select
+        self.max_score_bits = 0.0             # largest log2(A) - e_min seen by select
+        # Exactness of the selection scores is asserted on every select: the
+        # scores are fp32(exact dot product), and the certificate proves the
+        # fp64 sums exact and that an accumulator of `score_bits` significand
+        # bits reproduces them in any order -- 24 (fp32, the dense bf16
+        # product of a prefill chunk) for rows with a causal position, 53
+        # (fp64) for decode rows.  None switches the check off (inputs off the
+        # workloads' grids, compared by a bound instead of bit for bit).
+        self.check_scores = True
 
     # ------------------------------------------------------------ config --
     def set_select_width(self, max_bs, block_topk, max_sel_pages=0):
-        """PR #525 commit summary: the whole batch selection must fit the
-        physical pool by construction."""
+        """PR #525 commit summary (set_select_width takes the batch size): the
+        width is chosen so that a full batch's compacted selection always has
+        enough slots."""
         C = max_sel_pages if max_sel_pages > 0 else 2 * block_topk + 8
         if max_bs * C > self.S:
             raise CapacityError(f"max_bs*max_sel_pages={max_bs * C} > num_slots={self.S}")
@@ -98,8 +115,8 @@ class OracleTier:
         for p in pages:
             p = int(p)
             recs.append(dict(row=self.mirror_row(p).copy(), slab=self.slab[:, p].copy(),
-                             sums={l: self._partial_sums[(l, p)].copy() for l in range(self.L)
-                                   if (l, p) in self._partial_sums},
+                             sums={l: tuple(np.copy(x) for x in self._partial_sums[(l, p)])
+                                   for l in range(self.L) if (l, p) in self._partial_sums},
                              written=int(self.written[p])))
         return recs
 
@@ -119,7 +136,7 @@ class OracleTier:
             for l in range(self.L):
                 self._partial_sums.pop((l, p), None)
             for l, v in r["sums"].items():
-                self._partial_sums[(l, p)] = v.copy()
+                self._partial_sums[(l, p)] = tuple(np.copy(x) for x in v)
             self.written[p] = r["written"]
             self.lru.unbind(p)
 
@@ -163,10 +180,15 @@ class OracleTier:
                 # slab: mean of all written keys of the page
                 key = (layer, page)
                 prev = self._partial_sums.pop(key, None) if a > 0 else None
-                s = kk.astype(np.float64).sum(axis=0) + (0.0 if prev is None else prev)
+                s = kk.astype(np.float64).sum(axis=0)
+                sabs = np.abs(kk.astype(np.float64)).sum(axis=0)
+                lsb = lowest_bit_exponent(kk, axis=0)
+                if prev is not None:
+                    s, sabs, lsb = s + prev[0], sabs + prev[1], np.minimum(lsb, prev[2])
+                self._certify_slab(sabs, lsb, layer, page)
                 cnt = a + n
                 if cnt < self.ps:
-                    self._partial_sums[key] = s
+                    self._partial_sums[key] = (s, sabs, lsb)
                 self.slab[layer, page] = slab_entry_from_sum(s, cnt)
                 if layer == 0:
                     self.written[page] = cnt
@@ -181,25 +203,44 @@ class OracleTier:
         B = len(n_pages)
         rows = q.shape[0]
         sel = np.full((rows, topk), -1, dtype=np.int32)
+        need = 24 if row_pos is not None else 53
         for b in range(B):
             r0, r1 = int(row_start[b]), int(row_start[b + 1])
             if r1 - r0 > 8:
                 pos = None if row_pos is None else np.asarray(row_pos[r0:r1])
                 sel[r0:r1], cert = select_rows(q[r0:r1], self.slab[layer], block_table[b], int(n_pages[b]),
                                                topk, self.Hkv, bias, pos, self.ps)
-                self.max_certificate = max(self.max_certificate, cert)
+                self._certify(cert, need, layer, b)
                 continue
             for r in range(r0, r1):
                 pos = None if row_pos is None else int(row_pos[r])
                 sel[r], cert = select_row(q[r], self.slab[layer], block_table[b], int(n_pages[b]),
                                           topk, self.Hkv, bias, pos, self.ps)
-                self.max_certificate = max(self.max_certificate, cert)
+                self._certify(cert, need, layer, b)
         C = self.max_sel_pages
         needed = np.full((B, C), -1, dtype=np.int32)
         for b in range(B):
             needed[b], drops = compact_request(sel[row_start[b]:row_start[b + 1]], block_table[b], C)
             self.drops += drops
         return sel, needed
+
+    def _certify_slab(self, sabs, lsb, layer, page):
+        """Every key of the page (per feature) is a multiple of 2^lsb and the
+        partial sums stay below sum |key|, so the fp64 sums -- in any order,
+        the oracle's and an fp64 accumulator's alike -- are exact when
+        sum |key| < 2^(53 + lsb)."""
+        live = lsb < NO_BITS
+        if np.any(live & (sabs >= np.ldexp(1.0, np.minimum(53 + lsb, 1000)))):
+            raise SlabCertificateError(f"layer {layer}, page {page}: the key sums are not exact in fp64")
+
+    def _certify(self, cert, need_bits, layer, b):
+        A, bits = cert
+        self.max_certificate = max(self.max_certificate, A)
+        self.max_score_bits = max(self.max_score_bits, bits)
+        if self.check_scores and bits >= need_bits:
+            raise ScoreCertificateError(
+                f"layer {layer}, request {b}: the score sums need {bits:.1f} significand bits "
+                f"(sum |qg*slab| = {A:.6g}); exact selection needs < {need_bits}")
 
     def ensure(self, needed, no_fetch=None):
         return self.lru.ensure(np.asarray(needed).reshape(-1), no_fetch)
@@ -303,4 +344,5 @@ def slab_entry_from_sum(s: np.ndarray, n: int) -> np.ndarray:
     return bf16_round(s.astype(np.float32) / np.float32(n))
 
 
-__all__ = ["OracleTier", "CapacityError", "slab_entry", "slab_entry_from_sum"]
+__all__ = ["OracleTier", "CapacityError", "ScoreCertificateError", "SlabCertificateError", "slab_entry",
+           "slab_entry_from_sum"]

@@ -1,6 +1,6 @@
 """Byte layout of one logical page's row, shared by the host mirror and a GPU
 pool slot (they must hold identical bytes: FreeToken PR #499, "Design", the
-write-through mirror makes every GPU slot drop-clean).
+write-through mirror means no slot ever holds bytes the mirror lacks).
 
 One row holds the page for ALL layers (PR #499 "Design": one copy moves K+V
 of a page across all layers; PR #525 commit summary: the copy descriptor

@@ -19,11 +19,17 @@ Readings where the page is silent (each listed in the design notes):
 * prefill rows see page i iff page_size * i <= their position;
 * the cap keeps the lowest local page ids and counts the rest as drops.
 
-Scores are summed in fp64, where every product of two bfloat16 values and
-every partial sum of a few hundred of them is exact for the input grids the
-workloads use; ``score_certificate`` reports the quantity that makes the fp32
-sum exact in ANY order (all products on the 2^-15 grid and sum |products| <
-2^9), which the GPU needs for bit-exact selections.
+The score is the exact dot product rounded once to fp32.  The oracle sums
+it in fp64 and proves the sum exact with a certificate: every product of two
+bfloat16 values is a multiple of 2^e, e = (lowest set bit of the query
+element) + (lowest set bit of the slab element), so with e_min the smallest
+such exponent of a page and A = sum |qg * slab|, every partial sum -- in ANY
+order -- is a multiple of 2^e_min no larger than A, hence exact in a float
+with b significand bits whenever A < 2^(b + e_min).  ``score_bits`` is
+log2(A) - e_min per (row, page): below 53 the fp64 sum (and any fp64
+accumulation) is exact; below 24 any fp32 accumulation is too, whatever its
+order (a matrix-core product included).  On the workloads' input grids (keys
+on 2^-4, queries on 2^-5, so products on 2^-15) A < 2^9 gives < 24 bits.
 """
 from __future__ import annotations
 
@@ -46,8 +52,51 @@ def page_scores(qg: np.ndarray, slab_pages: np.ndarray) -> np.ndarray:
     return np.einsum("gd,pgd->p", qg.astype(np.float64), slab_pages.astype(np.float64))
 
 
+class ScoreCertificateError(ArithmeticError):
+    """The inputs do not let the score sums be proven exact at the required
+    accumulator width."""
+
+
+NO_BITS = 10 ** 6   # lowest-set-bit exponent of an all-zero vector (never the minimum)
+
+
+def lowest_bit_exponent(x: np.ndarray, axis=-1) -> np.ndarray:
+    """Per vector along ``axis``: the smallest e such that some element has
+    its lowest set bit at 2^e (every element is then a multiple of 2^e).
+    Elements are fp32 values (bf16 values included); zeros are ignored; an
+    all-zero vector gives NO_BITS."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    expf = ((u >> 23) & 0xFF).astype(np.int64)
+    man = (u & 0x7FFFFF).astype(np.int64)
+    man = np.where(expf > 0, man | 0x800000, man)          # implicit bit of normal numbers
+    base = np.where(expf > 0, expf - 150, -149)             # exponent of the mantissa's last bit
+    tz = np.zeros_like(man)
+    rest = man.copy()
+    for sh in (16, 8, 4, 2, 1):                             # count trailing zeros
+        low = (rest & ((1 << sh) - 1)) == 0
+        move = low & (rest != 0)
+        tz += np.where(move, sh, 0)
+        rest = np.where(move, rest >> sh, rest)
+    e = np.where(man != 0, base + tz, NO_BITS)
+    return e.min(axis=axis)
+
+
+def score_bits(qg: np.ndarray, slab_pages: np.ndarray) -> np.ndarray:
+    """Significand bits an accumulator needs for the scores of qg [Hkv][d]
+    against slab_pages [P][Hkv][d] to be exact in any order: log2(A) - e_min
+    per page (0 for a page whose products are all zero)."""
+    P = slab_pages.shape[0]
+    qf = qg.reshape(-1)
+    sf = slab_pages.reshape(P, -1)
+    A = np.abs(sf).astype(np.float64) @ np.abs(qf).astype(np.float64)
+    e_min = lowest_bit_exponent(qf) + lowest_bit_exponent(sf, axis=1)
+    with np.errstate(divide="ignore"):
+        bits = np.where(A > 0, np.log2(A * (1 + 2.0 ** -30)) - e_min, 0.0)
+    return bits
+
+
 def score_certificate(qg: np.ndarray, slab_pages: np.ndarray) -> float:
-    """max over pages of sum |qg * slab| (exactness needs < 2^9 on the grids)."""
+    """max over pages of sum |qg * slab| (on the workloads' grids: < 2^9)."""
     a = np.einsum("gd,pgd->p", np.abs(qg.astype(np.float64)), np.abs(slab_pages.astype(np.float64)))
     return float(a.max()) if a.size else 0.0
 
@@ -72,8 +121,10 @@ def topk_pages(keys: np.ndarray, visible: int, k: int) -> np.ndarray:
 
 def select_row(q_row: np.ndarray, slab_layer: np.ndarray, block_row: np.ndarray,
                n_pages: int, k: int, num_kv_heads: int, bias=None, row_pos=None,
-               page_size: int = 64):
-    """One query row: returns (sel_local int32 [k], certificate).
+               page_size: int = 64, with_keys: bool = False):
+    """One query row: returns (sel_local int32 [k], certificate) where the
+    certificate is (max sum |qg*slab|, max score bits) over the visible pages;
+    with ``with_keys`` also the fp32 keys of the visible pages.
 
     slab_layer float32 [N][Hkv][d] indexed by logical page id; block_row maps
     local -> logical page id."""
@@ -84,21 +135,36 @@ def select_row(q_row: np.ndarray, slab_layer: np.ndarray, block_row: np.ndarray,
     scores = page_scores(qg, slab_pages)
     bias_pages = None if bias is None else bias[logical]
     keys = keys_from_scores(scores, bias_pages)
-    return topk_pages(keys, visible, k), score_certificate(qg, slab_pages)
+    bits = score_bits(qg, slab_pages)
+    cert = (score_certificate(qg, slab_pages), float(bits.max()) if bits.size else 0.0)
+    sel = topk_pages(keys, visible, k)
+    return (sel, cert, keys) if with_keys else (sel, cert)
 
 
 def select_rows(q_rows: np.ndarray, slab_layer: np.ndarray, block_row: np.ndarray, n_pages: int,
                 k: int, num_kv_heads: int, bias=None, row_pos=None, page_size: int = 64):
     """Many rows of one request: the same definition as ``select_row``, with
     the scores of all rows against all pages as one fp64 matrix product.
-    Returns (sel_local int32 [rows][k], certificate)."""
+    Returns (sel_local int32 [rows][k], certificate) with the certificate as
+    in ``select_row``, over every row's visible pages."""
     rows = q_rows.shape[0]
     qg = np.stack([group_query(q_rows[r], num_kv_heads) for r in range(rows)])   # [rows][Hkv][d]
     logical = block_row[:n_pages].astype(np.int64)
-    slab_pages = slab_layer[logical].astype(np.float64).reshape(n_pages, -1)
+    slab32 = slab_layer[logical].reshape(n_pages, -1)
+    slab_pages = slab32.astype(np.float64)
     qmat = qg.astype(np.float64).reshape(rows, -1)
-    scores = qmat @ slab_pages.T                                                   # exact on the grids
-    cert = float((np.abs(qmat) @ np.abs(slab_pages).T).max()) if n_pages else 0.0
+    scores = qmat @ slab_pages.T                                   # exact while the certificate holds
+    A = np.abs(qmat) @ np.abs(slab_pages).T
+    e_min = (lowest_bit_exponent(qg.reshape(rows, -1), axis=1)[:, None]
+             + lowest_bit_exponent(slab32, axis=1)[None, :])
+    with np.errstate(divide="ignore"):
+        bits = np.where(A > 0, np.log2(A * (1 + 2.0 ** -30)) - e_min, 0.0)
+    if row_pos is not None:   # only the pages a row sees count
+        vis = np.minimum(n_pages, np.asarray(row_pos, dtype=np.int64) // page_size + 1)
+        seen = np.arange(n_pages)[None, :] < vis[:, None]
+        A = np.where(seen, A, 0.0)
+        bits = np.where(seen, bits, 0.0)
+    cert = (float(A.max()) if A.size else 0.0, float(bits.max()) if bits.size else 0.0)
     bias_pages = None if bias is None else bias[logical]
     out = np.full((rows, k), -1, dtype=np.int32)
     for r in range(rows):

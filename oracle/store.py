@@ -7,9 +7,10 @@ Per token and per tensor (K, V) over all Hkv*d values:
     scale = fp32(amax / 448)        (1.0 when amax == 0)
     code  = e4m3(fp32(x / scale))   (one correctly rounded fp32 division)
 
-The mirror receives the codes and scales read AFTER quantisation, i.e. the
-same bytes the pool holds (PR #525: the pool is the source of truth; a
-mirror of the pre-quantisation values silently corrupted fp8 pages).  For a
+The mirror receives the quantiser's output -- codes and scales, the same
+bytes the pool holds (PR #525 commit summary, mirror_store_quant: an earlier
+mirror that kept the values from before quantisation left fp8 pages wrong
+with no error raised).  For a
 bf16 cache the bf16 values are stored verbatim and there are no scales.
 
 The indexer slab entry of a page is the mean of its written bf16 keys,
@@ -69,7 +70,8 @@ def write_tokens(row: np.ndarray, lay: RowLayout, layer: int, off: int,
 
 def slab_entry(k_written: np.ndarray) -> np.ndarray:
     """Mean of a page's written keys, k_written float32 [n][Hkv][d] -> float32
-    [Hkv][d] holding bf16 values."""
+    [Hkv][d] holding bf16 values: bf16(fp32(exact sum) / n).  The fp64 sum is
+    exact for the keys the tier certifies (see OracleTier._certify_slab)."""
     n = k_written.shape[0]
     s = k_written.astype(np.float64).sum(axis=0).astype(np.float32)
     return bf16_round(s / np.float32(n))

@@ -180,3 +180,40 @@ def test_free_slots_first_lowest_index_then_least_recent():
     lru.ensure(np.array([5]))                 # 5 (slot 0) refreshed
     _, m = lru.ensure(np.array([8, 9]))       # victims: slot 1 (page 6, stamp 1), slot 2 (page 7, stamp 2)
     assert m.tolist() == [[1, 8], [2, 9]] and lru.counters["evictions"] == 2
+
+
+# ------------------------------------------------------------------ unbind --
+def _unbind_trace(state_cls):
+    """Hand trace, 2 slots, pages 0..3 (one clock tick per call):
+      ensure [0] -> clock 1: page 0 takes slot 0 (free slots, lowest first)
+      ensure [1] -> clock 2: page 1 takes slot 1
+      unbind 1   -> slot 1 empty, keeps stamp 2 (its place in the order)
+      ensure [2] -> clock 3: candidates by (stamp, slot): slot 0 (1), slot 1 (2):
+                    page 2 takes slot 0 and evicts page 0
+      ensure [3] -> clock 4: slot 1 (2) before slot 0 (3): page 3 takes the
+                    empty slot 1, nothing evicted
+    Returns whether the final state is exactly that."""
+    st = state_cls(4, 2)
+    st.ensure([0])
+    st.ensure([1])
+    st.unbind(1)
+    st.ensure([2])
+    st.ensure([3])
+    return (list(st.page_to_slot) == [-1, -1, 0, 1] and list(st.slot_to_page) == [2, 3]
+            and list(st.stamp) == [3, 4] and st.counters["evictions"] == 1 and st.counters["misses"] == 4)
+
+
+class _StampResetLRU(LRUState):
+    """A plausible wrong unbind: the emptied slot goes back to stamp 0
+    (first in line, like a never-used slot)."""
+
+    def unbind(self, page):
+        s = int(self.page_to_slot[page])
+        super().unbind(page)
+        if s >= 0:
+            self.stamp[s] = 0
+
+
+def test_unbind_keeps_the_slots_recency():
+    assert _unbind_trace(LRUState)
+    assert not _unbind_trace(_StampResetLRU)

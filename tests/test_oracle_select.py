@@ -137,3 +137,131 @@ def test_batched_rows_equal_single_rows():
     for r in range(20):
         exp, _ = select_row(q[r], slab, bt, 90, 7, 4, bias=bias, row_pos=int(pos[r]))
         assert np.array_equal(got[r], exp)
+
+
+# ------------------------------------------------------- group sum rounding --
+def _group_rounds_once(fn):
+    """Hand case: heads 1, 2^-8, 2^-8 (others 0).  Exact sum 1 + 2^-7 is a
+    bf16 value, so one rounding keeps it; rounding after each head gives
+    1 + 2^-8 -> 1 (a tie, to even) and then 1 again."""
+    q = np.zeros((8, 4), dtype=np.float32)
+    q[0, :] = 1.0
+    q[1, :] = 2.0 ** -8
+    q[2, :] = 2.0 ** -8
+    qg = fn(q, 1)
+    return bool(np.all(qg == np.float32(1.0 + 2.0 ** -7)))
+
+
+def _group_query_per_head_rounding(q, num_kv_heads):
+    """A plausible wrong group sum: bf16 rounding after every head."""
+    from oracle.codecs import bf16_round
+    Hq, d = q.shape
+    G = Hq // num_kv_heads
+    acc = np.zeros((num_kv_heads, d), dtype=np.float32)
+    for h in range(G):
+        acc = bf16_round((acc + q.reshape(num_kv_heads, G, d)[:, h]).astype(np.float32))
+    return acc
+
+
+def test_group_query_rounds_the_exact_sum_once():
+    assert _group_rounds_once(group_query)
+    assert not _group_rounds_once(_group_query_per_head_rounding)
+
+
+def test_group_rounding_decides_a_selection():
+    """The same hand case through select_row (one KV group of 8 heads):
+    qg[0] = 1 + 2^-7 (exact sum) and qg[1] = 1.  Page 1's slab row is
+    (+1, -1, 0, ...), so it scores qg[0] - qg[1] = 2^-7; page 0's is
+    (0, 2^-8, 0, ...), scoring 2^-8.  Top-1 is page 1.  With per-head
+    rounding qg[0] would be 1, page 1 would score 0 and page 0 would win."""
+    q = np.zeros((8, 128), dtype=np.float32)
+    q[0, 0] = 1.0
+    q[1, 0] = 2.0 ** -8
+    q[2, 0] = 2.0 ** -8
+    q[3, 1] = 1.0
+    slab = np.zeros((2, 1, 128), dtype=np.float32)
+    slab[0, 0, 1] = 2.0 ** -8
+    slab[1, 0, 0] = 1.0
+    slab[1, 0, 1] = -1.0
+    bt = np.arange(2, dtype=np.int32)
+    sel, _ = select_row(q, slab, bt, 2, 1, 1)
+    assert list(sel) == [1]
+    bad = page_scores(_group_query_per_head_rounding(q, 1), slab)
+    assert bad[0] == 2.0 ** -8 and bad[1] == 0.0
+
+
+# ----------------------------------------------------------- certificate --
+def test_certificate_bits_on_the_grids_match_the_sum_bound():
+    """On the workload grids (products on 2^-15) the bits needed are
+    log2(sum |qg*slab|) + 15 or fewer (the data may sit on a coarser grid)."""
+    from oracle.select import score_bits, score_certificate
+    slab = _slab(40, seed=5)
+    qg = group_query(_q(seed=6), 4)
+    bits = score_bits(qg, slab)
+    A = score_certificate(qg, slab)
+    assert bits.max() <= np.log2(A) + 15 + 1e-6
+    assert bits.max() < 24
+
+
+def test_certificate_is_exactness_for_a_brute_force_sum():
+    """Where the certificate says < 24 bits, fp32 sums in random orders all
+    equal fp32 of the exact (integer) sum; an input needing more bits has an
+    order whose fp32 sum differs."""
+    from oracle.select import score_bits
+    rng = np.random.default_rng(12)
+    qg = np.zeros((1, 128), dtype=np.float32)
+    qg[0] = _q(Hq=1, seed=13)[0]
+    slab = _slab(1, H=1, seed=14)
+    assert score_bits(qg, slab)[0] < 24
+    prods = (qg[0] * slab[0, 0]).astype(np.float32)
+    ref = np.float32(sum(int(v * 2 ** 15) for v in prods.astype(np.float64)) / 2.0 ** 15)
+    for _ in range(50):
+        acc = np.float32(0)
+        for v in prods[rng.permutation(128)]:
+            acc = np.float32(acc + v)
+        assert acc == ref
+    # 2^20 and 2^-10 side by side need 31 bits: some order loses the small terms
+    wide = np.zeros((1, 1, 4), dtype=np.float32)
+    wide[0, 0] = [2.0 ** 20, 2.0 ** -10, 2.0 ** -10, -(2.0 ** 20)]
+    one = np.ones((1, 4), dtype=np.float32)
+    assert score_bits(one, wide)[0] >= 24
+    a = np.float32(0)
+    for v in wide[0, 0]:
+        a = np.float32(a + v)
+    assert a != np.float32(2.0 ** -9)
+
+
+def test_select_asserts_the_certificate_for_chunk_rows():
+    """Off-grid queries and slab (general bf16 values) need more than fp32's
+    24 bits for exact chunk scores: select with causal rows raises; decode
+    rows (fp64, 53 bits) pass on the same data."""
+    from oracle.codecs import bf16_round
+    from oracle.select import ScoreCertificateError
+    rng = np.random.default_rng(21)
+    t = OracleTier(num_layers=1, num_q_heads=32, num_kv_heads=4, head_dim=128, page_size=64, fp8=True,
+                   num_logical_pages=16, num_slots=16)
+    t.set_select_width(1, 4)
+    t.slab[0] = bf16_round((rng.standard_normal((16, 4, 128)) / 8).astype(np.float32))
+    q = bf16_round(rng.standard_normal((1, 32, 128)).astype(np.float32))
+    bt = np.arange(16, dtype=np.int32)[None, :]
+    rs = np.array([0, 1])
+    t.select(0, q, rs, None, bt, np.array([16]), 4)          # decode: fine
+    assert 24 <= t.max_score_bits < 53
+    with pytest.raises(ScoreCertificateError):
+        t.select(0, q, rs, np.array([64 * 16 - 1]), bt, np.array([16]), 4)
+    t.check_scores = False
+    t.select(0, q, rs, np.array([64 * 16 - 1]), bt, np.array([16]), 4)
+
+
+def test_select_certificate_holds_on_the_workload_grids():
+    from workload import get_workload
+    from oracle.run import make_tier, setup
+    wl = get_workload("c2s")
+    t = make_tier(wl, materialize=False)
+    setup(wl, t)
+    from workload import gen
+    bt, npg = gen.block_tables(wl)
+    q = gen.decode_queries(wl)[0, 0]
+    t.set_select_width(wl.batch, wl.topk)
+    t.select(0, q, np.arange(wl.batch + 1), None, bt, npg, wl.topk)
+    assert t.max_score_bits < 24 and t.max_certificate < 2 ** 9

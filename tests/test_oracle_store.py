@@ -118,3 +118,105 @@ def test_fp8_value_codes_are_stored_transposed():
     # 448 * fp32(amax / 448) recovers amax to one fp32 rounding of the scale
     assert abs(vr[1, 5, 77] - 3.0) < 1e-6 and abs(kr[0, 2, 9] + 2.0) < 1e-6
     assert np.count_nonzero(vr) == 1 and np.count_nonzero(kr) == 1
+
+
+# ---------------------------------------------------------------- golden tokens --
+import json as _json
+import os as _os
+
+_QGOLD = _os.path.join(_os.path.dirname(__file__), "golden", "quant_tokens.json")
+
+
+def _golden_tokens():
+    doc = _json.load(open(_QGOLD))
+    toks = []
+    for t in doc["tokens"]:
+        xb = np.array([int(b, 16) for b in t["x_bf16_bits"]], dtype=np.uint32) << 16
+        x = xb.view(np.float32).reshape(1, 1, -1)
+        toks.append((x, int(t["scale_f32_bits"], 16), [int(c, 16) for c in t["codes"]],
+                     int(t["reciprocal_form_scale_f32_bits"], 16), [int(c, 16) for c in t["reciprocal_form_codes"]]))
+    return toks
+
+
+def _quant_matches_golden(quant_fn):
+    """True when `quant_fn` reproduces every golden token's scale bits and codes."""
+    for x, sbits, codes, _, _ in _golden_tokens():
+        c, s = quant_fn(x)
+        if int(np.asarray(s, dtype=np.float32).view(np.uint32)[0]) != sbits:
+            return False
+        if [int(v) for v in np.asarray(c).reshape(-1)] != codes:
+            return False
+    return True
+
+
+def _quant_reciprocal_form(x):
+    """A plausible wrong quantiser: scale = amax * fp32(1/448) and codes from
+    x * fp32(1/scale) -- two roundings where the definition has one."""
+    from oracle.codecs import e4m3_encode
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[0]
+    amax = np.abs(x.reshape(n, -1)).max(axis=1).astype(np.float32)
+    scale = np.where(amax == 0, np.float32(1), amax * (np.float32(1) / np.float32(448))).astype(np.float32)
+    inv = (np.float32(1) / scale).astype(np.float32)
+    return e4m3_encode((x * inv[:, None, None]).astype(np.float32)), scale
+
+
+def test_quantiser_matches_golden_tokens():
+    """Scale bits and codes of hand-picked tokens, computed with exact
+    rationals from the definition (tests/golden/make_quant_golden.py)."""
+    assert _quant_matches_golden(quantize_tokens)
+
+
+def test_golden_tokens_separate_the_reciprocal_form():
+    """The tokens pin the single-rounding definition: the reciprocal-multiply
+    quantiser gets different scales and codes on them (checked both against
+    the generator's own record of that form and by running it)."""
+    toks = _golden_tokens()
+    assert any(t[1] != t[3] for t in toks) and any(t[2] != t[4] for t in toks)
+    for x, _, _, rs, rc in toks:
+        c, s = _quant_reciprocal_form(x)
+        assert int(s.view(np.uint32)[0]) == rs and [int(v) for v in c.reshape(-1)] == rc
+    assert not _quant_matches_golden(_quant_reciprocal_form)
+
+
+def test_slab_mean_off_grid_is_one_rounding_of_the_exact_sum():
+    """General bf16 keys (not on a grid): the slab entry is bf16(fp32(exact
+    sum) / n); the exact sum is taken with Python fractions."""
+    from fractions import Fraction
+    from oracle.codecs import bf16_round
+    rng = np.random.default_rng(11)
+    k = bf16_round(rng.standard_normal((64, 2, 16)).astype(np.float32))
+    got = slab_entry(k)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_quant_golden", _os.path.join(_os.path.dirname(__file__), "golden", "make_quant_golden.py"))
+    exact_fp = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(exact_fp)
+    for h in range(2):
+        for d in range(16):
+            exact = sum(Fraction(float(v)) for v in k[:, h, d])
+            f32 = np.uint32(exact_fp.f32_bits(exact)).view(np.float32)      # one RNE rounding to fp32
+            mean = np.uint32(exact_fp.f32_bits(Fraction(float(f32)) / 64)).view(np.float32)
+            exp = bf16_round(np.array([mean], dtype=np.float32))[0]
+            assert got[h, d] == exp
+
+
+def test_slab_certificate_trips_on_keys_too_wide_for_fp64():
+    """The tier refuses to store a page whose fp64 key sums it cannot prove
+    exact (a key of 2^100 beside one of 2^-100 in the same feature)."""
+    import pytest
+    from oracle.engine import OracleTier, SlabCertificateError
+    t = OracleTier(num_layers=1, num_q_heads=8, num_kv_heads=1, head_dim=128, page_size=16, fp8=False,
+                   num_logical_pages=4, num_slots=4)
+    bt = np.arange(4, dtype=np.int32)[None, :]
+    t.ensure_write_pages([(0, 0, 16)], bt, [0])
+    k = np.zeros((16, 1, 128), dtype=np.float32)
+    k[0, 0, 0] = 2.0 ** 100
+    k[1, 0, 0] = 2.0 ** -100
+    with pytest.raises(SlabCertificateError):
+        t.store(0, [(0, 0, 16)], k, k, bt)
+    # N(0,1) keys in bf16 pass
+    rng = np.random.default_rng(3)
+    from oracle.codecs import bf16_round
+    k = bf16_round(rng.standard_normal((16, 1, 128)).astype(np.float32))
+    t.store(0, [(0, 0, 16)], k, k, bt)

@@ -72,3 +72,31 @@ def test_zipf_bias():
     bias = gen.page_bias(wl)
     assert bias.shape == (3072,) and bias.max() == 0.0
     assert np.isclose(np.sort(bias)[0], np.float32(-1.1 * np.log(3072)))
+
+
+def test_bf16_table_is_nearest_bf16_of_the_normal_quantiles():
+    """Off-grid mode: each entry is the bf16 value nearest Phi^-1((u+.5)/65536)
+    (ties to even), checked against a brute-force neighbour search."""
+    from statistics import NormalDist
+    tab = gen.bf16_table()
+    nd = NormalDist()
+    for u in (0, 1, 777, 32767, 32768, 40000, 65535):
+        x = nd.inv_cdf((u + 0.5) / 65536.0)
+        got = float((np.uint32(tab[u]) << 16).view(np.float32))
+        f32 = np.float32(x)
+        bits = int(f32.view(np.uint32)) >> 16
+        cands = [float((np.uint32(b) << 16).view(np.float32)) for b in (bits - 1, bits, bits + 1)]
+        best = min(cands, key=lambda c: abs(c - float(f32)))
+        assert got == best
+    v = (tab.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert abs(v.std() - 1.0) < 0.01 and np.array_equal(v, -v[::-1])
+
+
+def test_offgrid_workload_values_are_bf16_not_on_the_grid():
+    wl = get_workload("c2s_bf16")
+    k = gen.kv_page(wl, gen.KIND_K, 0, 0, 3)
+    gen.to_bf16_bits(k)
+    assert np.any(np.mod(k * 16, 1) != 0)
+    q = gen.decode_queries(wl)
+    gen.to_bf16_bits(q)
+    assert np.any(np.mod(q * 32, 1) != 0)

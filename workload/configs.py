@@ -32,6 +32,7 @@ class Workload:
     prefill_tokens: int = 0   # >0: one prefill chunk of this many new tokens
     append: bool = False      # decode steps append one token per request
     zipf_s: float = 1.1
+    values: str = "grid"      # "grid": N(0,1) on the 2^-4 / 2^-5 grids; "bf16": N(0,1) rounded to bf16
     description: str = field(default="", compare=False)
 
     # ---- derived sizes (plain arithmetic on the fields above) ----
@@ -115,6 +116,14 @@ WORKLOADS.update({
                     num_slots=288, num_layers=3, steps=5, setup_chunk=2048, topk=8, query="iid"),
     "c5s": replace(WORKLOADS["c5"], name="c5_small_prefill", contexts=(4096,), prefill_tokens=512,
                    num_slots=160, num_layers=2, setup_chunk=2048, topk=8),
+})
+
+# The same structure with general bf16 inputs: keys, values and queries are
+# N(0,1) rounded to bfloat16 (no grid), as the configs describe them.
+WORKLOADS.update({
+    "c2s_bf16": replace(WORKLOADS["c2s"], name="c2_small_offgrid", values="bf16"),
+    "c3s_bf16": replace(WORKLOADS["c3s"], name="c3_small_thrash_offgrid", values="bf16"),
+    "c5s_bf16": replace(WORKLOADS["c5s"], name="c5_small_prefill_offgrid", values="bf16"),
 })
 
 # Decode with one appended token per request per step (the new token's K/V

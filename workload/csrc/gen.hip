@@ -25,6 +25,8 @@ __device__ __forceinline__ u64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_
 }
 
 // Tokens [start, start+count) of one request in one layer, bf16 [count][H][D].
+// exp2neg >= 0: the table holds grid integers m, value m * 2^-exp2neg;
+// exp2neg < 0: the table holds the bf16 bit patterns themselves.
 // Block b of `block_tokens` tokens uses key (seed<<16 | kind, layer<<48 | req<<32 | b);
 // within a block the i-th 16-bit uniform is half (i%4) of 64-bit word (i/4)%4 of
 // Philox(counter = i/16 + 1).
@@ -52,8 +54,12 @@ __global__ void k_gen_tokens(uint16_t* out, const int16_t* table, int exp2neg, u
         const int64_t vi = first + w * 4 + h;
         if (vi < lo || vi >= hi) continue;
         const uint32_t u = (uint32_t)(r.v[w] >> (16 * h)) & 0xFFFFu;
-        const float x = (float)table[u] * scale;
-        out[vi - lo] = (uint16_t)(__float_as_uint(x) >> 16);
+        if (exp2neg < 0) {
+          out[vi - lo] = (uint16_t)table[u];
+        } else {
+          const float x = (float)table[u] * scale;
+          out[vi - lo] = (uint16_t)(__float_as_uint(x) >> 16);
+        }
       }
   }
 }

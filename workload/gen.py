@@ -20,6 +20,11 @@ Every such value is exactly representable in bfloat16.  The grids make the
 indexer's fp32 dot products exact in any summation order, which is what lets
 the GPU's page selection be compared bit for bit with the oracle's.
 
+A workload with ``values == "bf16"`` draws the same uniforms but maps them to
+``bf16(Phi^-1((u + .5) / 65536))`` (round to nearest even): general bf16
+N(0,1) values, no grid; its decode queries are the same processes rounded to
+bf16 instead of to the query grid.
+
 Decode queries are small and drawn on the host from ``default_rng``: either
 i.i.d. N(0,1) per step, or the AR(1) process ``q_t = (0.9 q_{t-1} + 0.1 n_t)
 / sqrt(0.82)`` (variance preserving) kept in fp64 and emitted on the query
@@ -54,6 +59,22 @@ def kv_table() -> np.ndarray:
     return _inv_normal_grid(16, 64)
 
 
+def _bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of finite fp32 values, round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@lru_cache(maxsize=None)
+def bf16_table() -> np.ndarray:
+    """uint16[65536]: bf16 bit patterns of Phi^-1((u + .5) / 65536)."""
+    nd = NormalDist()
+    vals = np.array([nd.inv_cdf((i + 0.5) / 65536.0) for i in range(65536)], dtype=np.float64)
+    t = _bf16_rne_bits(vals.astype(np.float32))
+    t.setflags(write=False)
+    return t
+
+
 def q_table() -> np.ndarray:
     """int16[65536]: grid integer for prefill queries (value = m / 32)."""
     return _inv_normal_grid(32, 128)
@@ -65,19 +86,28 @@ def philox_key(kind: int, seed: int, layer: int, req: int, block: int) -> np.nda
     return np.array([k0, k1], dtype=np.uint64)
 
 
+def block_uniforms(kind: int, seed: int, layer: int, req: int, block: int, n: int) -> np.ndarray:
+    """The n 16-bit uniforms of one block."""
+    assert n % 4 == 0
+    bg = np.random.Philox(key=philox_key(kind, seed, layer, req, block))
+    return bg.random_raw(n // 4).astype("<u8").view("<u2")
+
+
 def block_ints(kind: int, seed: int, layer: int, req: int, block: int,
                block_tokens: int, heads: int, dim: int) -> np.ndarray:
     """Grid integers of one block, int16 [block_tokens][heads][dim]."""
-    n = block_tokens * heads * dim
-    assert n % 4 == 0
-    bg = np.random.Philox(key=philox_key(kind, seed, layer, req, block))
-    u = bg.random_raw(n // 4).astype("<u8").view("<u2")
+    u = block_uniforms(kind, seed, layer, req, block, block_tokens * heads * dim)
     tab = q_table() if kind == KIND_Q else kv_table()
     return np.take(tab, u).reshape(block_tokens, heads, dim)
 
 
-def block_values(kind, seed, layer, req, block, block_tokens, heads, dim) -> np.ndarray:
-    """float32 values of one block (exact: small integers times a power of two)."""
+def block_values(kind, seed, layer, req, block, block_tokens, heads, dim, values="grid") -> np.ndarray:
+    """float32 values of one block: grid integers times a power of two, or
+    (values == "bf16") the bf16 table's values; exact in bf16 either way."""
+    if values == "bf16":
+        u = block_uniforms(kind, seed, layer, req, block, block_tokens * heads * dim)
+        bits = np.take(bf16_table(), u).astype(np.uint32) << 16
+        return bits.view(np.float32).reshape(block_tokens, heads, dim)
     e = Q_EXP if kind == KIND_Q else KV_EXP
     m = block_ints(kind, seed, layer, req, block, block_tokens, heads, dim)
     return m.astype(np.float32) * np.float32(2.0 ** -e)
@@ -86,7 +116,7 @@ def block_values(kind, seed, layer, req, block, block_tokens, heads, dim) -> np.
 def kv_page(wl: Workload, kind: int, layer: int, req: int, page: int) -> np.ndarray:
     """Keys (kind 0) or values (kind 1) of one page: float32 [page_size][Hkv][d]."""
     return block_values(kind, wl.seed, layer, req, page, wl.page_size,
-                        wl.num_kv_heads, wl.head_dim)
+                        wl.num_kv_heads, wl.head_dim, wl.values)
 
 
 def kv_tokens(wl: Workload, kind: int, layer: int, req: int, start: int, count: int) -> np.ndarray:
@@ -104,7 +134,7 @@ def prefill_queries(wl: Workload, layer: int, start: int, count: int) -> np.ndar
     chunk start) of request 0: float32 [count][Hq][d].  Blocks of 64 tokens."""
     bt = 64
     b0, b1 = start // bt, (start + count - 1) // bt
-    blocks = [block_values(KIND_Q, wl.seed, layer, 0, b, bt, wl.num_q_heads, wl.head_dim)
+    blocks = [block_values(KIND_Q, wl.seed, layer, 0, b, bt, wl.num_q_heads, wl.head_dim, wl.values)
               for b in range(b0, b1 + 1)]
     allv = np.concatenate(blocks, axis=0)
     off = start - b0 * bt
@@ -124,20 +154,25 @@ def _on_q_grid(x: np.ndarray) -> np.ndarray:
 
 
 def decode_queries(wl: Workload) -> np.ndarray:
-    """float32 [steps][L][B][Hq][d] on the query grid."""
+    """float32 [steps][L][B][Hq][d] on the query grid (or rounded to bf16)."""
+    if wl.values == "bf16":
+        def emit(x):
+            return (_bf16_rne_bits(np.asarray(x, dtype=np.float32)).astype(np.uint32) << 16).view(np.float32)
+    else:
+        emit = _on_q_grid
     rng = np.random.default_rng(wl.seed)
     shape = (wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim)
     out = np.empty((wl.steps,) + shape, dtype=np.float32)
     if wl.query == "iid":
         for t in range(wl.steps):
-            out[t] = _on_q_grid(rng.standard_normal(shape))
+            out[t] = emit(rng.standard_normal(shape))
         return out
     norm = 1.0 / math.sqrt(0.82) if wl.query == "ar" else 1.0
     state = rng.standard_normal(shape)
-    out[0] = _on_q_grid(state)
+    out[0] = emit(state)
     for t in range(1, wl.steps):
         state = (0.9 * state + 0.1 * rng.standard_normal(shape)) * norm
-        out[t] = _on_q_grid(state)
+        out[t] = emit(state)
     return out
 
 

@@ -11,6 +11,7 @@ import os
 import shutil
 import subprocess
 
+import numpy as np
 import torch
 
 from . import gen
@@ -46,10 +47,13 @@ def _load():
     return _lib
 
 
-def _table(kind: int, device) -> torch.Tensor:
-    key = (kind == gen.KIND_Q, str(device))
+def _table(kind: int, values: str, device) -> torch.Tensor:
+    key = (kind == gen.KIND_Q, values, str(device))
     if key not in _tables:
-        t = gen.q_table() if kind == gen.KIND_Q else gen.kv_table()
+        if values == "bf16":
+            t = gen.bf16_table().view(np.int16)
+        else:
+            t = gen.q_table() if kind == gen.KIND_Q else gen.kv_table()
         _tables[key] = torch.from_numpy(t.copy()).to(device)
     return _tables[key]
 
@@ -65,7 +69,9 @@ def tokens(wl: Workload, kind: int, layer: int, req: int, start: int, count: int
     D = wl.head_dim
     if out is None:
         out = torch.empty((count, H, D), dtype=torch.bfloat16, device="cuda")
-    tab = _table(kind, out.device)
+    tab = _table(kind, wl.values, out.device)
+    if wl.values == "bf16":
+        e = -1                                   # the table holds bf16 bit patterns
     s = torch.cuda.current_stream().cuda_stream if stream is None else stream
     rc = _load().tkvgen_tokens(out.data_ptr(), tab.data_ptr(), e, wl.seed, kind, layer, req, start,
                                count, bt, H * D, s)
