@@ -15,8 +15,10 @@
  * quantised and written through to the mirror, so eviction is a pure rebind.
  *
  * Conventions
- *  - All device pointers are caller-owned device memory (the library never
- *    allocates device memory).  The pinned host mirror is owned by the ctx.
+ *  - All device pointers are caller-owned device memory.  The library
+ *    allocates no device memory, except for a staging buffer that
+ *    tkv_prefix_save and tkv_prefix_restore allocate and free within the
+ *    call.  The pinned host mirror is owned by the ctx.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    calls except tkv_create/tkv_attach_device/tkv_read_counters/
  *    tkv_debug_read_state and the cold-prefix calls (tkv_prefix_save/
@@ -81,6 +83,8 @@ extern "C" {
 #define TKV_ERR_CAPACITY 2     /* an ensure needed more distinct pages than slots: call ignored */
 #define TKV_ERR_NOT_RESIDENT 4 /* store to a page with no slot: mirror and slab written, pool not */
 #define TKV_ERR_BAD_MISS 8     /* fetch list entry outside the pool or the page space: skipped */
+#define TKV_ERR_RUN_LEN 16     /* a write run spans more pages than its call's max_run_len allows:
+                                  the pages past that reach were not made resident / not written */
 
 typedef struct tkv_config {
   int32_t num_layers;
@@ -101,7 +105,7 @@ typedef struct tkv_config {
 typedef struct tkv_sizes {
   size_t pool_bytes;      /* num_slots * row_bytes */
   size_t slab_bytes;      /* bf16 slab */
-  size_t state_bytes;     /* residency state, counters and the slab's fp32 running sums */
+  size_t state_bytes;     /* residency state, counters and the slab's fp64 running key sums */
   size_t workspace_bytes; /* per-call scratch for the largest call the config allows */
   size_t mirror_bytes;    /* pinned host mirror (allocated by tkv_create) */
   size_t row_bytes;       /* bytes of one page row (all layers) */
@@ -138,10 +142,18 @@ int tkv_create(const tkv_config* cfg, tkv_ctx** out);
 int tkv_attach_device(tkv_ctx* ctx, const tkv_device_buffers* bufs, void* stream);
 
 /* FreeToken PR #525 commit summary (set_select_width takes max_bs): the
- * whole batch's selection must fit the pool by construction.  Sets the
- * compaction width C = max_sel_pages (0 -> 2*block_topk + 8, PR #499
- * "Design").  TKV_E_CAPACITY if max_bs*C > num_slots or > max_width. */
+ * width is chosen so that a full batch's compacted selection always has
+ * enough slots.  Sets the compaction width C = max_sel_pages (0 ->
+ * 2*block_topk + 8, PR #499 "Design").  TKV_E_CAPACITY if max_bs*C >
+ * num_slots or > max_width; the width is then left as it was. */
 int tkv_set_select_width(tkv_ctx* ctx, int32_t max_bs, int32_t block_topk, int32_t max_sel_pages);
+
+/* The compaction width C the last successful tkv_set_select_width set: the
+ * row length of `needed` (int32 [B][C]) and the ensure width per request of
+ * the fused decode calls (B*C entries of out_slots and miss).  Callers size
+ * those buffers from this value.  0 before any width is set or for a NULL
+ * ctx. */
+int32_t tkv_select_width(const tkv_ctx* ctx);
 
 /* Empties the pool (every page non-resident, clock 0) and zeroes the
  * counters and error word.  Slab and mirror contents are kept. */
@@ -295,7 +307,7 @@ int tkv_decode_layer_prefetch(tkv_ctx* ctx, int32_t layer, const uint16_t* q, in
                               void* copy_stream);
 
 /* ensure_write_pages (PR #499 "Design": one fixed-shape launch of stride
- * samples plus one boundary sample per request run): run r writes tokens
+ * samples at page steps and a last sample at each run's end): run r writes tokens
  * run_start[r] .. run_start[r]+run_len[r]-1 of request run_req[r].  Every
  * page the runs touch is made resident (one ensure call); a page whose
  * first position is >= old_len[req] has no content yet and is bound without
@@ -323,9 +335,9 @@ int tkv_store_kv_mirror(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const ui
  * reused; on a later hit it comes back host to host into the mirror and the
  * LRU's fetch on selection covers residency).  A record is one page's
  * mirror row (row_bytes) followed by its indexer slab entries for every
- * layer: bf16 values [L][Hkv*d], then fp32 key sums [L][Hkv*d] (what a
+ * layer: bf16 values [L][Hkv*d], then fp64 key sums [L][Hkv*d] (what a
  * partly written page's later tokens add to); tkv_prefix_record_bytes
- * gives its size. */
+ * gives its size (row_bytes + L*Hkv*d*10). */
 int64_t tkv_prefix_record_bytes(const tkv_ctx* ctx);
 
 /* Copies the records of `n` logical pages (pages: host int32 [n], each in

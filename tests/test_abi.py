@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "tkv.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|int64_t|void|const char\*|const void\*)\s+(tkv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|int64_t|void|const char\*|const void\*)\s+(tkv_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_path():

@@ -237,3 +237,45 @@ def test_store_to_a_page_without_slot():
     o.store(layer, [(0, 0, n)], k, v, bt)
     compare_state(g, o, "after the store", check_rows=True)
     assert g.tier.read_counters()["error_word"] == TKV_ERR_NOT_RESIDENT
+
+
+def test_runs_longer_than_max_run_len_are_flagged():
+    """A run whose device-side length spans more pages than the call's
+    max_run_len reaches is reported, not silently cut: the write-ensure's
+    samples miss a page and the store's grid does not reach the last one;
+    both set the run-length bit (and the store to the page the ensure missed
+    sets the not-resident bit)."""
+    TKV_ERR_RUN_LEN = 16
+    say("[edges] run longer than max_run_len")
+    t = _small_tier(16, 16)
+    i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device="cuda")
+    bt = torch.arange(64, dtype=torch.int32, device="cuda").view(1, 64)
+    n = 3 * 64                                           # three pages on the device ...
+    t.ensure_write_pages(i32([0]), i32([0]), i32([n]), 64, bt, i32([0]))   # ... max_run_len one page
+    torch.cuda.synchronize()
+    assert t.read_counters()["error_word"] == TKV_ERR_RUN_LEN
+    st = t.read_state()
+    assert st["page_to_slot"][0] >= 0 and st["page_to_slot"][2] >= 0 and st["page_to_slot"][1] < 0
+    t.reset_residency()
+    t.ensure_write_pages(i32([0]), i32([0]), i32([n]), n, bt, i32([0]))    # right length: all three
+    torch.cuda.synchronize()
+    assert t.read_counters()["error_word"] == 0
+    k = torch.zeros(n, 4, 128, dtype=torch.bfloat16, device="cuda")
+    t.store_kv_mirror(0, k, k, i32([0]), i32([0]), i32([n]), i32([0]), 64, bt)   # grid reaches 2 pages
+    torch.cuda.synchronize()
+    assert t.read_counters()["error_word"] == TKV_ERR_RUN_LEN
+
+
+def test_binding_takes_the_compaction_width_from_the_library():
+    """The buffers the binding sizes (needed [B][C], out_slots/miss [B*C])
+    use the width the library set, read back through tkv_select_width, for
+    the default (2*block_topk + 8, FreeToken PR #499 "Design") and an
+    explicit max_sel_pages; a refused width leaves the old one."""
+    from tiered_kv_cache_indexer_amd import TkvError
+    t = _small_tier(64, 64)
+    assert t.lib.tkv_select_width(t.ctx) == 0
+    assert t.set_select_width(1, 8, 0) == 24 == t.lib.tkv_select_width(t.ctx) == t.C
+    assert t.set_select_width(1, 8, 5) == 5 == t.lib.tkv_select_width(t.ctx) == t.C
+    with pytest.raises(TkvError):
+        t.set_select_width(1, 8, 65)                    # more than the 64 slots
+    assert t.lib.tkv_select_width(t.ctx) == 5

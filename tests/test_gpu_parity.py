@@ -135,7 +135,8 @@ def test_gpu_generator_matches_numpy():
     say("[parity] Philox generator")
     for key, kind, layer, req, start, count in [("c2", 0, 3, 0, 0, 200), ("c2", 1, 11, 0, 4000, 300),
                                                 ("c4", 0, 5, 2, 12345, 77), ("c1", 1, 0, 0, 17, 40),
-                                                ("c5", 2, 7, 0, 100, 130)]:
+                                                ("c5", 2, 7, 0, 100, 130), ("c2s_bf16", 0, 1, 0, 0, 200),
+                                                ("c3s_bf16", 1, 2, 0, 640, 65), ("c5s_bf16", 2, 1, 0, 64, 130)]:
         wl = get_workload(key)
         got = gpu_gen.tokens(wl, kind, layer, req, start, count).float().cpu().numpy()
         if kind == gen.KIND_Q:

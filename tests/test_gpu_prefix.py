@@ -45,14 +45,14 @@ def test_prefix_save_restore_decode():
     orecs = o.prefix_save(src)
     L, E = wl.num_layers, wl.num_kv_heads * wl.head_dim
     rb = g.tier.row_bytes
-    assert recs.shape == (len(src), rb + L * E * 6)
+    assert recs.shape == (len(src), rb + L * E * 10)
     for i, r in enumerate(orecs):
         assert np.array_equal(recs[i, :rb], r["row"]), f"record {i}: row"
         vals = recs[i, rb:rb + L * E * 2].view(np.uint16).reshape(L, -1)
         assert np.array_equal(vals, bf16_bits_from_f32(r["slab"]).reshape(L, -1)), f"record {i}: slab"
-        sums = recs[i, rb + L * E * 2:].view(np.float32).reshape(L, -1)
+        sums = recs[i, rb + L * E * 2:].view(np.float64).reshape(L, -1)
         for layer, v in r["sums"].items():
-            assert np.array_equal(sums[layer], v.reshape(-1).astype(np.float32)), f"record {i}: sums"
+            assert np.array_equal(sums[layer], v[0].reshape(-1)), f"record {i}: sums"
     assert any(r["sums"] for r in orecs)            # the partly written last page
     g.tier.prefix_restore(dst, recs)
     o.prefix_restore(dst, orecs)

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtkv.so")
 
 KV_BF16, KV_FP8, KV_NVFP4 = 0, 1, 2
-ERR_PAGE_RANGE, ERR_CAPACITY, ERR_NOT_RESIDENT, ERR_BAD_MISS = 1, 2, 4, 8
+ERR_PAGE_RANGE, ERR_CAPACITY, ERR_NOT_RESIDENT, ERR_BAD_MISS, ERR_RUN_LEN = 1, 2, 4, 8, 16
 
 E = {0: "TKV_OK", -1: "TKV_E_INVALID_ARG", -2: "TKV_E_UNSUPPORTED_FORMAT", -3: "TKV_E_CAPACITY",
      -4: "TKV_E_OOM", -5: "TKV_E_HIP", -6: "TKV_E_STATE"}
@@ -63,6 +63,7 @@ SIGNATURES = {
     "tkv_create": (C.c_int, [C.POINTER(Config), C.POINTER(C.c_void_p)]),
     "tkv_attach_device": (C.c_int, [P, C.POINTER(DeviceBuffers), P]),
     "tkv_set_select_width": (C.c_int, [P, I32, I32, I32]),
+    "tkv_select_width": (I32, [P]),
     "tkv_reset_residency": (C.c_int, [P, P]),
     "tkv_select_pages": (C.c_int, [P, I32, P, I32, P, P, P, I32, P, I32, P, I32, P, P, P]),
     "tkv_lru_ensure": (C.c_int, [P, P, I32, P, P, P, P, P]),

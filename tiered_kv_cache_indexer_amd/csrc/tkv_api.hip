@@ -122,7 +122,7 @@ static Layout make_layout(const tkv_config* c) {
   L.st_s2p = o; o = align256(o + S * 4);
   L.st_stamp = o; o = align256(o + S * 8);
   L.st_order = o; o = align256(o + 2 * S * 4);
-  L.st_acc = o; o = align256(o + NL * N * H * D * 4);
+  L.st_acc = o; o = align256(o + NL * N * H * D * 8);
   L.st_total = o;
   const size_t W = c->max_width, R = c->max_rows, P = c->max_pages_per_req;
   o = 0;
@@ -244,7 +244,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.slot_to_page = (int32_t*)(st + L.st_s2p);
   d.stamp = (int64_t*)(st + L.st_stamp);
   d.order = (int32_t*)(st + L.st_order);
-  d.slab_acc = (float*)(st + L.st_acc);
+  d.slab_acc = (double*)(st + L.st_acc);
   uint8_t* ws = (uint8_t*)b->workspace;
   d.scores = (float*)(ws + L.ws_scores);
   d.sel_slots = (int32_t*)(ws + L.ws_sel_slots);
@@ -293,6 +293,8 @@ int tkv_set_select_width(tkv_ctx* c, int32_t max_bs, int32_t block_topk, int32_t
   c->C = C;
   return TKV_OK;
 }
+
+int32_t tkv_select_width(const tkv_ctx* c) { return c ? c->C : 0; }
 
 static int need_attached(tkv_ctx* c) {
   if (!c) return fail(TKV_E_INVALID_ARG, "ctx is NULL");
@@ -700,7 +702,7 @@ int tkv_debug_read_state(tkv_ctx* c, int32_t* page_to_slot, int32_t* slot_to_pag
 int64_t tkv_prefix_record_bytes(const tkv_ctx* c) {
   if (!c) return 0;
   const int64_t E = (int64_t)c->cfg.num_kv_heads * c->cfg.head_dim;
-  return (int64_t)c->row_bytes + (int64_t)c->cfg.num_layers * E * 6;
+  return (int64_t)c->row_bytes + (int64_t)c->cfg.num_layers * E * 10;
 }
 
 static int check_prefix_pages(tkv_ctx* c, const int32_t* pages, int32_t n, bool distinct) {
@@ -723,13 +725,13 @@ static int check_prefix_pages(tkv_ctx* c, const int32_t* pages, int32_t n, bool 
 // Slab entries of `n` pages between records and the device, 128 pages at a time.
 static int prefix_slab(tkv_ctx* c, const int32_t* pages, int32_t n, uint8_t* recs, bool save, hipStream_t s) {
   const size_t E = (size_t)c->cfg.num_kv_heads * c->cfg.head_dim, L = c->cfg.num_layers;
-  const size_t rec = (size_t)tkv_prefix_record_bytes(c), vbytes = L * E * 2, sbytes = L * E * 4;
+  const size_t rec = (size_t)tkv_prefix_record_bytes(c), vbytes = L * E * 2, sbytes = L * E * 8;
   const int SLICE = 128;
   const int m = std::min(n, SLICE);
   void* dev = nullptr;
   HIPCHECK(hipMalloc(&dev, m * (vbytes + sbytes) + (size_t)m * 4), "hipMalloc (prefix staging)");
   uint16_t* dv = (uint16_t*)dev;
-  float* ds = (float*)((uint8_t*)dev + m * vbytes);
+  double* ds = (double*)((uint8_t*)dev + m * vbytes);
   int32_t* dp = (int32_t*)((uint8_t*)dev + m * (vbytes + sbytes));
   std::vector<uint8_t> host(m * (vbytes + sbytes));
   hipError_t e = hipSuccess;

@@ -13,6 +13,7 @@
 #define DERR_CAPACITY 2
 #define DERR_NOT_RESIDENT 4
 #define DERR_BAD_MISS 8
+#define DERR_RUN_LEN 16
 
 enum { CNT_ENSURE = 0, CNT_HITS, CNT_MISSES, CNT_FRESH, CNT_EVICT, CNT_DROPS, CNT_BYTES_FETCHED,
        CNT_BYTES_MIRRORED, CNT_N };
@@ -34,7 +35,7 @@ struct DevCtx {
   uint8_t* pool;
   uint8_t* mirror;          // device-visible address of the pinned host mirror
   uint16_t* slab;           // bf16 [L][N][Hkv][D]
-  float* slab_acc;          // fp32 [L][N][Hkv][D] running key sums
+  double* slab_acc;         // fp64 [L][N][Hkv][D] running key sums (exact for bf16 keys: see k_store)
   // residency state
   StateHdr* hdr;
   int32_t* page_to_slot;    // [N]
@@ -201,6 +202,9 @@ __device__ __forceinline__ uint32_t xor_lane_u32(uint32_t v, int m) {
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = xor_lane_u32((uint32_t)v, m), hi = xor_lane_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double xor_lane_f64(double v, int m) {
+  return __longlong_as_double((long long)shfl_xor_u64((uint64_t)__double_as_longlong(v), m));
 }
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   uint32_t lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(uint32_t)(v >> 32), src, 64);

@@ -177,6 +177,8 @@ __global__ void k_write_samples(DevCtx c, int n_runs, const int32_t* run_req, co
         if (k * c.PS < len) pos = start + k * c.PS;
       } else {
         pos = start + len - 1;
+        // the stride samples reach pages start/PS .. start/PS + spr-2 only
+        if ((start + len - 1) / c.PS - start / c.PS >= spr) set_error(c.hdr, DERR_RUN_LEN);
       }
     }
     int needed = -1;
@@ -260,7 +262,7 @@ hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st) {
   if (full) {
     const int64_t E = (int64_t)c.L * c.N * c.Hkv * c.D;
     if ((e = launch_fill_bytes(c.slab, E * 2, 0, st)) != hipSuccess) return e;
-    if ((e = launch_fill_bytes(c.slab_acc, E * 4, 0, st)) != hipSuccess) return e;
+    if ((e = launch_fill_bytes(c.slab_acc, E * 8, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.row_done, c.max_rows, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.glob_done, 4, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.attn_done, (int64_t)c.max_batch * c.Hkv, 0, st)) != hipSuccess) return e;

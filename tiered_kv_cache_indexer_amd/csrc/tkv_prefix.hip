@@ -3,11 +3,11 @@
 // (its logical ids get reused); on a later hit it comes back host to host
 // into the offloader's mirror, and the LRU's fetch on selection covers
 // residency.  A record is a page's mirror row followed by its indexer slab
-// entries for every layer: bf16 values [L][Hkv*d] and the fp32 key sums
+// entries for every layer: bf16 values [L][Hkv*d] and the fp64 key sums
 // [L][Hkv*d] (the running sum a partly written page's later tokens add to).
 //
 // The rows move host to host (threads over memcpy); only the slab entries,
-// 6 bytes per feature, cross the host link, in slices of 128 pages.
+// 10 bytes per feature, cross the host link, in slices of 128 pages.
 #include <algorithm>
 #include <cstring>
 #include <thread>
@@ -19,7 +19,7 @@
 namespace {
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_slab_gather(DevCtx c, const int32_t* pages, uint16_t* vals,
-                                                           float* sums) {
+                                                           double* sums) {
   const int i = blockIdx.x, l = blockIdx.y, n_layers = gridDim.y;
   const int E = c.Hkv * c.D;
   const size_t src = ((size_t)l * c.N + pages[i]) * E, dst = ((size_t)i * n_layers + l) * E;
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_slab_gather(DevCtx c, const int32
 }
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_slab_scatter(DevCtx c, const int32_t* pages, const uint16_t* vals,
-                                                            const float* sums) {
+                                                            const double* sums) {
   const int i = blockIdx.x, l = blockIdx.y, n_layers = gridDim.y;
   const int E = c.Hkv * c.D;
   const size_t dst = ((size_t)l * c.N + pages[i]) * E, src = ((size_t)i * n_layers + l) * E;
@@ -75,14 +75,14 @@ void prefix_copy_rows(uint8_t* dst, size_t dst_stride, const uint8_t* src, size_
   for (auto& x : th) x.join();
 }
 
-hipError_t launch_slab_gather(const DevCtx& c, const int32_t* pages, int n, uint16_t* vals, float* sums,
+hipError_t launch_slab_gather(const DevCtx& c, const int32_t* pages, int n, uint16_t* vals, double* sums,
                               hipStream_t st) {
   hipLaunchKernelGGL(k_slab_gather, dim3(n, c.L), dim3(TKV_BLOCK), 0, st, c, pages, vals, sums);
   return hipGetLastError();
 }
 
 hipError_t launch_slab_scatter(const DevCtx& c, const int32_t* pages, int n, const uint16_t* vals,
-                               const float* sums, hipStream_t st) {
+                               const double* sums, hipStream_t st) {
   hipLaunchKernelGGL(k_slab_scatter, dim3(n, c.L), dim3(TKV_BLOCK), 0, st, c, pages, vals, sums);
   return hipGetLastError();
 }

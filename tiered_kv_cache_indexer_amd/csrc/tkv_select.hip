@@ -13,10 +13,12 @@
 // select over the scores; the last row of the call compacts every request
 // and, for the fused decode step, runs the LRU ensure in the same launch.
 //
-// The slab values are bf16 on a 2^-10 grid and the query sums bf16 on a
-// 2^-5 grid, so every product is exact in fp32 and so is every partial sum
-// while sum |q*slab| < 2^9: the scores -- and hence the selections -- do not
-// depend on the summation order.
+// Scores: a product of two bf16 values is exact in fp32; the products are
+// summed in fp64, where every partial sum is exact as long as the page's
+// products are multiples of 2^e with sum |q*slab| < 2^(53+e) (about 40 of
+// the 53 bits for normally distributed bf16 queries and keys; 24 on the
+// workloads' grids), so the score is the exact dot product rounded once to
+// fp32 whatever the order of the additions -- and the selections are too.
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 #include "tkv_lru_dev.h"
@@ -356,20 +358,20 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   float keys[PASSES];
 #pragma unroll
   for (int it = 0; it < PASSES; ++it) {
-    float part = 0.f;
+    double part = 0.0;
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       const uint32_t w[4] = {v[it][s].x, v[it][s].y, v[it][s].z, v[it][s].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        part += qg[s][2 * t] * __uint_as_float(w[t] << 16);
-        part += qg[s][2 * t + 1] * __uint_as_float(w[t] & 0xFFFF0000u);
+        part += (double)(qg[s][2 * t] * __uint_as_float(w[t] << 16));            // exact product
+        part += (double)(qg[s][2 * t + 1] * __uint_as_float(w[t] & 0xFFFF0000u));
       }
     }
 #pragma unroll
-    for (int o = LANES / 2; o > 0; o >>= 1) part += __uint_as_float(xor_lane_u32(__float_as_uint(part), o));
+    for (int o = LANES / 2; o > 0; o >>= 1) part += xor_lane_f64(part, o);
     const int lg = logical[it];
-    float key = part;
+    float key = (float)part;
     if (lg < 0) key = -INFINITY;
     else if (a.bias) key = key + a.bias[lg];
     keys[it] = key;

@@ -1,9 +1,10 @@
 // store_kv with the write-through mirror (gfx950).
 //
-// FreeToken PR #499, "Design": every store_kv is mirrored to the pinned host
-// bank over the unified address space, so a GPU slot is always drop-clean.
-// PR #525 commit summary (mirror_store_quant): the mirror takes the e4m3
-// codes and fp32 scales AFTER quantisation -- the pool is the source of truth.
+// FreeToken PR #499, "Design": each store is also written to the pinned host
+// mirror through the device-visible mapping, so a slot never holds bytes the
+// mirror lacks and evicting it costs nothing.  PR #525 commit summary
+// (mirror_store_quant): the mirror gets the quantiser's output, the e4m3
+// codes and fp32 scales the pool gets, not the values from before it.
 //
 // One workgroup per (run, page of the run).  A wave takes groups of four page
 // positions, loads the group's K and V rows at once and quantises one token
@@ -15,7 +16,12 @@
 // transposed ([h][d][page]): each lane packs its 8 rows' bytes for 4
 // consecutive positions into words, the block is staged in LDS and written
 // out row by row.  The workgroup also sums the page's keys for the indexer
-// slab: slab = bf16(running sum / tokens written).
+// slab: slab = bf16(fp32(running sum) / tokens written).  The sums are fp64:
+// every bf16 key of a page feature is a multiple of 2^e (e the lowest set
+// bit among them) and every partial sum is bounded by sum |key|, so while
+// sum |key| < 2^(53+e) -- any page of normally distributed bf16 keys -- each
+// fp64 addition is exact and the result does not depend on the order the
+// waves add in; fp32 sums would round once the keys span more than 24 bits.
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
@@ -40,7 +46,7 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   constexpr bool STAGE_K = FP8 && E8 <= 64;
   constexpr int STORE_BLOCK = store_block<E8>();
   constexpr int NW = STORE_BLOCK / 64;
-  __shared__ float ksum_w[NW][E];
+  __shared__ double ksum_w[NW][E];
   __shared__ uint32_t vt[VT_WORDS];
   __shared__ __align__(16) uint8_t kt[STAGE_K ? E * 64 : 16];
   __shared__ __align__(16) float sct[STAGE_K ? 2 * 64 : 4];
@@ -49,6 +55,8 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   const int PS = c.PS, D = c.D;
   const int req = a.run_req[r], start = a.run_start[r], len = a.run_len[r];
   if (len <= 0) return;
+  // the grid reaches gridDim.y pages of the run: a longer run is flagged
+  if (j == 0 && tid == 0 && (start + len - 1) / PS - start / PS >= (int)gridDim.y) set_error(c.hdr, DERR_RUN_LEN);
   const int lp = start / PS + j;
   const int t0 = max(start, lp * PS), t1 = min(start + len, (lp + 1) * PS);
   if (t0 >= t1) return;
@@ -72,11 +80,11 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   if (FP8)
     for (int w = tid; w < E * VROW; w += STORE_BLOCK) vt[w] = 0u;
 
-  float ksum[SPL][8];
+  double ksum[SPL][8];
 #pragma unroll
   for (int s = 0; s < SPL; ++s)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) ksum[s][t] = 0.f;
+    for (int t = 0; t < 8; ++t) ksum[s][t] = 0.0;
   if (FP8) __syncthreads();
 
   // a wave handles groups of 4 consecutive page positions
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
           for (int t = 0; t < 8; ++t) amax = fmaxf(amax, fabsf(x[s][t]));
           if (kv == 0)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) ksum[s][t] += x[s][t];
+            for (int t = 0; t < 8; ++t) ksum[s][t] += (double)x[s][t];
         }
         uint8_t* mblk = mir + kv * cb;
         uint8_t* pblk = pol ? pol + kv * cb : nullptr;
@@ -289,12 +297,12 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   const size_t sbase = ((size_t)a.layer * c.N + page) * E;
   const int cnt = off + n;
   for (int e = tid; e < E; e += STORE_BLOCK) {
-    float sum = 0.f;
+    double sum = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; w += 4) sum += (ksum_w[w][e] + ksum_w[w + 1][e]) + (ksum_w[w + 2][e] + ksum_w[w + 3][e]);
     if (off > 0) sum += c.slab_acc[sbase + e];
     c.slab_acc[sbase + e] = sum;
-    c.slab[sbase + e] = f32_to_bf16(sum / (float)cnt);
+    c.slab[sbase + e] = f32_to_bf16((float)sum / (float)cnt);
   }
   if (tid == 0) {
     const int64_t tok_bytes = c.layer_bytes / PS;

@@ -93,7 +93,7 @@ class TieredKV:
     # ------------------------------------------------------------ config ----
     def set_select_width(self, max_bs, block_topk, max_sel_pages=0):
         check(self.lib.tkv_set_select_width(self.ctx, max_bs, block_topk, max_sel_pages))
-        self.C = max_sel_pages if max_sel_pages > 0 else 2 * block_topk + 8
+        self.C = int(self.lib.tkv_select_width(self.ctx))   # the width the library set
         return self.C
 
     def reset_residency(self, stream=None):
