@@ -359,6 +359,18 @@ int tkv_prefix_save(tkv_ctx* ctx, const int32_t* pages, int32_t n, void* records
  * before returning; allocates and frees a staging buffer. */
 int tkv_prefix_restore(tkv_ctx* ctx, const int32_t* pages, int32_t n, const void* records, void* stream);
 
+/* tkv_prefix_restore for callers that cannot allocate memory during the
+ * call (serving loops and harnesses that forbid hipMalloc/hipFree): same
+ * arguments, results and synchronisation; the slab entries pass through a
+ * fixed 2 MiB device array the library holds on each GPU until the process
+ * ends (its address is taken once per device in tkv_attach_device), in
+ * passes of as many pages as fit (34 at 12 layers x 4 KV heads x d 128), and
+ * the mirror rows are copied in the calling thread.  TKV_E_CAPACITY when one
+ * page's slab entries (num_layers*num_kv_heads*head_dim*10 bytes) do not
+ * fit.  All ctxs on one GPU share the array; calls are serialised within a
+ * process, and each pass overwrites what the previous one staged. */
+int tkv_prefix_restore_noalloc(tkv_ctx* ctx, const int32_t* pages, int32_t n, const void* records, void* stream);
+
 /* Copies the counters to the host.  Synchronises `stream`. */
 int tkv_read_counters(tkv_ctx* ctx, tkv_counters* out, void* stream);
 

@@ -86,6 +86,7 @@ SIGNATURES = {
     "tkv_prefix_record_bytes": (I64, [P]),
     "tkv_prefix_save": (C.c_int, [P, P, I32, P, P]),
     "tkv_prefix_restore": (C.c_int, [P, P, I32, P, P]),
+    "tkv_prefix_restore_noalloc": (C.c_int, [P, P, I32, P, P]),
     "tkv_mirror_host_ptr": (C.c_void_p, [P]),
     "tkv_destroy": (None, [P]),
     "tkv_last_error": (C.c_char_p, []),

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/tkv.h"
@@ -12,8 +13,20 @@
 #include "tkv_launch.h"
 
 
+// Staging memory of tkv_prefix_restore_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends.  Host code never passes
+// `scratch` itself to a kernel or a copy (on the host the name is only a
+// stand-in): it uses the device address hipGetSymbolAddress returns, taken
+// once per device when the first ctx attaches there.
+#define TKV_SCRATCH_BYTES (2u << 20)
+static __device__ __align__(256) uint8_t scratch[TKV_SCRATCH_BYTES];
+#define TKV_MAX_DEVICES 64
+static void* g_scratch_ptr[TKV_MAX_DEVICES];
+static std::mutex g_scratch_mu[TKV_MAX_DEVICES];   // one restore at a time per device in this process
+
 struct tkv_ctx {
   tkv_config cfg;
+  int device = -1;      // the device current at tkv_attach_device
   size_t row_bytes, layer_bytes, code_bytes;
   size_t mirror_bytes;
   uint8_t* mirror_host = nullptr;
@@ -270,6 +283,18 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.attn_range_pages = ATTN_RANGE_PAGES_DEFAULT;
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
   d.max_batch = f.max_batch; d.max_width = f.max_width;
+  int dev = 0;
+  HIPCHECK(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= TKV_MAX_DEVICES) return fail(TKV_E_INVALID_ARG, "device %d >= %d", dev, TKV_MAX_DEVICES);
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu[dev]);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      HIPCHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev] = p;
+    }
+  }
+  c->device = dev;
   hipStream_t s = (hipStream_t)stream;
   HIPCHECK(launch_reset(d, 1, s), "initialise device state");
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");
@@ -779,7 +804,7 @@ int tkv_prefix_save(tkv_ctx* c, const int32_t* pages, int32_t n, void* records, 
   WAIT_REST(c, s);
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // stores to the mirror have landed
   const size_t rec = (size_t)tkv_prefix_record_bytes(c);
-  prefix_copy_rows((uint8_t*)records, rec, c->mirror_host, c->row_bytes, c->row_bytes, pages, n, false);
+  prefix_copy_rows((uint8_t*)records, rec, c->mirror_host, c->row_bytes, c->row_bytes, pages, n, false, 8);
   return prefix_slab(c, pages, n, (uint8_t*)records, true, s);
 }
 
@@ -791,8 +816,68 @@ int tkv_prefix_restore(tkv_ctx* c, const int32_t* pages, int32_t n, const void* 
   WAIT_REST(c, s);
   HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // no copy still reads these rows
   const size_t rec = (size_t)tkv_prefix_record_bytes(c);
-  prefix_copy_rows(c->mirror_host, c->row_bytes, (const uint8_t*)records, rec, c->row_bytes, pages, n, true);
+  prefix_copy_rows(c->mirror_host, c->row_bytes, (const uint8_t*)records, rec, c->row_bytes, pages, n, true, 8);
   return prefix_slab(c, pages, n, const_cast<uint8_t*>((const uint8_t*)records), false, s);
+}
+
+// Distinct ids without allocating anything: pairwise comparison.
+static int check_prefix_pages_noalloc(tkv_ctx* c, const int32_t* pages, int32_t n) {
+  int rc = check_prefix_pages(c, pages, n, false);
+  if (rc) return rc;
+  for (int i = 1; i < n; ++i)
+    for (int j = 0; j < i; ++j)
+      if (pages[i] == pages[j])
+        return fail(TKV_E_INVALID_ARG, "pages has duplicates (pages[%d] == pages[%d] == %d)", j, i, pages[i]);
+  return TKV_OK;
+}
+
+// Pages of slab entries one pass of the no-alloc restore stages: values
+// [m][L][E] bf16, then (256-aligned) key sums [m][L][E] fp64, then (256-
+// aligned) the page ids; 0 when one page does not fit.
+static int noalloc_slice_pages(size_t vbytes, size_t sbytes) {
+  for (int m = (int)(TKV_SCRATCH_BYTES / (vbytes + sbytes + 4)); m > 0; --m)
+    if (align256(m * vbytes) + align256(m * sbytes) + (size_t)m * 4 <= TKV_SCRATCH_BYTES) return m;
+  return 0;
+}
+
+int tkv_prefix_restore_noalloc(tkv_ctx* c, const int32_t* pages, int32_t n, const void* records, void* stream) {
+  int rc = check_prefix_pages_noalloc(c, pages, n);
+  if (rc) return rc;
+  if (!records) return fail(TKV_E_INVALID_ARG, "records is NULL");
+  const size_t E = (size_t)c->cfg.num_kv_heads * c->cfg.head_dim, L = c->cfg.num_layers;
+  const size_t vbytes = L * E * 2, sbytes = L * E * 8;
+  const int m = noalloc_slice_pages(vbytes, sbytes);
+  if (m < 1)
+    return fail(TKV_E_CAPACITY, "one page's slab entries (%zu bytes, num_layers=%d x num_kv_heads*head_dim=%zu) "
+                "exceed the %u-byte staging array of the no-alloc restore", vbytes + sbytes + 4,
+                c->cfg.num_layers, E, (unsigned)TKV_SCRATCH_BYTES);
+  int cur = -1;
+  HIPCHECK(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != c->device)
+    return fail(TKV_E_STATE, "device %d is current; the ctx was attached on device %d", cur, c->device);
+  uint8_t* base = (uint8_t*)g_scratch_ptr[c->device];
+  if (!base) return fail(TKV_E_STATE, "no staging address for device %d", c->device);
+  uint16_t* dv = (uint16_t*)base;
+  double* ds = (double*)(base + align256(m * vbytes));
+  int32_t* dp = (int32_t*)(base + align256(m * vbytes) + align256(m * sbytes));
+  hipStream_t s = (hipStream_t)stream;
+  WAIT_REST(c, s);
+  HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // no copy still reads these rows
+  const size_t rec = (size_t)tkv_prefix_record_bytes(c);
+  const uint8_t* recs = (const uint8_t*)records;
+  prefix_copy_rows(c->mirror_host, c->row_bytes, recs, rec, c->row_bytes, pages, n, true, 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu[c->device]);
+  for (int i0 = 0; i0 < n; i0 += m) {
+    const int k = std::min(m, n - i0);
+    const uint8_t* r0 = recs + (size_t)i0 * rec + c->row_bytes;
+    HIPCHECK(hipMemcpyAsync(dp, pages + i0, (size_t)k * 4, hipMemcpyHostToDevice, s), "restore: page ids");
+    HIPCHECK(hipMemcpy2DAsync(dv, vbytes, r0, rec, vbytes, k, hipMemcpyHostToDevice, s), "restore: slab values");
+    HIPCHECK(hipMemcpy2DAsync(ds, sbytes, r0 + vbytes, rec, sbytes, k, hipMemcpyHostToDevice, s), "restore: key sums");
+    HIPCHECK(launch_slab_scatter(c->dev, dp, k, dv, ds, s), "restore: slab scatter");
+    HIPCHECK(launch_unbind(c->dev, dp, k, s), "restore: unbind");
+    HIPCHECK(hipStreamSynchronize(s), "hipStreamSynchronize");   // the next pass reuses the staging
+  }
+  return TKV_OK;
 }
 
 int tkv_debug_set_attn_kernel(tkv_ctx* c, int32_t kernel) {

@@ -30,7 +30,7 @@ hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStrea
 hipError_t launch_e4m3_decode(const uint8_t* in, float* out, int64_t n, hipStream_t st);
 size_t select_dyn_lds(const DevCtx& c);
 void prefix_copy_rows(uint8_t* dst, size_t dst_stride, const uint8_t* src, size_t src_stride, size_t row_bytes,
-                      const int32_t* pages, int n, bool to_mirror);
+                      const int32_t* pages, int n, bool to_mirror, int max_threads);
 hipError_t launch_slab_gather(const DevCtx& c, const int32_t* pages, int n, uint16_t* vals, double* sums,
                               hipStream_t st);
 hipError_t launch_slab_scatter(const DevCtx& c, const int32_t* pages, int n, const uint16_t* vals,

@@ -55,10 +55,11 @@ __global__ void k_unbind(DevCtx c, const int32_t* pages, int n) {
 
 }  // namespace
 
-// Copies rows between the mirror and records with up to 8 host threads.
+// Copies rows between the mirror and records with up to `max_threads` host
+// threads (1: in the calling thread, no thread objects created).
 void prefix_copy_rows(uint8_t* dst, size_t dst_stride, const uint8_t* src, size_t src_stride, size_t row_bytes,
-                      const int32_t* pages, int n, bool to_mirror) {
-  const int T = std::max(1, std::min(8, n / 4));
+                      const int32_t* pages, int n, bool to_mirror, int max_threads) {
+  const int T = std::max(1, std::min(max_threads, n / 4));
   auto work = [&](int t) {
     for (int i = t; i < n; i += T) {
       const size_t p = (size_t)pages[i];

@@ -245,13 +245,15 @@ class TieredKV:
         check(self.lib.tkv_prefix_save(self.ctx, pages.ctypes.data, len(pages), out.ctypes.data, _stream(stream)))
         return out
 
-    def prefix_restore(self, pages, records: np.ndarray, stream=None) -> None:
+    def prefix_restore(self, pages, records: np.ndarray, stream=None, noalloc=False) -> None:
+        """Rehydration of records into `pages`; with `noalloc` through
+        tkv_prefix_restore_noalloc (no memory allocated during the call)."""
         pages = np.ascontiguousarray(pages, dtype=np.int32)
         records = np.ascontiguousarray(records, dtype=np.uint8)
         if records.shape != (len(pages), self.prefix_record_bytes()):
             raise ValueError(f"records shape {records.shape} != ({len(pages)}, {self.prefix_record_bytes()})")
-        check(self.lib.tkv_prefix_restore(self.ctx, pages.ctypes.data, len(pages), records.ctypes.data,
-                                          _stream(stream)))
+        fn = self.lib.tkv_prefix_restore_noalloc if noalloc else self.lib.tkv_prefix_restore
+        check(fn(self.ctx, pages.ctypes.data, len(pages), records.ctypes.data, _stream(stream)))
 
     ATTN_AUTO, ATTN_VECTOR, ATTN_MATRIX = 0, 1, 2
 
