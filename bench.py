@@ -1,23 +1,31 @@
 """Benchmark: sparse decode steps/s (all layers) at 196k context, top-2048.
 
-Workload c3 (synthetic): 12 sparse-attention layers, batch 1, 32 query heads
-/ 4 KV heads, head_dim 128, 64-token pages, context 196,608 tokens (3,072
-pages per layer), top-32 pages (2,048 tokens), fp8 e4m3 KV with per-token
-fp32 scales, a 256-slot GPU pool over a pinned host mirror, log-Zipf(1.1)
-page bias, AR(1) queries.  One step = one decode call for each of the 12
-layers (indexer + compact + LRU ensure, fused host->device copy of the missed
-pages across all layers, sparse paged attention).  When the warmup steps miss
-pages, the calls are decode_layer_split: each miss's slices of the decoded
-layer and the next one are copied on the decode stream, the rest of its row
-on a second stream, beside the attention and the next layer's selection;
-otherwise decode_layer (one stream).
+Headline workload c3 (synthetic): 12 sparse-attention layers, batch 1, 32
+query heads / 4 KV heads, head_dim 128, 64-token pages, context 196,608
+tokens (3,072 pages per layer), top-32 pages (2,048 tokens), fp8 e4m3 KV with
+per-token fp32 scales, a 256-slot GPU pool over a pinned host mirror,
+log-Zipf(1.1) page bias, AR(1) queries.  One step = one decode call for each
+of the 12 layers (indexer + compact + LRU ensure, fused host->device copy of
+the missed pages across all layers, sparse paged attention).  When the warmup
+steps miss pages, the calls are decode_layer_split: each miss's slices of the
+decoded layer and the next one are copied on the decode stream, the rest of
+its row on a second stream, beside the attention and the next layer's
+selection; otherwise decode_layer (one stream).
 
 Timing: W untimed steps, then K steps bracketed by synchronize + HIP events
 on the decode stream (the copy stream joined before the closing event).
 Separate passes then time, with HIP events, every rest-of-rows copy on the
-copy stream (the roofline figure), and select+ensure, the whole-row copy and
-the attention one launch at a time.  The oracle (CPU) is timed on a bounded
-sample of the same workload as the cpu_baseline.
+copy stream, and select+ensure, the whole-row copy and the attention one
+launch at a time.
+
+The same JSON line carries, under "configs", the other four workloads (c1
+tiny bf16, c2 64k resident, c4 batch-4 mixed, c5 prefill chunk), each with
+its own steps (the same W and K), roofline and CPU baseline, and cold-pool
+figures for c3 (a step from an empty pool) and c5 (a chunk from an empty
+pool: the bulk fetch of the cached context).  The oracle (CPU) is timed in a
+child process started before this process touches the GPU, on its own
+cores, on a bounded sample of each workload: the first steps of the same
+timed window the GPU measured.
 """
 from __future__ import annotations
 
@@ -106,13 +114,17 @@ def parse():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--measure-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--graph", action="store_true", help="replay each decode step as a captured HIP graph")
     ap.add_argument("--decode", choices=["auto", "split", "plain"], default="auto",
                     help="split: decode_layer_split (each miss's other layers copied on a second stream); "
                          "plain: decode_layer; auto: split when the warmup steps missed pages")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the preload, host-tail, prefix and append figures (profiling runs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the --config workload: no other configs, no cold-pool figures")
+    ap.add_argument("--cpu-deadline", type=float, default=480.0,
+                    help="seconds from the start after which unfinished CPU baselines are dropped")
+    ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -151,7 +163,11 @@ def calibrate(torch):
 
 def measure_kernels(torch, g, start_step, nsteps):
     """Run `nsteps` decode steps through the unfused entry points with HIP
-    events around every fetch and attention launch (same stream)."""
+    events around every select+ensure, fetch and attention launch (same
+    stream), synchronising after each layer so that every window measures its
+    own launches from an idle queue (without it, a queue that the host keeps
+    full let one 36 us select window read 700 us in a process that had run
+    other workloads first)."""
     wl, t = g.wl, g.tier
     rs = torch.arange(wl.batch + 1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -171,6 +187,7 @@ def measure_kernels(torch, g, start_step, nsteps):
             t.sparse_paged_attn(layer, q, rs, g.ctx_len, g.sel[layer], g.bt, g.out[layer])
             e[3].record(stream)
             ev.append(e)
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     c1 = t.read_counters()
     sel_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
@@ -199,16 +216,40 @@ def measure_kernels(torch, g, start_step, nsteps):
     )
 
 
-def cpu_baseline(wl, nsteps):
-    """The oracle, as written, on a bounded sample: its setup (slab of every
-    page) is untimed; then `nsteps` full decode steps (12 layers: select,
-    compact, LRU, fetch copy, fp64 attention).  Rebuilding page bytes from the
-    input generator (the lazy mirror) is input generation and is excluded."""
+# ------------------------------------------------------------ CPU baseline --
+# The oracle, as written, timed on this host in a child process (started
+# before the parent touches the GPU and pinned to cores the parent does not
+# use).  Decode workloads: untimed setup and untimed steps 0..W-1, then the
+# first n of the GPU's timed steps W..W+K-1, all layers (select, compact,
+# LRU ensure, fetch copy, fp64 attention).  Rebuilding page rows from the
+# input generator (the oracle's lazy mirror) is input generation and is
+# subtracted.  Prefill: the chunk's store, selection, ensure and fetch for all
+# rows and layers, attention for a stated sample of rows, scaled to the chunk.
+
+CPU_SAMPLE_STEPS = {"c1": 20, "c2": 6, "c3": 4, "c4": 2}
+CPU_PREFILL_ROWS = 128
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_decode_baseline(key, warmup, steps):
+    import dataclasses
+
     import numpy as np
 
     from oracle import run
-    from workload import gen
+    from workload import gen, get_workload
 
+    base = get_workload(key)
+    n = min(steps, CPU_SAMPLE_STEPS.get(key, 3))
+    wl = dataclasses.replace(base, steps=max(base.steps, warmup + steps))
     t0 = time.perf_counter()
     tier = run.make_tier(wl, materialize=False)
     run.setup(wl, tier)
@@ -229,23 +270,153 @@ def cpu_baseline(wl, nsteps):
     q = gen.decode_queries(wl)
     rs = np.arange(wl.batch + 1)
     tier.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for s in range(nsteps):
-            for layer in range(wl.num_layers):
-                tier.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
-        wall = time.perf_counter() - t0
+
+    def step(s):
+        for layer in range(wl.num_layers):
+            tier.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+
+    a = time.perf_counter()
+    for s in range(warmup):
+        step(s)
+    warm_s = time.perf_counter() - a
+    spent[0] = 0.0
+    a = time.perf_counter()
+    for s in range(warmup, warmup + n):
+        step(s)
+    wall = time.perf_counter() - a
     work = wall - spent[0]
+    threads = _oracle_threads()
+    return dict(value=round(n / work, 3), unit="steps/s", cores=threads, kind="oracle",
+                sample=(f"decode steps {warmup}..{warmup + n - 1} of {wl.name} (the first {n} of the GPU's "
+                        f"timed steps {warmup}..{warmup + steps - 1}), all {wl.num_layers} layers: select, "
+                        f"compact, LRU ensure, fetch copy, fp64 attention; timed {work:.2f}s; untimed: setup "
+                        f"{setup_s:.1f}s, steps 0..{warmup - 1} {warm_s:.1f}s, page-row rebuild from the input "
+                        f"generator {spent[0]:.1f}s; NumPy with BLAS on {threads} threads (the step loop is "
+                        f"single-threaded Python)"),
+                max_score_bits=round(float(tier.max_score_bits), 2),
+                max_score_abs_sum=round(float(tier.max_certificate), 3))
+
+
+def cpu_prefill_baseline(key):
+    import numpy as np
+
+    from oracle import run
+    from workload import get_workload
+
+    wl = get_workload(key)
+    t0 = time.perf_counter()
+    tier = run.make_tier(wl, materialize=False)
+    run.setup(wl, tier)
+    setup_s = time.perf_counter() - t0
+    n = wl.prefill_tokens
+    rows = list(range(0, n, max(1, n // CPU_PREFILL_ROWS)))
+    spent = {"rebuild": 0.0, "attn": 0.0}
+    builder, attend_row = tier.row_builder, tier.attention_row
+
+    def timed_builder(page):
+        a = time.perf_counter()
+        r = builder(page)
+        spent["rebuild"] += time.perf_counter() - a
+        return r
+
+    def timed_attention_row(*args, **kw):
+        a = time.perf_counter()
+        r0 = spent["rebuild"]
+        out = attend_row(*args, **kw)
+        spent["attn"] += time.perf_counter() - a - (spent["rebuild"] - r0)
+        return out
+
+    tier.row_builder = timed_builder
+    tier.attention_row = timed_attention_row
+    a = time.perf_counter()
+    run.prefill(wl, tier, attention_rows=rows)
+    wall = time.perf_counter() - a
+    base_s = wall - spent["rebuild"] - spent["attn"]
+    est = base_s + spent["attn"] * n / len(rows)
+    threads = _oracle_threads()
+    return dict(value=round(n / est, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=(f"{wl.name}: the {n}-token chunk's store, selection (all rows), ensure and fetch for all "
+                        f"{wl.num_layers} layers ({base_s:.1f}s), attention for {len(rows)} of the {n} rows of "
+                        f"every layer (every {n // len(rows)}th, {spent['attn']:.1f}s), scaled to the chunk: "
+                        f"{est:.1f}s; untimed: setup {setup_s:.1f}s, page-row rebuild {spent['rebuild']:.1f}s; "
+                        f"NumPy with BLAS on {threads} threads"),
+                max_score_bits=round(float(tier.max_score_bits), 2),
+                max_score_abs_sum=round(float(tier.max_certificate), 3))
+
+
+def cpu_child_main(spec_path):
+    """Child process: run the CPU baselines the spec lists, in order, writing
+    the results file after each (so a parent that stops waiting keeps what
+    finished)."""
+    spec = json.load(open(spec_path))
+    sys.stdin.readline()          # the parent says "go" once its GPU measurements are done
+    cores = spec.get("cores")
+    if cores:
+        os.sched_setaffinity(0, cores)
+    from threadpoolctl import threadpool_limits
+    out = {}
+    with threadpool_limits(limits=max(1, len(cores) if cores else os.cpu_count())):
+        for item in spec["runs"]:
+            key = item["key"]
+            t0 = time.perf_counter()
+            try:
+                if item.get("prefill"):
+                    out[key] = cpu_prefill_baseline(key)
+                else:
+                    out[key] = cpu_decode_baseline(key, item["warmup"], item["steps"])
+            except Exception as e:   # reported, never silently dropped
+                out[key] = {"error": f"{type(e).__name__}: {e}"}
+            out[key]["wall_s"] = round(time.perf_counter() - t0, 1)
+            tmp = spec["out"] + ".tmp"
+            json.dump(out, open(tmp, "w"))
+            os.replace(tmp, spec["out"])
+            print(f"[cpu] {key} done in {out[key]['wall_s']}s", file=sys.stderr, flush=True)
+
+
+def start_cpu_child(args, keys):
+    """Starts the CPU-baseline child process before this process uses the GPU
+    (it waits for go_cpu_child, so the oracle never shares the host with the
+    GPU measurements: a busy host slowed the launch-bound passes up to 20x).
+    Returns (process, results path, start time) or None."""
+    import subprocess
+    import tempfile
     try:
-        cores = len(os.sched_getaffinity(0))
+        cores = sorted(os.sched_getaffinity(0))
     except Exception:
-        cores = os.cpu_count()
-    return dict(value=round(nsteps / work, 3), unit="steps/s", cores=1, kind="oracle",
-                sample=(f"first {nsteps} decode steps of {wl.name} (all {wl.num_layers} layers: "
-                        f"select, compact, LRU ensure, fetch, fp64 attention), NumPy with BLAS limited to 1 thread; "
-                        f"untimed: setup {setup_s:.1f}s, lazy page-row rebuild {spent[0]:.1f}s; "
-                        f"host has {cores} cores"))
+        cores = list(range(os.cpu_count() or 1))
+    d = tempfile.mkdtemp(prefix="tkv_cpu_")
+    spec = {"out": os.path.join(d, "cpu.json"), "cores": cores,
+            "runs": [{"key": k, "warmup": args.warmup, "steps": args.steps, "prefill": k == "c5"} for k in keys]}
+    spec_path = os.path.join(d, "spec.json")
+    json.dump(spec, open(spec_path, "w"))
+    proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", spec_path],
+                            stdin=subprocess.PIPE, stdout=subprocess.DEVNULL, stderr=sys.stderr, text=True)
+    return proc, spec["out"], time.perf_counter()
+
+
+def go_cpu_child(child):
+    if child is not None:
+        child[0].stdin.write("go\n")
+        child[0].stdin.flush()
+
+
+def collect_cpu_child(child, t_start, deadline):
+    """Waits for the child until `deadline` seconds after the bench started;
+    then stops it (its own PID) and returns whatever finished."""
+    if child is None:
+        return {}
+    proc, path, _ = child
+    go_cpu_child(child)
+    try:
+        proc.wait(timeout=max(1.0, deadline - (time.perf_counter() - t_start)))
+    except Exception:
+        log("[bench] CPU baselines past the deadline: stopping the child")
+        proc.kill()
+        proc.wait()
+    try:
+        return json.load(open(path))
+    except Exception:
+        return {}
 
 
 def bench_append(torch, key, steps, warmup):
@@ -384,19 +555,22 @@ def bench_host_tail(torch, g, s0, steps):
                     "pool as the fetch path left it; GB/s = last step's host bytes / mean step time"}
 
 
-def bench_prefill(args, torch):
+def bench_prefill(torch, key, warmup, steps, cold_reps=0):
     """c5: one 4,096-token prefill chunk over 65,536 cached tokens, 12 layers:
     write-ensure, then per layer store (write-through) -> select (matrix-core
     indexer, causal per-query top-32) -> ensure -> fetch -> causal sparse
     attention.  Keys, values and queries are generated on the GPU before the
     timed region; the tier is reset and the context rewritten (untimed)
-    before every repetition."""
+    before every repetition.  With `cold_reps`, that many more repetitions
+    start from an empty pool (residency reset after the context is written):
+    layer 0's ensure then misses the cached pages its rows select and its
+    fetch moves them all over the host link."""
     import numpy as np
 
     from workload import gen, get_workload, gpu_gen
     from workload.gpu_run import GpuWorkload
 
-    wl = get_workload(args.config)
+    wl = get_workload(key)
     L, n, start = wl.num_layers, wl.prefill_tokens, wl.contexts[0]
     g = GpuWorkload(wl)
     t = g.tier
@@ -415,11 +589,14 @@ def bench_prefill(args, torch):
     old_len = torch.tensor([start], dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     names = ("store", "select", "ensure", "fetch", "attn")
-    reps = []
-    for rep in range(args.warmup + args.steps):
+    reps, colds = [], []
+    for rep in range(warmup + steps + cold_reps):
+        cold = rep >= warmup + steps
         t.reset_residency()
         t.set_select_width(1, wl.topk, 2 * wl.topk + 8)
         g.setup()
+        if cold:
+            t.reset_residency()
         torch.cuda.synchronize()
         t.set_select_width(1, wl.topk, wl.max_sel_pages)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 5 * L)]
@@ -441,7 +618,14 @@ def bench_prefill(args, torch):
                                 bufs["out"], row_pos=bufs["row_pos"])
             e[4].record(stream)
         torch.cuda.synchronize()
-        if rep < args.warmup:
+        if cold:
+            c = t.read_counters()
+            e = ev[2:7]
+            fetch0 = e[2].elapsed_time(e[3])
+            colds.append(dict(total_ms=ev[0].elapsed_time(ev[-1]), layer0_fetch_ms=fetch0,
+                              misses=c["misses"], bytes_fetched=c["bytes_fetched"]))
+            continue
+        if rep < warmup:
             continue
         split = dict(write_ensure=ev[0].elapsed_time(ev[1]))
         for i, nm in enumerate(names):
@@ -479,7 +663,7 @@ def bench_prefill(args, torch):
         "metric": "prefill chunk tokens/s (4,096 new over 65,536 cached, 12 layers)",
         "value": round(n / (ms["total"] * 1e-3), 1),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms["total"], 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8-e4m3 KV, bf16 q/out, bf16 MFMA indexer, fp32 math", "data": "synthetic",
@@ -507,33 +691,38 @@ def bench_prefill(args, torch):
                           "frac": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12 / 2500.0, 5)},
         "mirror_write_GBps": round(n * tok_bytes * L / (ms["store"] * 1e-3) / 1e9, 2),
         "error_word": c["error_word"],
+        "cold_chunk": ({"ms_per_chunk": round(float(np.mean([x["total_ms"] for x in colds])), 3),
+                        "tokens_per_s": round(n / (float(np.mean([x["total_ms"] for x in colds])) * 1e-3), 1),
+                        "misses": colds[-1]["misses"], "bytes_fetched": colds[-1]["bytes_fetched"],
+                        "layer0_fetch_ms": round(float(np.mean([x["layer0_fetch_ms"] for x in colds])), 3),
+                        "roofline": {"kernel": "k_fetch (layer 0's fetch of the cached pages, all layers' rows)",
+                                     "bound": "host_link",
+                                     "achieved": round(colds[-1]["bytes_fetched"] / (float(np.mean(
+                                         [x["layer0_fetch_ms"] for x in colds])) * 1e-3) / 1e9, 2),
+                                     "peak": LINK_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": round(colds[-1]["bytes_fetched"] / (float(np.mean(
+                                         [x["layer0_fetch_ms"] for x in colds])) * 1e-3) / 1e9 / LINK_PEAK_GBPS,
+                                         4),
+                                     "traffic": None},
+                        "note": "residency reset after the context is written: the chunk's rows select cached "
+                                "pages that are not resident, layer 0's ensure misses them and one fetch moves "
+                                "their rows (every layer) host to device"} if colds else None),
         "cpu_baseline": None,
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by request, one tier per GPU, with no exchange)", file=sys.stderr)
-        sys.exit(2)
+def bench_decode(torch, key, args, headline):
+    """Decode steps of workload `key`: W untimed, K timed (HIP events on the
+    decode stream), then the per-launch passes.  Returns (result, workload
+    runner, split flag, copy stream)."""
     import dataclasses
-
-    import torch
 
     from workload import get_workload
     from workload.gpu_run import GpuWorkload
 
-    base = get_workload(args.config)
-    if base.prefill_tokens:
-        torch.cuda.set_device(0)
-        print(json.dumps(bench_prefill(args, torch)), flush=True)
-        return
+    base = get_workload(key)
     total = args.warmup + args.steps + 2 * args.measure_steps
     wl = dataclasses.replace(base, steps=max(base.steps, total))
-    torch.cuda.set_device(0)
-    calib = calibrate(torch)
-    log(f"[bench] calibration {calib}")
     t0 = time.perf_counter()
     g = GpuWorkload(wl)
     g.setup()
@@ -621,7 +810,7 @@ def main():
         rest = dict(us=rest_us, bytes=rest_bytes, GBps=rest_bytes / (rest_us * 1e-6) / 1e9, launches=len(ev))
         log(f"[bench] rest copy {rest}")
     plain = None
-    if split and not args.no_extras:
+    if split and headline and not args.no_extras:
         # the same steps from the same state through decode_layer, on a second tier
         g2 = GpuWorkload(wl)
         g2.setup()
@@ -650,7 +839,7 @@ def main():
     link_bytes_step = (c1["bytes_fetched"] - c0["bytes_fetched"]) / args.steps
     err = c1["error_word"]
     fetch_share = k["fetch_us"] * wl.num_layers / (ms * 1e3)
-    t_read, t_write = fetch_traffic() if args.config == "c3" else (None, None)
+    t_read, t_write = fetch_traffic() if key == "c3" else (None, None)
     result = {
         "metric": "sparse decode steps/s (all layers) at 196k ctx, top-2048; achieved HBM GB/s",
         "value": round(1e3 / ms, 3),
@@ -675,7 +864,7 @@ def main():
                       "bound": "host_link",
                       "achieved": round(link_bytes_step / (ms * 1e-3) / 1e9, 2), "peak": LINK_PEAK_GBPS,
                       "unit": "GB/s", "frac": round(link_bytes_step / (ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4),
-                      "traffic": split_traffic(misses_step / wl.num_layers) if args.config == "c3" else None,
+                      "traffic": split_traffic(misses_step / wl.num_layers) if key == "c3" else None,
                       "traffic_note": "FETCH_SIZE (the host reads, which pass the L2s) + WRITE_SIZE (the HBM "
                                       "writes): every copied byte counts twice, so 2 x bytes_per_launch is the "
                                       "floor",
@@ -693,7 +882,7 @@ def main():
                        "bytes_per_launch": round(rest["bytes"]), "avg_launch_us": round(rest["us"], 2),
                        "launches": rest["launches"],
                        "traffic": pmc_traffic("c3_pmc_traffic.json", "k_fetch_rest", "tkv_fetch.hip")
-                       if args.config == "c3" else None,
+                       if key == "c3" else None,
                        "note": "HIP events on the copy stream around each call, in steps of their own: there "
                                "the copies do not overlap the next call's slice copy, as they do in the timed "
                                "steps"} if rest else None),
@@ -708,7 +897,8 @@ def main():
                          "bound": "hbm",
                          "achieved": round(k["attn_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(k["attn_GBps"] / HBM_PEAK_GBPS, 4),
-                         "traffic": pmc_traffic("c3_pmc_traffic.json", "k_attn_mfma_split", "tkv_attn_mfma.hip"),
+                         "traffic": pmc_traffic("c3_pmc_traffic.json", "k_attn_mfma_split", "tkv_attn_mfma.hip")
+                         if key == "c3" else None,
                          "bytes_per_launch": k["attn_bytes_per_launch"],
                          "avg_launch_us": round(k["attn_us"], 2)},
         "select_ensure": {"avg_us": round(k["select_ensure_us"], 2),
@@ -716,12 +906,135 @@ def main():
         "link": {"misses_per_step": round(misses_step, 1),
                  "bytes_per_step": round(link_bytes_step),
                  "step_GBps": round(link_bytes_step / (ms * 1e-3) / 1e9, 2)},
-        "calibration": calib,
         "launch": ("hip graph per step" if args.graph else "eager, one C call per layer")
                   + (" (decode_layer_split: copy stream joined once, after the timed steps; rest-copy "
                      "events in %d steps of their own)" % args.measure_steps if split else ""),
         "error_word": err,
     }
+    # per-step HBM bytes the method needs (slab of every visible page, the
+    # selected pages' K/V codes and scales, queries and outputs), all layers
+    qo = 2 * wl.batch * wl.num_q_heads * wl.head_dim * 2
+    step_bytes = wl.num_layers * (int(g.npg_np.sum()) * wl.num_kv_heads * wl.head_dim * 2
+                                  + wl.batch * wl.topk * g.tier.layer_bytes + qo)
+    result["_kernels"] = k
+    result["step_hbm"] = {"bytes_per_step": step_bytes, "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5)}
+    return result, g, split, side
+
+
+def bench_cold_step(torch, g, s0, reps):
+    """c3 from an empty pool: residency reset, then one decode step (all
+    layers through decode_layer: every selected page misses); `reps` times.
+    Link rate = bytes fetched / step time (the copies dominate it)."""
+    import numpy as np
+    wl, t = g.wl, g.tier
+    stream = torch.cuda.current_stream()
+    rec = []
+    for i in range(reps + 1):
+        t.reset_residency()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.decode_step((s0 + i) % g.q.shape[0])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        c = t.read_counters()
+        if i:
+            rec.append((e0.elapsed_time(e1), c["misses"], c["bytes_fetched"]))
+    ms = float(np.mean([r[0] for r in rec]))
+    b = float(np.mean([r[2] for r in rec]))
+    return {"ms_per_step": round(ms, 4), "misses_per_step": round(float(np.mean([r[1] for r in rec])), 1),
+            "bytes_per_step": round(b),
+            "roofline": {"kernel": "k_fetch (each layer's whole-row copy of its misses), over the step",
+                         "bound": "host_link", "achieved": round(b / (ms * 1e-3) / 1e9, 2),
+                         "peak": LINK_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(b / (ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4), "traffic": None},
+            "note": f"residency reset before each of {reps} steps (decode_layer, one stream): every page the "
+                    "step selects misses; achieved = bytes fetched / step time"}
+
+
+def pcie_link(torch):
+    """Negotiated PCIe link of the GPU and of the bridges above it (sysfs)."""
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+    except Exception as e:
+        return {"error": f"no PCI address: {e}"}
+    out = {"device": bdf, "chain": []}
+    path = os.path.realpath(os.path.join("/sys/bus/pci/devices", bdf))
+    for _ in range(6):
+        rec = {"bdf": os.path.basename(path)}
+        for f in ("current_link_speed", "current_link_width", "max_link_speed", "max_link_width"):
+            try:
+                rec[f] = open(os.path.join(path, f)).read().strip()
+            except Exception:
+                pass
+        if len(rec) == 1:
+            break
+        out["chain"].append(rec)
+        path = os.path.dirname(path)
+    return out
+
+
+def decode_summary(r, cpu):
+    """The sub-object of one decode workload in the default line.  Workloads
+    whose timed steps are link-bound (the copies take most of the step: c4)
+    keep the host-link roofline; the others (c1, c2: few or no misses) are
+    priced against HBM on their dominant kernel, the indexer launch or the
+    attention launch, whichever took longer."""
+    keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "decode_path", "roofline",
+            "roofline_hbm", "select_ensure", "link", "step_hbm", "rest_copy", "error_word")
+    out = {"workload": r["config"]["workload"], **{k: r.get(k) for k in keep}}
+    out["metric"] = "decode steps/s (all layers)"
+    link_share = r["link"]["bytes_per_step"] / (r["ms_per_step"] * 1e-3) / 1e9 / LINK_PEAK_GBPS
+    if link_share < 0.25:
+        k = r["_kernels"]
+        sel = {"kernel": "k_select_scan + k_ensure (indexer scan, top-k, compaction; LRU ensure)", "bound": "hbm",
+               "achieved": round(k["select_ensure_GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": round(k["select_ensure_GBps"] / HBM_PEAK_GBPS, 5), "traffic": None,
+               "bytes_per_launch": k["select_bytes_per_launch"], "avg_launch_us": round(k["select_ensure_us"], 2)}
+        att = dict(r["roofline_hbm"])
+        out["roofline_link"] = out["roofline"]
+        if k["select_ensure_us"] >= k["attn_us"]:
+            out["roofline"], out["roofline_hbm"] = sel, att
+        else:
+            out["roofline"], out["roofline_hbm"] = att, sel
+    out["cpu_baseline"] = cpu
+    return out
+
+
+def main():
+    t_start = time.perf_counter()
+    args = parse()
+    if args.cpu_baseline_child:
+        cpu_child_main(args.cpu_baseline_child)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by request, one tier per GPU, with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    others = [] if args.headline_only else [k for k in ("c1", "c2", "c4", "c5") if k != args.config]
+    # the CPU baselines start before this process touches the GPU
+    child = None if args.no_cpu_baseline else start_cpu_child(args, [args.config] + others)
+
+    import torch
+
+    from workload import get_workload
+
+    torch.cuda.set_device(0)
+    base = get_workload(args.config)
+    if base.prefill_tokens:
+        result = bench_prefill(torch, args.config, args.warmup, args.steps, cold_reps=0 if args.headline_only else 2)
+        cpu = collect_cpu_child(child, t_start, args.cpu_deadline)
+        result["cpu_baseline"] = cpu.get(args.config)
+        print(json.dumps(result), flush=True)
+        return
+    calib = calibrate(torch)
+    calib["pcie_link"] = pcie_link(torch)
+    log(f"[bench] calibration {calib}")
+    result, g, split, side = bench_decode(torch, args.config, args, headline=True)
+    result["calibration"] = calib
     if args.no_extras:
         result.update(prefetch=None, host_tail=None, prefix_rehydrate=None, decode_append=None)
     else:
@@ -733,18 +1046,43 @@ def main():
         log(f"[bench] host tail {result['host_tail']}")
         result["prefix_rehydrate"] = bench_prefix(g, 375)
         log(f"[bench] prefix {result['prefix_rehydrate']}")
-        if args.config == "c3":
-            del g
-            torch.cuda.empty_cache()
-            result["decode_append"] = bench_append(torch, "c3a", min(args.steps, 40), 4)
-            log(f"[bench] decode append {result['decode_append']}")
-        else:
-            result["decode_append"] = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(base, args.cpu_steps)
+    if not args.headline_only:
+        result["cold_step"] = bench_cold_step(torch, g, args.warmup + args.steps, 3)
+        log(f"[bench] cold step {result['cold_step']}")
+    if not args.no_extras and args.config == "c3":
+        del g
+        torch.cuda.empty_cache()
+        result["decode_append"] = bench_append(torch, "c3a", min(args.steps, 40), 4)
+        log(f"[bench] decode append {result['decode_append']}")
     else:
-        result["cpu_baseline"] = None
+        result["decode_append"] = None
+        del g
+        torch.cuda.empty_cache()
+    subs = {}
+    for key in others:
+        if key == "c5":
+            r = bench_prefill(torch, key, 1, 3, cold_reps=2)
+            subs[key] = {"workload": r["config"]["workload"], **{k: r[k] for k in (
+                "metric", "value", "unit", "ms_per_step", "steps", "warmup", "split_ms", "roofline",
+                "roofline_mfma", "mirror_write_GBps", "cold_chunk", "error_word")}}
+            subs[key]["roofline_link"] = {"kernel": "k_store (mirror writes of the chunk's new K/V, all layers)",
+                                          "bound": "host_link", "achieved": r["mirror_write_GBps"],
+                                          "peak": LINK_PEAK_GBPS, "unit": "GB/s",
+                                          "frac": round(r["mirror_write_GBps"] / LINK_PEAK_GBPS, 4),
+                                          "traffic": None}
+        else:
+            r, gk, _, _ = bench_decode(torch, key, args, headline=False)
+            subs[key] = decode_summary(r, None)
+            del gk
+            torch.cuda.empty_cache()
+        log(f"[bench] {key}: {subs[key]['value']} {subs[key]['unit']}")
+    cpu = collect_cpu_child(child, t_start, args.cpu_deadline)
+    result["cpu_baseline"] = cpu.get(args.config)
+    for key in subs:
+        subs[key]["cpu_baseline"] = cpu.get(key)
+    result.pop("_kernels", None)
+    result["configs"] = subs
+    result["bench_wall_s"] = round(time.perf_counter() - t_start, 1)
     print(json.dumps(result), flush=True)
 
 

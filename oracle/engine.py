@@ -23,8 +23,7 @@ import numpy as np
 from .attention import attend
 from .layout import RowLayout
 from .lru import LRUState
-from .select import (NO_BITS, ScoreCertificateError, compact_request, lowest_bit_exponent, select_row,
-                     select_rows)
+from .select import NO_BITS, ScoreCertificateError, compact_request, select_row, select_rows
 from .store import read_kv, slab_entry, write_tokens
 
 ERR_NOT_RESIDENT = 4      # store to a page that is not resident (pool not written)
@@ -180,9 +179,13 @@ class OracleTier:
                 # slab: mean of all written keys of the page
                 key = (layer, page)
                 prev = self._partial_sums.pop(key, None) if a > 0 else None
-                s = kk.astype(np.float64).sum(axis=0)
-                sabs = np.abs(kk.astype(np.float64)).sum(axis=0)
-                lsb = lowest_bit_exponent(kk, axis=0)
+                k64 = kk.astype(np.float64)
+                s = k64.sum(axis=0)
+                mags = np.abs(k64)
+                sabs = mags.sum(axis=0)
+                # every fp32 value of magnitude >= m is a multiple of 2^(floor(log2 m) - 23)
+                mn = np.where(mags > 0, mags, np.inf).min(axis=0)
+                lsb = np.where(np.isfinite(mn), np.frexp(np.where(np.isfinite(mn), mn, 1.0))[1] - 24, NO_BITS)
                 if prev is not None:
                     s, sabs, lsb = s + prev[0], sabs + prev[1], np.minimum(lsb, prev[2])
                 self._certify_slab(sabs, lsb, layer, page)
@@ -225,7 +228,8 @@ class OracleTier:
         return sel, needed
 
     def _certify_slab(self, sabs, lsb, layer, page):
-        """Every key of the page (per feature) is a multiple of 2^lsb and the
+        """Every key of the page (per feature) is a multiple of 2^lsb (a lower
+        bound: floor(log2 of the smallest nonzero |key|) - 23) and the
         partial sums stay below sum |key|, so the fp64 sums -- in any order,
         the oracle's and an fp64 accumulator's alike -- are exact when
         sum |key| < 2^(53 + lsb)."""

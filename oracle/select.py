@@ -66,17 +66,11 @@ def lowest_bit_exponent(x: np.ndarray, axis=-1) -> np.ndarray:
     Elements are fp32 values (bf16 values included); zeros are ignored; an
     all-zero vector gives NO_BITS."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    expf = ((u >> 23) & 0xFF).astype(np.int64)
-    man = (u & 0x7FFFFF).astype(np.int64)
-    man = np.where(expf > 0, man | 0x800000, man)          # implicit bit of normal numbers
-    base = np.where(expf > 0, expf - 150, -149)             # exponent of the mantissa's last bit
-    tz = np.zeros_like(man)
-    rest = man.copy()
-    for sh in (16, 8, 4, 2, 1):                             # count trailing zeros
-        low = (rest & ((1 << sh) - 1)) == 0
-        move = low & (rest != 0)
-        tz += np.where(move, sh, 0)
-        rest = np.where(move, rest >> sh, rest)
+    expf = (u >> 23) & 0xFF
+    man = (u & 0x7FFFFF) | np.where(expf > 0, np.uint32(0x800000), np.uint32(0))   # implicit bit
+    low = man & (np.uint32(0) - man)                        # the lowest set bit, a power of two (or 0)
+    tz = np.frexp(low.astype(np.float64))[1] - 1            # its position
+    base = np.where(expf > 0, expf.astype(np.int64) - 150, -149)   # exponent of the mantissa's last bit
     e = np.where(man != 0, base + tz, NO_BITS)
     return e.min(axis=axis)
 

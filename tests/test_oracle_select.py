@@ -265,3 +265,28 @@ def test_select_certificate_holds_on_the_workload_grids():
     t.set_select_width(wl.batch, wl.topk)
     t.select(0, q, np.arange(wl.batch + 1), None, bt, npg, wl.topk)
     assert t.max_score_bits < 24 and t.max_certificate < 2 ** 9
+
+
+def test_lowest_bit_exponent_brute_force():
+    """Per element, the exponent of the lowest set bit of an fp32 value,
+    from its exact integer ratio (normals, subnormals, signs; zeros ignored)."""
+    from oracle.select import NO_BITS, lowest_bit_exponent
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, size=4000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    x = np.concatenate([x, np.float32([0.0, -0.0, 1.0, 2.0 ** -149, 3 * 2.0 ** -140, -1.5, 6.0])])
+
+    def lsb(v):
+        num, den = float(v).as_integer_ratio()
+        num = abs(num)
+        return (num & -num).bit_length() - 1 - (den.bit_length() - 1)
+
+    for v in x:
+        exp = lsb(v) if v != 0 else NO_BITS
+        assert lowest_bit_exponent(np.array([v], dtype=np.float32)) == exp, v
+    m = x.reshape(-1)[: (x.size // 7) * 7].reshape(-1, 7)
+    got = lowest_bit_exponent(m, axis=1)
+    for r in range(m.shape[0]):
+        nz = [lsb(v) for v in m[r] if v != 0]
+        assert got[r] == (min(nz) if nz else NO_BITS)
