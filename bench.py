@@ -164,10 +164,10 @@ def calibrate(torch):
 def measure_kernels(torch, g, start_step, nsteps):
     """Run `nsteps` decode steps through the unfused entry points with HIP
     events around every select+ensure, fetch and attention launch (same
-    stream), synchronising after each layer so that every window measures its
-    own launches from an idle queue (without it, a queue that the host keeps
-    full let one 36 us select window read 700 us in a process that had run
-    other workloads first)."""
+    stream, launched back to back).  Durations are the median over the
+    launches: now and then one window reads 0.7-1.4 ms where the others read
+    30 us (whether the queue runs full or drains between layers), and the
+    mean would be that outlier's."""
     wl, t = g.wl, g.tier
     rs = torch.arange(wl.batch + 1, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -187,13 +187,13 @@ def measure_kernels(torch, g, start_step, nsteps):
             t.sparse_paged_attn(layer, q, rs, g.ctx_len, g.sel[layer], g.bt, g.out[layer])
             e[3].record(stream)
             ev.append(e)
-            torch.cuda.synchronize()
     torch.cuda.synchronize()
     c1 = t.read_counters()
-    sel_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
-    fetch_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev)
+    import numpy as np
     n = len(ev)
+    sel_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * n
+    fetch_ms = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * n
+    attn_ms = float(np.median([e[2].elapsed_time(e[3]) for e in ev])) * n
     fetched = c1["bytes_fetched"] - c0["bytes_fetched"]
     misses = c1["misses"] - c0["misses"]
     # algorithmic bytes
@@ -555,7 +555,7 @@ def bench_host_tail(torch, g, s0, steps):
                     "pool as the fetch path left it; GB/s = last step's host bytes / mean step time"}
 
 
-def bench_prefill(torch, key, warmup, steps, cold_reps=0):
+def bench_prefill(torch, key, warmup, steps, cold_reps=0, split_store=False):
     """c5: one 4,096-token prefill chunk over 65,536 cached tokens, 12 layers:
     write-ensure, then per layer store (write-through) -> select (matrix-core
     indexer, causal per-query top-32) -> ensure -> fetch -> causal sparse
@@ -564,7 +564,9 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
     before every repetition.  With `cold_reps`, that many more repetitions
     start from an empty pool (residency reset after the context is written):
     layer 0's ensure then misses the cached pages its rows select and its
-    fetch moves them all over the host link."""
+    fetch moves them all over the host link.  `split_store`: the stores
+    through tkv_store_kv_mirror_split (mirror writes of whole pages on a
+    second stream beside the selection and the ensure)."""
     import numpy as np
 
     from workload import gen, get_workload, gpu_gen
@@ -588,8 +590,9 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
     run_off = torch.zeros(1, dtype=torch.int32, device="cuda")
     old_len = torch.tensor([start], dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
     names = ("store", "select", "ensure", "fetch", "attn")
-    reps, colds = [], []
+    reps, colds, copy_ms = [], [], []
     for rep in range(warmup + steps + cold_reps):
         cold = rep >= warmup + steps
         t.reset_residency()
@@ -599,14 +602,17 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
             t.reset_residency()
         torch.cuda.synchronize()
         t.set_select_width(1, wl.topk, wl.max_sel_pages)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 5 * L)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 + 5 * L)]   # the last: chunk end
+        evc = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
         ev[0].record(stream)
         t.ensure_write_pages(run_req, run_start, run_len, n, g.bt, old_len)
         ev[1].record(stream)
         for layer in range(L):
             e = ev[2 + 5 * layer: 7 + 5 * layer]
-            t.store_kv_mirror(layer, K[layer], V[layer], run_req, run_start, run_len, run_off, n, g.bt)
+            t.store_kv_mirror(layer, K[layer], V[layer], run_req, run_start, run_len, run_off, n, g.bt,
+                              copy_stream=side if split_store else None)
             e[0].record(stream)
+            evc[layer].record(side)                   # after this layer's mirror copy
             t.select_pages(layer, Q[layer], bufs["row_start"], g.bt, g.n_pages, wl.topk, bufs["sel"],
                            bufs["needed"], row_pos=bufs["row_pos"])
             e[1].record(stream)
@@ -617,6 +623,8 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
             t.sparse_paged_attn(layer, Q[layer], bufs["row_start"], bufs["ctx_len"], bufs["sel"], g.bt,
                                 bufs["out"], row_pos=bufs["row_pos"])
             e[4].record(stream)
+        stream.wait_stream(side)
+        ev[-1].record(stream)
         torch.cuda.synchronize()
         if cold:
             c = t.read_counters()
@@ -640,6 +648,8 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
             split["attn"] += e[3].elapsed_time(e[4])
         split["total"] = ev[0].elapsed_time(ev[-1])
         reps.append(split)
+        # each layer's mirror copy starts when its store's pool part ends
+        copy_ms.append(sum(ev[2 + 5 * layer].elapsed_time(evc[layer]) for layer in range(L)))
     ms = {k: float(np.mean([r[k] for r in reps])) for k in reps[0]}
     # algorithmic work of the last repetition's last layer, scaled by layers
     sel = bufs["sel"].cpu().numpy()
@@ -689,7 +699,14 @@ def bench_prefill(torch, key, warmup, steps, cold_reps=0):
                           "achieved": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12, 2),
                           "peak": 2500.0, "unit": "TFLOP/s",
                           "frac": round(gemm_flop_layer * L / (ms["select"] * 1e-3) / 1e12 / 2500.0, 5)},
-        "mirror_write_GBps": round(n * tok_bytes * L / (ms["store"] * 1e-3) / 1e9, 2),
+        "mirror_write_GBps": round(n * tok_bytes * L / (float(np.mean(copy_ms) if split_store else ms["store"])
+                                                        * 1e-3) / 1e9, 2),
+        "store_path": ("tkv_store_kv_mirror_split: split_ms.store is the pool part on the chunk's stream; the "
+                       "mirror copy runs on a second stream beside the selection and ensure (its time: "
+                       "mirror_copy_ms; mirror_write_GBps = mirror bytes / that time)" if split_store else
+                       "tkv_store_kv_mirror: pool and mirror written by the store kernel "
+                       "(mirror_write_GBps = mirror bytes / store time)"),
+        "mirror_copy_ms": round(float(np.mean(copy_ms)), 3) if split_store else None,
         "error_word": c["error_word"],
         "cold_chunk": ({"ms_per_chunk": round(float(np.mean([x["total_ms"] for x in colds])), 3),
                         "tokens_per_s": round(n / (float(np.mean([x["total_ms"] for x in colds])) * 1e-3), 1),
@@ -1064,7 +1081,13 @@ def main():
             r = bench_prefill(torch, key, 1, 3, cold_reps=2)
             subs[key] = {"workload": r["config"]["workload"], **{k: r[k] for k in (
                 "metric", "value", "unit", "ms_per_step", "steps", "warmup", "split_ms", "roofline",
-                "roofline_mfma", "mirror_write_GBps", "cold_chunk", "error_word")}}
+                "roofline_mfma", "mirror_write_GBps", "store_path", "cold_chunk", "error_word")}}
+            rs = bench_prefill(torch, key, 1, 3, split_store=True)
+            subs[key]["split_store"] = {k: rs[k] for k in ("ms_per_step", "split_ms", "mirror_write_GBps",
+                                                           "mirror_copy_ms", "store_path")}
+            subs[key]["split_store"]["note"] = ("the same chunk with the stores' mirror writes on a second "
+                                                "stream: the store's own time drops, the selection beside "
+                                                "the host writes slows by about as much")
             subs[key]["roofline_link"] = {"kernel": "k_store (mirror writes of the chunk's new K/V, all layers)",
                                           "bound": "host_link", "achieved": r["mirror_write_GBps"],
                                           "peak": LINK_PEAK_GBPS, "unit": "GB/s",

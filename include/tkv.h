@@ -330,6 +330,29 @@ int tkv_store_kv_mirror(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const ui
                         const int32_t* run_len, const int32_t* run_tok_off, int32_t max_run_len,
                         const int32_t* block_table, int32_t max_pages, void* stream);
 
+/* tkv_store_kv_mirror with its mirror writes moved off `stream` (FreeToken
+ * PR #499, "Design": the write-through mirror; here the writes of a run's
+ * whole pages leave after the pool's).  On `stream` the new K/V are
+ * quantised into the pool slots and the slab, and the layer's block of each
+ * page the write begins (the block is then defined in full: written
+ * positions and the zero-filled tail) is built in a staging copy in the
+ * workspace; a copy kernel on `copy_stream` then moves those blocks to the
+ * mirror rows.  Writes that continue a page go to the mirror directly, on
+ * `stream`.  Once `copy_stream` reaches the end of the copy, pool, slab and
+ * mirror hold what tkv_store_kv_mirror writes.  Every later call of this
+ * library that reads or writes the mirror or the pool waits for the copy
+ * (fetches, decode layers, attention, write-ensures, stores, prefix calls,
+ * tkv_read_counters); tkv_select_pages and tkv_lru_ensure run beside it.
+ * A caller that reads the mirror itself first waits for `copy_stream`.
+ * The staging holds one run of max_rows tokens (max_rows/page_size + 1
+ * blocks); blocks past it are written directly.  `copy_stream` NULL or equal
+ * to `stream`: the same as tkv_store_kv_mirror.  Calls on one ctx must not
+ * overlap. */
+int tkv_store_kv_mirror_split(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const uint16_t* v,
+                              int32_t n_runs, const int32_t* run_req, const int32_t* run_start,
+                              const int32_t* run_len, const int32_t* run_tok_off, int32_t max_run_len,
+                              const int32_t* block_table, int32_t max_pages, void* stream, void* copy_stream);
+
 /* Cold-prefix records (FreeToken PR #525, "What the patch does", items
  * 2-4: a prefix leaving the tier is copied out because logical ids get
  * reused; on a later hit it comes back host to host into the mirror and the

@@ -279,3 +279,46 @@ def test_binding_takes_the_compaction_width_from_the_library():
     with pytest.raises(TkvError):
         t.set_select_width(1, 8, 65)                    # more than the 64 slots
     assert t.lib.tkv_select_width(t.ctx) == 5
+
+
+def test_corrupted_mirror_byte_is_caught_after_refetch():
+    """Failure forcing (FreeToken PR #525, commit summary: a mirror that held
+    the wrong bytes corrupted fp8 pages with no error): one byte of a
+    non-resident page's mirror row is flipped from the host, the page is
+    fetched, and the pool-row byte compare against the oracle must report
+    that slot -- at exactly that byte.  With the byte restored and the row
+    fetched again, the compare passes."""
+    import ctypes
+    wl = replace(get_workload("c3s"), name="edge_mirror_corruption", num_layers=2, steps=1)
+    say("[edges] corrupted mirror byte")
+    g, o = _pair(wl)
+    t = g.tier
+    compare_state(g, o, "before the corruption")
+    st = t.read_state()
+    bt, _ = gen.block_tables(wl)
+    page = next(int(p) for p in bt[0] if p >= 0 and st["page_to_slot"][p] < 0)
+    off = t.layer_bytes + 1000                                   # layer 1, inside the K codes
+    ptr = t.lib.tkv_mirror_host_ptr(t.ctx)
+    mir = np.ctypeslib.as_array((ctypes.c_uint8 * (o.N * t.row_bytes)).from_address(ptr)).reshape(o.N, t.row_bytes)
+    good = int(mir[page, off])
+    mir[page, off] = good ^ 0x5A
+    i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device="cuda")
+    out = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    miss = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t.lru_ensure(i32([page]), out, miss, cnt)
+    t.fetch_pages(miss, cnt)
+    out_o, miss_o = o.ensure([page])
+    o.fetch(miss_o)
+    torch.cuda.synchronize()
+    slot = int(out.item())
+    assert slot == int(out_o[0]) >= 0
+    row_g = t.pool_rows()[slot].cpu().numpy()
+    diff = np.nonzero(row_g != o.pool_row(slot))[0]
+    assert list(diff) == [off], diff                             # the compare sees exactly the flipped byte
+    with pytest.raises(AssertionError, match=f"mirror row {page}"):
+        compare_state(g, o, "after the corruption")
+    mir[page, off] = good                                        # restore, fetch the row again into its slot
+    t.fetch_pages(i32([[slot, page]]), i32([1]))
+    o.fetch(np.array([[slot, page]]))
+    compare_state(g, o, "after the restore")

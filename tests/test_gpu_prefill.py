@@ -19,17 +19,21 @@ def _capture(store):
     return on_layer
 
 
-@pytest.mark.parametrize("kernel,ranges", [(0, 0), (0, 16), (1, 0)], ids=["auto", "auto-16-page-ranges", "vector"])
-def test_prefill_small_bit_exact(kernel, ranges):
+@pytest.mark.parametrize("kernel,ranges,split", [(0, 0, False), (0, 16, False), (1, 0, False), (0, 0, True)],
+                         ids=["auto", "auto-16-page-ranges", "vector", "auto-split-store"])
+def test_prefill_small_bit_exact(kernel, ranges, split):
+    """The chunk against the oracle; `split`: the stores' mirror writes of
+    whole pages on a second stream (tkv_store_kv_mirror_split), everything
+    else ordered after them by the library."""
     from workload.gpu_run import GpuWorkload
     wl = get_workload("c5s")
-    say(f"[prefill] {wl.name} attention kernel {kernel}, range pages {ranges}")
+    say(f"[prefill] {wl.name} attention kernel {kernel}, range pages {ranges}, split store {split}")
     g = GpuWorkload(wl)
     g.tier.set_attn_kernel(kernel)
     g.tier.set_attn_range(ranges)
     g.setup()
     got = []
-    g.prefill(on_layer=_capture(got))
+    g.prefill(on_layer=_capture(got), copy_stream=torch.cuda.Stream() if split else None)
     torch.cuda.synchronize()
     o = run.make_tier(wl, materialize=True)
     run.setup(wl, o)

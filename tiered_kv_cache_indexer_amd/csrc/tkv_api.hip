@@ -44,6 +44,12 @@ struct tkv_ctx {
   hipEvent_t ev_slice = nullptr, ev_rest[2] = {nullptr, nullptr};
   bool rest_pending = false, last_split = false;
   unsigned long long rest_cap = 0;
+  // Split store (tkv_store_kv_mirror_split): the staged mirror blocks are
+  // copied on the caller's copy stream; ev_mirror follows the latest copy,
+  // recorded in capture sequence mirror_cap (0: none).
+  hipEvent_t ev_mstage = nullptr, ev_mirror = nullptr;
+  bool mirror_pending = false;
+  unsigned long long mirror_cap = 0;
   int rest_last = 0, chain_len = 0, prev_layer = -1, prev_width = 0;
 };
 
@@ -79,7 +85,8 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_attn_state, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_stage, ws_stage_page, ws_attn_state, ws_total;
+  size_t stage_blocks;
 };
 
 static int validate(const tkv_config* c) {
@@ -159,6 +166,11 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_pmiss = o; o = align256(o + W * 8);
   L.ws_pmiss_count = o; o = align256(o + 4);
   L.ws_bg_miss = o; o = align256(o + 2 * (1 + 2 * W) * 4);
+  // split store staging: one run of max_rows tokens (its pages plus the
+  // boundary block the store grid adds)
+  L.stage_blocks = (R + PS - 1) / PS + 1;
+  L.ws_stage = o; o = align256(o + L.stage_blocks * L.layer);
+  L.ws_stage_page = o; o = align256(o + L.stage_blocks * 4);
   // records of the page-range prefill attention: only configs with more rows than requests
   L.ws_attn_state = o;
   if (c->max_rows > c->max_batch) o = align256(o + R * (size_t)H * ATTN_STATE_FLOATS * 4);
@@ -223,7 +235,8 @@ void tkv_destroy(tkv_ctx* c) {
   if (c->ev_copy) hipEventDestroy(c->ev_copy);
   for (hipEvent_t e : c->ev_rest)
     if (e) hipEventSynchronize(e);
-  for (hipEvent_t e : {c->ev_slice, c->ev_rest[0], c->ev_rest[1]})
+  if (c->ev_mirror) hipEventSynchronize(c->ev_mirror);
+  for (hipEvent_t e : {c->ev_slice, c->ev_rest[0], c->ev_rest[1], c->ev_mstage, c->ev_mirror})
     if (e) hipEventDestroy(e);
   if (c->mirror_host) hipHostFree(c->mirror_host);
   delete c;
@@ -279,6 +292,9 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.pmiss = (int32_t*)(ws + L.ws_pmiss);
   d.pmiss_count = (int32_t*)(ws + L.ws_pmiss_count);
   d.bg_miss = (int32_t*)(ws + L.ws_bg_miss);
+  d.stage = ws + L.ws_stage;
+  d.stage_page = (int32_t*)(ws + L.ws_stage_page);
+  d.stage_blocks = (int)L.stage_blocks;
   d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;
   d.attn_range_pages = ATTN_RANGE_PAGES_DEFAULT;
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
@@ -339,8 +355,20 @@ static unsigned long long capture_id(hipStream_t s) {
 // recorded in another capture sequence (or outside the one `s` records into)
 // is not waited for: a graph holds only its own work, and the caller orders
 // graphs against eager work.
+//
+// It also orders `s` after the latest staged mirror copy of a split store:
+// every call that waits here reads or writes the mirror or the pool (the
+// selection and the ensure do neither and run beside that copy).
+static int wait_mirror(tkv_ctx* c, hipStream_t s) {
+  if (c->mirror_pending && capture_id(s) == c->mirror_cap)
+    HIPCHECK(hipStreamWaitEvent(s, c->ev_mirror, 0), "hipStreamWaitEvent(mirror copy)");
+  return TKV_OK;
+}
+
 static int wait_rest(tkv_ctx* c, hipStream_t s) {
   c->last_split = false;
+  int rc = wait_mirror(c, s);
+  if (rc) return rc;
   if (!c->rest_pending || capture_id(s) != c->rest_cap) return TKV_OK;
   HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last], 0), "hipStreamWaitEvent(rest copy)");
   return TKV_OK;
@@ -376,6 +404,10 @@ static int split_copies(tkv_ctx* c, int layer, const int32_t* miss, const int32_
   }
   const int k = c->chain_len & 1;
   int32_t* keep = c->dev.bg_miss + (size_t)k * (1 + 2 * (size_t)c->cfg.max_width);
+  {
+    int rc = wait_mirror(c, s);   // the copies read mirror rows a split store may still be writing
+    if (rc) return rc;
+  }
   const int nxt = (layer + 1) % L;
   HIPCHECK(launch_fetch_slice(c->dev, miss, miss_count, W, layer, nxt, keep, s), "decode slice fetch launch");
   HIPCHECK(hipEventRecord(c->ev_slice, s), "hipEventRecord");
@@ -664,10 +696,10 @@ int tkv_ensure_write_pages(tkv_ctx* c, int32_t n_runs, const int32_t* run_req, c
   return TKV_OK;
 }
 
-int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,
-                        const int32_t* run_req, const int32_t* run_start, const int32_t* run_len,
-                        const int32_t* run_tok_off, int32_t max_run_len, const int32_t* block_table,
-                        int32_t max_pages, void* stream) {
+static int store_impl(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,
+                      const int32_t* run_req, const int32_t* run_start, const int32_t* run_len,
+                      const int32_t* run_tok_off, int32_t max_run_len, const int32_t* block_table,
+                      int32_t max_pages, void* stream, void* copy_stream, bool split) {
   int rc = need_attached(c);
   if (rc) return rc;
   if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
@@ -679,9 +711,46 @@ int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint
   StoreArgs a{};
   a.layer = layer; a.k = k; a.v = v; a.n_runs = n_runs; a.run_req = run_req; a.run_start = run_start;
   a.run_len = run_len; a.run_tok_off = run_tok_off; a.bt = block_table; a.max_pages = max_pages;
-  WAIT_REST(c, stream);
-  HIPCHECK(launch_store(c->dev, a, max_run_len, (hipStream_t)stream), "store_kv_mirror launch");
+  hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
+  WAIT_REST(c, s);   // also the previous split store's copy, which read the staging buffer
+  if (!split || !cs || cs == s) {
+    HIPCHECK(launch_store(c->dev, a, max_run_len, s), "store_kv_mirror launch");
+    return TKV_OK;
+  }
+  if (!c->ev_mirror) {
+    HIPCHECK(hipEventCreateWithFlags(&c->ev_mstage, hipEventDisableTiming), "hipEventCreate");
+    HIPCHECK(hipEventCreateWithFlags(&c->ev_mirror, hipEventDisableTiming), "hipEventCreate");
+  }
+  const int ppr = (max_run_len + c->cfg.page_size - 1) / c->cfg.page_size + 1;
+  const int64_t blocks = (int64_t)n_runs * ppr;
+  a.stage = c->dev.stage;
+  a.stage_page = c->dev.stage_page;
+  a.stage_blocks = c->dev.stage_blocks;
+  HIPCHECK(launch_store(c->dev, a, max_run_len, s), "store_kv_mirror_split launch");
+  HIPCHECK(hipEventRecord(c->ev_mstage, s), "hipEventRecord");
+  HIPCHECK(hipStreamWaitEvent(cs, c->ev_mstage, 0), "hipStreamWaitEvent");
+  HIPCHECK(launch_mirror_copy(c->dev, layer, (int)std::min<int64_t>(blocks, c->dev.stage_blocks), cs),
+           "mirror copy launch");
+  HIPCHECK(hipEventRecord(c->ev_mirror, cs), "hipEventRecord");
+  c->mirror_pending = true;
+  c->mirror_cap = capture_id(s);
   return TKV_OK;
+}
+
+int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,
+                        const int32_t* run_req, const int32_t* run_start, const int32_t* run_len,
+                        const int32_t* run_tok_off, int32_t max_run_len, const int32_t* block_table,
+                        int32_t max_pages, void* stream) {
+  return store_impl(c, layer, k, v, n_runs, run_req, run_start, run_len, run_tok_off, max_run_len, block_table,
+                    max_pages, stream, nullptr, false);
+}
+
+int tkv_store_kv_mirror_split(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,
+                              const int32_t* run_req, const int32_t* run_start, const int32_t* run_len,
+                              const int32_t* run_tok_off, int32_t max_run_len, const int32_t* block_table,
+                              int32_t max_pages, void* stream, void* copy_stream) {
+  return store_impl(c, layer, k, v, n_runs, run_req, run_start, run_len, run_tok_off, max_run_len, block_table,
+                    max_pages, stream, copy_stream, true);
 }
 
 int tkv_read_counters(tkv_ctx* c, tkv_counters* out, void* stream) {

@@ -66,6 +66,9 @@ struct DevCtx {
   int32_t* pmiss_count;     // [1]
   float* attn_state;        // [max_rows][Hkv][ATTN_STATE_FLOATS] page-range attention records (or null)
   int32_t* bg_miss;         // [2][1 + 2*max_width] miss count and list kept for the split copy's later parts
+  uint8_t* stage;           // [stage_blocks][layer_bytes] mirror blocks of the split store, copied later
+  int32_t* stage_page;      // [stage_blocks] logical page of each staged block (-1: none)
+  int stage_blocks;
   int max_rows, max_pages, max_topk, max_batch, max_width;
   int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
   int attn_range_pages;     // pages per range of the multi-pass prefill attention (0 = one pass)
@@ -106,6 +109,9 @@ struct SelArgs {
 };
 
 struct StoreArgs {
+  uint8_t* stage;        // split store: mirror blocks of pages the write begins go here (null: direct)
+  int32_t* stage_page;
+  int stage_blocks;
   int layer;
   const uint16_t* k;
   const uint16_t* v;

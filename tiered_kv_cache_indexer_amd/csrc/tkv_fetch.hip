@@ -18,8 +18,12 @@
 #include "tkv_dev.h"
 #include "tkv_launch.h"
 
+#ifndef FETCH_GRID
 #define FETCH_GRID 1024
+#endif
+#ifndef FETCH_CHUNK
 #define FETCH_CHUNK (64 * 1024)
+#endif
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -71,7 +75,9 @@ hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* mis
 // misses in flight at once) the two together moved 52.3 GB/s on MI355X; with
 // 64-384 workgroups 53.7-54.4 GB/s (+3.5% decode steps at 196k context, with
 // 16 or 12 rest workgroups alike); more loads per thread gained nothing.
+#ifndef SLICE_GRID
 #define SLICE_GRID 256
+#endif
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32_t* miss, const int32_t* miss_count,
                                                            int width, int s0, int s1, int32_t* keep) {
   int m = *miss_count;
@@ -108,8 +114,18 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 // workgroups still keep the link busy.  Timed call by call on MI355X: 8-16
 // workgroups with 4-12 loads per thread move 51-53 GB/s, 32 workgroups 48,
 // 48-64 workgroups 43: more host reads in flight slow the link down.
+#ifndef REST_GRID
 #define REST_GRID 16
+#endif
+#ifndef REST_UNROLL
 #define REST_UNROLL 8
+#endif
+#ifndef REST_CHUNK
+#define REST_CHUNK FETCH_CHUNK
+#endif
+#ifndef REST_MIN_ITEMS
+#define REST_MIN_ITEMS 12
+#endif
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_t* keep, int width, int sa, int sb) {
   int m = keep[0];
   if (m > width) m = width;
@@ -117,7 +133,12 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
   const int64_t nvl = c.layer_bytes / 16;
   const int64_t a = (int64_t)sa * nvl, b = (int64_t)sb * nvl;
   const int64_t nvec = c.row_bytes / 16 - (sa == sb ? 1 : 2) * nvl;
-  const int cpr = (int)((nvec + FETCH_CHUNK / 16 - 1) / (FETCH_CHUNK / 16));
+  // item size from the call's volume: REST_CHUNK items when there are at
+  // least REST_MIN_ITEMS per workgroup, a quarter of that otherwise (few
+  // misses: more, smaller items balance the workgroups)
+  const int64_t big = (int64_t)m * ((nvec + REST_CHUNK / 16 - 1) / (REST_CHUNK / 16));
+  const int64_t cvec = big >= (int64_t)REST_MIN_ITEMS * gridDim.x ? REST_CHUNK / 16 : REST_CHUNK / 64;
+  const int cpr = (int)((nvec + cvec - 1) / cvec);
   const int64_t items = (int64_t)m * cpr;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
     const int mi = (int)(it / cpr), ch = (int)(it - (int64_t)mi * cpr);
@@ -128,8 +149,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
     }
     const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
     u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
-    const int64_t v_end = min(nvec, (int64_t)(ch + 1) * (FETCH_CHUNK / 16));
-    for (int64_t v0 = (int64_t)ch * (FETCH_CHUNK / 16) + threadIdx.x; v0 < v_end; v0 += TKV_BLOCK * REST_UNROLL) {
+    const int64_t v_end = min(nvec, (int64_t)(ch + 1) * cvec);
+    for (int64_t v0 = (int64_t)ch * cvec + threadIdx.x; v0 < v_end; v0 += TKV_BLOCK * REST_UNROLL) {
       u32x4 t[REST_UNROLL];
       int64_t r[REST_UNROLL];
 #pragma unroll

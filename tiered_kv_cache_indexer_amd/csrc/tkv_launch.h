@@ -21,6 +21,7 @@ hipError_t launch_write_ensure(const DevCtx& c, int n_runs, const int32_t* run_r
                                const int32_t* bt, int max_pages, const int32_t* old_len,
                                hipStream_t st);
 hipError_t launch_store(const DevCtx& c, const StoreArgs& a, int max_run_len, hipStream_t st);
+hipError_t launch_mirror_copy(const DevCtx& c, int layer, int blocks, hipStream_t st);
 hipError_t launch_attn(const DevCtx& c, AttnArgs a, hipStream_t st);
 bool attn_mfma_supported(const DevCtx& c);
 hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st);

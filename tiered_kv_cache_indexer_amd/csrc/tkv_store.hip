@@ -53,6 +53,8 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x, j = blockIdx.y;
   const int PS = c.PS, D = c.D;
+  const int blk = r * (int)gridDim.y + j;                  // staging block of the split store
+  if (a.stage && tid == 0 && blk < a.stage_blocks) a.stage_page[blk] = -1;
   const int req = a.run_req[r], start = a.run_start[r], len = a.run_len[r];
   if (len <= 0) return;
   // the grid reaches gridDim.y pages of the run: a longer run is flagged
@@ -72,7 +74,14 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
   }
   const int slot = c.page_to_slot[page];
   if (slot < 0 && tid == 0) set_error(c.hdr, DERR_NOT_RESIDENT);
-  uint8_t* mir = c.mirror + (size_t)page * c.row_bytes + (size_t)a.layer * c.layer_bytes;
+  // split store: a write that begins the page defines the page's whole block
+  // of this layer (written positions, zero-filled tail), so it is built in
+  // the staging copy and moved to the mirror afterwards; other writes go to
+  // the mirror directly
+  const bool staged = a.stage && off == 0 && blk < a.stage_blocks;
+  uint8_t* mir = staged ? a.stage + (size_t)blk * c.layer_bytes
+                        : c.mirror + (size_t)page * c.row_bytes + (size_t)a.layer * c.layer_bytes;
+  if (staged && tid == 0) a.stage_page[blk] = page;
   uint8_t* pol = slot >= 0 ? c.pool + (size_t)slot * c.row_bytes + (size_t)a.layer * c.layer_bytes : nullptr;
   const size_t cb = (size_t)c.code_bytes;
   const int tok_first = a.run_tok_off[r] + (t0 - start);  // input row of page position `off`
@@ -309,6 +318,45 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
     const int64_t nb = (int64_t)(n + (off == 0 ? PS - n : 0)) * tok_bytes;
     atomicAdd((unsigned long long*)&c.hdr->counters[CNT_BYTES_MIRRORED], (unsigned long long)nb);
   }
+}
+
+// The split store's second half: each staged block (one per store
+// workgroup) to its page's mirror row, this layer's block.  A small grid
+// walks (block, 16 KiB part) items with four 16-byte vectors in flight per
+// thread: like the rest-of-rows copy's host reads, host writes from a grid
+// spread over every CU slow the kernels running beside them (the selection
+// of a 4,096-row chunk took 0.13 ms a layer instead of 0.06 with 260
+// workgroups writing).
+#ifndef MIRROR_COPY_GRID
+#define MIRROR_COPY_GRID 16
+#endif
+__global__ __launch_bounds__(TKV_BLOCK) void k_mirror_copy(DevCtx c, int layer, int blocks) {
+  constexpr int PART = 16384 / 16;            // vectors per item
+  const int64_t nvec = c.layer_bytes / 16;
+  const int parts = (int)((nvec + PART - 1) / PART);
+  const int items = blocks * parts;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int b = it / parts, part = it - b * parts;
+    const int page = c.stage_page[b];
+    if (page < 0 || (int64_t)page >= c.N) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(c.stage + (size_t)b * c.layer_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(c.mirror + (size_t)page * c.row_bytes + (size_t)layer * c.layer_bytes);
+    const int64_t v0 = (int64_t)part * PART, v1 = min(nvec, v0 + PART);
+    for (int64_t v = v0 + threadIdx.x; v < v1; v += 4 * TKV_BLOCK) {
+      uint4 t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v + u * TKV_BLOCK < v1) t[u] = src[v + u * TKV_BLOCK];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (v + u * TKV_BLOCK < v1) dst[v + u * TKV_BLOCK] = t[u];
+    }
+  }
+}
+
+hipError_t launch_mirror_copy(const DevCtx& c, int layer, int blocks, hipStream_t st) {
+  hipLaunchKernelGGL(k_mirror_copy, dim3(MIRROR_COPY_GRID), dim3(TKV_BLOCK), 0, st, c, layer, blocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_store(const DevCtx& c, const StoreArgs& a, int max_run_len, hipStream_t st) {

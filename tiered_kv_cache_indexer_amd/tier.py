@@ -186,13 +186,17 @@ class TieredKV:
             _ptr(old_len, torch.int32, "old_len"), _stream(stream)))
 
     def store_kv_mirror(self, layer, k, v, run_req, run_start, run_len, run_tok_off, max_run_len,
-                        block_table, stream=None):
-        check(self.lib.tkv_store_kv_mirror(
-            self.ctx, layer, _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), run_req.numel(),
-            _ptr(run_req, torch.int32, "run_req"), _ptr(run_start, torch.int32, "run_start"),
-            _ptr(run_len, torch.int32, "run_len"), _ptr(run_tok_off, torch.int32, "run_tok_off"),
-            max_run_len, _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
-            _stream(stream)))
+                        block_table, stream=None, copy_stream=None):
+        """With `copy_stream`: tkv_store_kv_mirror_split (the mirror writes of
+        whole pages on that stream, after the pool's)."""
+        args = (self.ctx, layer, _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), run_req.numel(),
+                _ptr(run_req, torch.int32, "run_req"), _ptr(run_start, torch.int32, "run_start"),
+                _ptr(run_len, torch.int32, "run_len"), _ptr(run_tok_off, torch.int32, "run_tok_off"),
+                max_run_len, _ptr(block_table, torch.int32, "block_table"), block_table.shape[1], _stream(stream))
+        if copy_stream is None:
+            check(self.lib.tkv_store_kv_mirror(*args))
+        else:
+            check(self.lib.tkv_store_kv_mirror_split(*args, _stream(copy_stream)))
 
     # ------------------------------------------------------------ readout ---
     def read_counters(self, stream=None) -> dict:

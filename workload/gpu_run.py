@@ -194,9 +194,11 @@ class GpuWorkload:
             ctx_len=torch.tensor([wl.contexts[0] + n], dtype=torch.int32, device="cuda"),
         )
 
-    def prefill(self, bufs=None, on_layer=None):
+    def prefill(self, bufs=None, on_layer=None, copy_stream=None):
         """The prefill chunk of request 0: one write-ensure, then per layer
-        store -> select (causal rows) -> ensure -> fetch -> attention."""
+        store -> select (causal rows) -> ensure -> fetch -> attention.  With
+        `copy_stream`, the stores are split: whole pages' mirror writes run on
+        that stream beside the selection and the ensure."""
         wl, t = self.wl, self.tier
         bufs = bufs or self.prefill_buffers()
         start, n = wl.contexts[0], wl.prefill_tokens
@@ -210,7 +212,8 @@ class GpuWorkload:
         for layer in range(wl.num_layers):
             gpu_gen.tokens(wl, gen.KIND_K, layer, 0, start, n, out=bufs["k"])
             gpu_gen.tokens(wl, gen.KIND_V, layer, 0, start, n, out=bufs["v"])
-            t.store_kv_mirror(layer, bufs["k"], bufs["v"], run_req, run_start, run_len, run_off, n, self.bt)
+            t.store_kv_mirror(layer, bufs["k"], bufs["v"], run_req, run_start, run_len, run_off, n, self.bt,
+                              copy_stream=copy_stream)
             gpu_gen.tokens(wl, gen.KIND_Q, layer, 0, 0, n, out=bufs["q"])
             t.select_pages(layer, bufs["q"], bufs["row_start"], self.bt, self.n_pages, wl.topk,
                            bufs["sel"], bufs["needed"], row_pos=bufs["row_pos"])
