@@ -457,11 +457,15 @@ def bench_append(torch, key, steps, warmup):
     return out
 
 
-def bench_prefetch(torch, g, s0, steps):
+def bench_prefetch(torch, g, s0, steps, base_ms, base_misses, link_util):
     """Decode steps with the top-k preload: layer l preloads the page list
     layer l+1 needed last time, its copy on a second stream under layer l's
     selection (tkv_decode_layer_prefetch).  Continues from the tier state the
-    fetch path left."""
+    fetch path left.  Also the gate the runner applies: the preload is used
+    only when the link has idle time (the timed steps moved less than 0.85
+    of the measured pinned-copy ceiling) and it does not add link bytes
+    (misses per step with it at most 2% above those without); otherwise the
+    steps run without it, at the headline's speed."""
     wl, t = g.wl, g.tier
     n_q = g.q.shape[0]
     side = torch.cuda.Stream()
@@ -492,11 +496,19 @@ def bench_prefetch(torch, g, s0, steps):
             if a:
                 shares.append(len(a & b) / len(a))
         prev = cur
+    misses = (c1["misses"] - c0["misses"]) / steps
+    enabled = link_util < 0.85 and misses <= 1.02 * base_misses
     return {"ms_per_step": round(ms, 4), "steps_per_s": round(1e3 / ms, 2),
-            "misses_per_step": round((c1["misses"] - c0["misses"]) / steps, 1),
+            "misses_per_step": round(misses, 1),
             "link_bytes_per_step": round((c1["bytes_fetched"] - c0["bytes_fetched"]) / steps),
             "prediction_hit_share": round(float(np.mean(shares)), 3),
-            "note": "misses include the preloads'; prediction = the next layer's last needed list"}
+            "note": "misses include the preloads'; prediction = the next layer's last needed list",
+            "gated": {"link_util": round(link_util, 3), "misses_per_step_without": round(base_misses, 1),
+                      "enabled": bool(enabled),
+                      "ms_per_step": round(ms if enabled else base_ms, 4),
+                      "steps_per_s": round(1e3 / (ms if enabled else base_ms), 2),
+                      "rule": "preload only when the link moved < 0.85 of the pinned-copy ceiling and the preload "
+                              "adds at most 2% misses; else the steps run without it"}}
 
 
 def bench_prefix(g, n):
@@ -822,7 +834,8 @@ def bench_decode(torch, key, args, headline):
         torch.cuda.synchronize()
         cr1 = g.tier.read_counters()
         s_next += args.measure_steps
-        rest_us = 1e3 * sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        import numpy as np
+        rest_us = 1e3 * float(np.median([a.elapsed_time(b) for a, b in ev]))   # median: see measure_kernels
         rest_bytes = (cr1["bytes_fetched"] - cr0["bytes_fetched"]) * (L - 2) / L / len(ev)
         rest = dict(us=rest_us, bytes=rest_bytes, GBps=rest_bytes / (rest_us * 1e-6) / 1e9, launches=len(ev))
         log(f"[bench] rest copy {rest}")
@@ -1055,8 +1068,10 @@ def main():
     if args.no_extras:
         result.update(prefetch=None, host_tail=None, prefix_rehydrate=None, decode_append=None)
     else:
+        link_util = result["link"]["step_GBps"] / max(1e-9, calib["h2d_memcpy_GBps"])
         result["prefetch"] = bench_prefetch(torch, g, args.warmup + args.steps + args.measure_steps,
-                                            min(args.steps, 50))
+                                            min(args.steps, 50), result["ms_per_step"],
+                                            result["link"]["misses_per_step"], link_util)
         log(f"[bench] prefetch {result['prefetch']}")
         result["host_tail"] = bench_host_tail(torch, g, args.warmup + args.steps + args.measure_steps,
                                               min(args.steps, 50))

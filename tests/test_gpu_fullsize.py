@@ -128,3 +128,59 @@ def test_c5_fullsize_prefill():
             assert_close(out, ref, f"{where}: attention")
     new_pages = list(range(wl.contexts[0] // wl.page_size, wl.num_logical_pages))
     compare_state(g, o, "c5 after the chunk", sample_pages=new_pages[:3] + new_pages[-2:])
+
+
+def test_c3_fullsize_steady_state_split():
+    """The bench's timed window at full size: steps 0-2 through decode_layer,
+    then decode_layer_split with the copy stream joined only where a step is
+    compared (as the bench joins it once, after its timed steps); every layer
+    of steps 5 and 24 (the first and last timed steps of the driver's
+    5 warmup + 20 timed steps) against the oracle -- selections, compaction,
+    slot maps, miss lists -- LRU state and counters at steps 5, 14 and 24,
+    attention on two layers of step 24, pool rows of pages copied then."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c3")
+    say(f"[fullsize] c3 steady state: {wl.description}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    o = run.make_tier(wl, materialize=False)
+    run.setup(wl, o)
+    say("[fullsize] c3 steady state: setups done")
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    side = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+    check_layers, check_state, attn_step = {5, 24}, {5, 14, 24}, 24
+    rng = np.random.default_rng(11)
+    for s in range(25):
+        if s < 3:
+            g.decode_step(s)
+        else:
+            g.decode_step_split(s, side, join=False)
+        if s in check_state:
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+        for layer in range(wl.num_layers):
+            with_attn = s == attn_step and layer in (3, 10)
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias, with_attention=with_attn)
+            if s in check_layers:
+                where = f"c3 steady step {s} layer {layer}"
+                assert np.array_equal(g.sel[layer].cpu().numpy(), rec["sel"]), f"{where}: sel"
+                assert np.array_equal(g.needed[layer].cpu().numpy(), rec["needed"]), f"{where}: needed"
+                assert np.array_equal(g.out_slots[layer].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+                m = int(g.miss_count[layer].item())
+                assert np.array_equal(g.miss[layer].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+                if with_attn:
+                    assert_close(bf16_to_f64(g.out[layer]), rec["out"], f"{where}: attention")
+        if s in check_state:
+            resident = [int(p) for p in o.lru.slot_to_page if p >= 0]
+            picked = sorted(rng.choice(resident, size=4, replace=False).tolist())
+            compare_state(g, o, f"c3 steady step {s}", sample_pages=picked)
+            say(f"[fullsize] c3 steady state: step {s} ok")
+    c = g.tier.read_counters()
+    assert c["error_word"] == 0 and c["drops"] == 0 and c["misses"] > 0
