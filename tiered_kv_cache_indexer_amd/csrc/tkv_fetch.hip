@@ -114,6 +114,17 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 // workgroups still keep the link busy.  Timed call by call on MI355X: 8-16
 // workgroups with 4-12 loads per thread move 51-53 GB/s, 32 workgroups 48,
 // 48-64 workgroups 43: more host reads in flight slow the link down.
+//
+// The stall is per XCD: a host read in flight holds a place in the queue of
+// its XCD's L2 towards the fabric, and other loads of that XCD that miss
+// wait behind it.  Measured with a probe: a 48-workgroup 3 MB HBM read takes
+// 1.3 us alone, 23 us beside this copy spread over the XCDs (8 loads per
+// thread), 6 us with 2 loads per thread at the same 56 GB/s, and 4.0 against
+// 4.1 us when the copy runs on one XCD and the read on the others.  Putting
+// the copy on one XCD and the decode's kernels on the other seven (work
+// claimed by the workgroups placed there) lost in the decode steps: the
+// confined copy moved about half as many bytes beside the decode's kernels,
+// and the claims cost the selection more than it gained.
 #ifndef REST_GRID
 #define REST_GRID 16
 #endif
@@ -126,6 +137,36 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 #ifndef REST_MIN_ITEMS
 #define REST_MIN_ITEMS 12
 #endif
+// loads in flight per thread with the small items: fewer host reads in
+// flight stall the decode's kernels less (measured on the batch-4 workload,
+// where the copy is not the critical path: 2 loads 1.43-1.44 ms per step, 4
+// or 8 loads 1.48-1.53) and the link stays as busy
+#ifndef REST_SMALL_UNROLL
+#define REST_SMALL_UNROLL 2
+#endif
+
+// Vectors [v_begin, v_end) of the rest of one row, U loads in flight per
+// thread: rest vector x is row vector x, stepped over slice sa, then sb.
+template <int U>
+__device__ __forceinline__ void rest_copy_vectors(const u32x4* src, u32x4* dst, int64_t v_begin, int64_t v_end,
+                                                  int64_t a, int64_t b, int64_t nvl, bool two) {
+  for (int64_t v0 = v_begin + threadIdx.x; v0 < v_end; v0 += TKV_BLOCK * U) {
+    u32x4 t[U];
+    int64_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t x = v0 + u * TKV_BLOCK;
+      if (x >= a) x += nvl;
+      if (two && x >= b) x += nvl;
+      r[u] = x;
+      if (v0 + u * TKV_BLOCK < v_end) t[u] = __builtin_nontemporal_load(src + x);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * TKV_BLOCK < v_end) dst[r[u]] = t[u];
+  }
+}
+
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_t* keep, int width, int sa, int sb) {
   int m = keep[0];
   if (m > width) m = width;
@@ -137,7 +178,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
   // least REST_MIN_ITEMS per workgroup, a quarter of that otherwise (few
   // misses: more, smaller items balance the workgroups)
   const int64_t big = (int64_t)m * ((nvec + REST_CHUNK / 16 - 1) / (REST_CHUNK / 16));
-  const int64_t cvec = big >= (int64_t)REST_MIN_ITEMS * gridDim.x ? REST_CHUNK / 16 : REST_CHUNK / 64;
+  const bool large = big >= (int64_t)REST_MIN_ITEMS * gridDim.x;
+  const int64_t cvec = large ? REST_CHUNK / 16 : REST_CHUNK / 64;
   const int cpr = (int)((nvec + cvec - 1) / cvec);
   const int64_t items = (int64_t)m * cpr;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -149,23 +191,9 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
     }
     const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
     u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
-    const int64_t v_end = min(nvec, (int64_t)(ch + 1) * cvec);
-    for (int64_t v0 = (int64_t)ch * cvec + threadIdx.x; v0 < v_end; v0 += TKV_BLOCK * REST_UNROLL) {
-      u32x4 t[REST_UNROLL];
-      int64_t r[REST_UNROLL];
-#pragma unroll
-      for (int u = 0; u < REST_UNROLL; ++u) {
-        // row vector of the u-th rest vector: step over slice sa, then sb
-        int64_t x = v0 + u * TKV_BLOCK;
-        if (x >= a) x += nvl;
-        if (sb != sa && x >= b) x += nvl;
-        r[u] = x;
-        if (v0 + u * TKV_BLOCK < v_end) t[u] = __builtin_nontemporal_load(src + x);
-      }
-#pragma unroll
-      for (int u = 0; u < REST_UNROLL; ++u)
-        if (v0 + u * TKV_BLOCK < v_end) dst[r[u]] = t[u];
-    }
+    const int64_t v_begin = (int64_t)ch * cvec, v_end = min(nvec, v_begin + cvec);
+    if (large) rest_copy_vectors<REST_UNROLL>(src, dst, v_begin, v_end, a, b, nvl, sb != sa);
+    else rest_copy_vectors<REST_SMALL_UNROLL>(src, dst, v_begin, v_end, a, b, nvl, sb != sa);
   }
 }
 
