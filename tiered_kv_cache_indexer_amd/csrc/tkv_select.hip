@@ -220,55 +220,59 @@ __device__ void compact_block(const DevCtx& c, const SelArgs& a, int b, uint32_t
   __syncthreads();
 }
 
+// Slots of every row's selected pages, all rows in one pass (one round trip
+// to memory for any batch): a row that is its request's only row with top-k
+// <= C takes them from the ensure's output (its selection is the needed list,
+// in order); other rows translate page -> slot after the ensure.
 __device__ void write_sel_slots(const DevCtx& c, const SelArgs& a) {
-  for (int b = 0; b < a.B; ++b) {
-    const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
-    const bool direct = (r1 - r0 == 1) && (a.topk <= a.C);
-    const int32_t* btb = a.bt + (size_t)b * a.max_pages;
-    for (int idx = threadIdx.x; idx < (r1 - r0) * a.topk; idx += TKV_BLOCK) {
-      const int i = a.sel_local[(size_t)r0 * a.topk + idx];
-      int slot = -1;
-      if (i >= 0 && i < a.max_pages) {
-        if (direct) {
-          slot = a.out_slots[(size_t)b * a.C + idx];
-        } else {
-          const int p = btb[i];
-          if (p >= 0 && (int64_t)p < c.N) slot = c.page_to_slot[p];
-        }
+  const int n = a.rows * a.topk;
+  for (int e = threadIdx.x; e < n; e += TKV_BLOCK) {
+    const int r = e / a.topk, j = e - r * a.topk;
+    const int b = request_of_row(a.row_start, a.B, r);
+    const int i = a.sel_local[e];
+    int slot = -1;
+    if (i >= 0 && i < a.max_pages) {
+      if (a.row_start[b + 1] - a.row_start[b] == 1 && a.topk <= a.C) {
+        slot = a.out_slots[(size_t)b * a.C + j];
+      } else {
+        const int p = a.bt[(size_t)b * a.max_pages + i];
+        if (p >= 0 && (int64_t)p < c.N) slot = c.page_to_slot[p];
       }
-      a.sel_slots[(size_t)r0 * a.topk + idx] = slot;
     }
+    a.sel_slots[e] = slot;
   }
 }
 
 // Shared tail once every row's selection is written: compaction and ensure.
-// A request with one row: its selection is already ascending and unique, so
-// the compaction is a block-table lookup of the first C entries.
-__device__ void compact_single_row(const DevCtx& c, const SelArgs& a, int b, int r, int* sm_scan) {
-  const int32_t* sel = a.sel_local + (size_t)r * a.topk;
-  const int32_t* btb = a.bt + (size_t)b * a.max_pages;
-  int32_t* nd = a.needed + (size_t)b * a.C;
-  int valid = 0;
-  for (int j = threadIdx.x; j < a.topk; j += TKV_BLOCK) valid += sel[j] >= 0;
-  const int u = block_sum(valid, sm_scan);
-  for (int j = threadIdx.x; j < a.C; j += TKV_BLOCK) {
-    int v = -1;
-    if (j < a.topk) {
-      const int i = sel[j];
-      if (i >= 0 && i < a.max_pages) v = btb[i];
+// Requests with one row, all in one pass (one round trip for the selections
+// and one for the block table, whatever the batch): such a row's selection
+// is already ascending and unique, so its compaction is a block-table lookup
+// of the first C entries, and each valid entry past C is a drop.
+__device__ void compact_single_rows(const DevCtx& c, const SelArgs& a, int* sm_scan) {
+  const int J = a.topk > a.C ? a.topk : a.C;
+  int drops = 0;
+  for (int e = threadIdx.x; e < a.B * J; e += TKV_BLOCK) {
+    const int b = e / J, j = e - b * J;
+    const int r = a.row_start[b];
+    if (a.row_start[b + 1] - r != 1) continue;
+    const int i = j < a.topk ? a.sel_local[(size_t)r * a.topk + j] : -1;
+    if (j < a.C) {
+      int v = -1;
+      if (i >= 0 && i < a.max_pages) v = a.bt[(size_t)b * a.max_pages + i];
+      a.needed[(size_t)b * a.C + j] = v;
+    } else if (i >= 0) {
+      ++drops;
     }
-    nd[j] = v;
   }
-  if (threadIdx.x == 0 && u > a.C) c.hdr->counters[CNT_DROPS] += u - a.C;
+  drops = block_sum(drops, sm_scan);
+  if (threadIdx.x == 0 && drops > 0) c.hdr->counters[CNT_DROPS] += drops;
   __syncthreads();
 }
 
 __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan) {
-  for (int b = 0; b < a.B; ++b) {
-    const int r0 = a.row_start[b], r1 = a.row_start[b + 1];
-    if (r1 - r0 == 1) compact_single_row(c, a, b, r0, sm_scan);
-    else compact_block(c, a, b, dyn, sm_scan);
-  }
+  compact_single_rows(c, a, sm_scan);
+  for (int b = 0; b < a.B; ++b)
+    if (a.row_start[b + 1] - a.row_start[b] != 1) compact_block(c, a, b, dyn, sm_scan);
   if (a.do_ensure) {
     EnsureOut o{a.out_slots, a.miss, a.miss_count};
     lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan, dyn);   // dyn is free after the compaction
