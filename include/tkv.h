@@ -197,7 +197,11 @@ int tkv_lru_ensure(tkv_ctx* ctx, const int32_t* needed, int32_t width, const uin
 /* Fused host->device page copy (PR #499 "Design": one launch copies K+V of
  * a page across all layers; PR #525 commit summary: with the scale banks):
  * pool row miss[i][0] := mirror row miss[i][1] for i < *miss_count, all
- * layers, codes and scales.  `width` bounds *miss_count (fixed launch shape). */
+ * layers, codes and scales.  `width` bounds *miss_count (fixed launch shape).
+ * The miss list is one an ensure of this ctx wrote (tkv_lru_ensure): that
+ * ensure completed the mirror rows of its misses from any block a split
+ * store still held in its staging copy, so the fetch does not wait for a
+ * split store's mirror copy. */
 int tkv_fetch_pages(tkv_ctx* ctx, const int32_t* miss, const int32_t* miss_count, int32_t width,
                     void* stream);
 
@@ -339,19 +343,32 @@ int tkv_store_kv_mirror(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const ui
  * workspace; a copy kernel on `copy_stream` then moves those blocks to the
  * mirror rows.  Writes that continue a page go to the mirror directly, on
  * `stream`.  Once `copy_stream` reaches the end of the copy, pool, slab and
- * mirror hold what tkv_store_kv_mirror writes.  Every later call of this
- * library that reads or writes the mirror or the pool waits for the copy
- * (fetches, decode layers, attention, write-ensures, stores, prefix calls,
- * tkv_read_counters); tkv_select_pages and tkv_lru_ensure run beside it.
- * A caller that reads the mirror itself first waits for `copy_stream`.
- * The staging holds one run of max_rows tokens (max_rows/page_size + 1
- * blocks); blocks past it are written directly.  `copy_stream` NULL or equal
- * to `stream`: the same as tkv_store_kv_mirror.  Calls on one ctx must not
- * overlap. */
+ * mirror hold what tkv_store_kv_mirror writes.
+ * When `stream` is not being captured, the copy is enqueued later: by the
+ * next attention call on the ctx (tkv_sparse_paged_attn, a decode layer),
+ * ordered after that call's position on `stream` so that it runs beside the
+ * attention, or by any earlier call that needs the mirror, or by
+ * tkv_mirror_flush.  Calls that read or write the mirror wait for it
+ * (stores, write-ensures, prefix calls, host-tail attention, tkv_read_
+ * counters and the debug readbacks); ensures meanwhile copy the staged
+ * block of any page they make a fetch of into its mirror row first, so
+ * fetches and the copies of decode layers need no wait; tkv_select_pages,
+ * tkv_lru_ensure and attention over the pool run beside the copy.  A caller
+ * that reads the mirror itself first calls tkv_mirror_flush and waits for
+ * `stream`.  The staging holds one run of max_rows tokens (max_rows/
+ * page_size + 1 blocks); blocks past it are written directly.  `copy_stream`
+ * NULL or equal to `stream`: the same as tkv_store_kv_mirror.  Calls on one
+ * ctx must not overlap. */
 int tkv_store_kv_mirror_split(tkv_ctx* ctx, int32_t layer, const uint16_t* k, const uint16_t* v,
                               int32_t n_runs, const int32_t* run_req, const int32_t* run_start,
                               const int32_t* run_len, const int32_t* run_tok_off, int32_t max_run_len,
                               const int32_t* block_table, int32_t max_pages, void* stream, void* copy_stream);
+
+/* Enqueues the mirror copy a split store deferred (if any) and orders
+ * `stream` after it (the write-through mirror of FreeToken PR #499,
+ * "Design", complete from `stream`'s point of view).  Fails with
+ * TKV_E_STATE when the deferred copy's store stream is being captured. */
+int tkv_mirror_flush(tkv_ctx* ctx, void* stream);
 
 /* Cold-prefix records (FreeToken PR #525, "What the patch does", items
  * 2-4: a prefix leaving the tier is copied out because logical ids get

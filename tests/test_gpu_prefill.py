@@ -140,3 +140,56 @@ def test_range_passes_equal_single_pass(pages):
         outs.append(out)
     assert torch.equal(outs[0], outs[1])
     assert torch.equal(outs[0], bufs["out"])
+
+
+def test_split_store_page_evicted_and_fetched_before_its_mirror_copy():
+    """A page a split store began is evicted and fetched again before any
+    attention call enqueued the store's deferred mirror copy: the ensure
+    completes the page's mirror row from the staging copy, so the fetched
+    pool row holds the stored bytes (checked before anything waits for the
+    copy), and after the copy the whole state equals the oracle's."""
+    from dataclasses import replace
+
+    from workload import gpu_gen
+    from workload.gpu_run import GpuWorkload
+    wl = replace(get_workload("c5s"), name="c5_small_prefill_tiny_pool", num_slots=24, setup_chunk=1024)
+    say(f"[prefill] {wl.name}: split store, evict, refetch before the mirror copy")
+    g = GpuWorkload(wl)
+    g.setup()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    t = g.tier
+    PS = wl.page_size
+    start, n = wl.contexts[0], wl.prefill_tokens
+    bt, _ = gen.block_tables(wl)
+    i32 = lambda xs: torch.tensor(list(xs), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    t.ensure_write_pages(i32([0]), i32([start]), i32([n]), n, g.bt, i32([start]))
+    o.ensure_write_pages([(0, start, n)], bt, [start])
+    layer = 1
+    k = gpu_gen.tokens(wl, gen.KIND_K, layer, 0, start, n)
+    v = gpu_gen.tokens(wl, gen.KIND_V, layer, 0, start, n)
+    t.store_kv_mirror(layer, k, v, i32([0]), i32([start]), i32([n]), i32([0]), n, g.bt, copy_stream=side)
+    run.store_run(o, layer, 0, start, n, gen.kv_tokens(wl, gen.KIND_K, layer, 0, start, n),
+                  gen.kv_tokens(wl, gen.KIND_V, layer, 0, start, n), bt)
+    chunk = [int(p) for p in bt[0, start // PS:(start + n) // PS]]
+    others = [int(p) for p in bt[0, :start // PS]][:wl.num_slots]
+    W = wl.num_slots
+    out_slots = torch.full((W,), -1, dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W, 2), dtype=torch.int32, device="cuda")
+    miss_count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for needed in (others, chunk):          # every slot rebound, then the chunk's pages missed again
+        t.lru_ensure(i32(needed), out_slots[:len(needed)], miss, miss_count)
+        t.fetch_pages(miss, miss_count, width=len(needed))
+        _, misses = o.ensure(np.array(needed, dtype=np.int64))
+        o.fetch(misses)
+        torch.cuda.synchronize()
+        m = int(miss_count.item())
+        assert np.array_equal(miss[:m].cpu().numpy(), misses), f"misses of {needed}"
+    assert {int(p) for p in misses[:, 1]} == set(chunk)
+    pool = t.pool_rows()
+    for p in chunk:
+        s = int(o.lru.page_to_slot[p])
+        assert s >= 0, f"page {p} not resident in the oracle"
+        assert np.array_equal(pool[s].cpu().numpy(), o.pool_row(s)), f"pool row of page {p} (slot {s})"
+    compare_state(g, o, "after the mirror copy")

@@ -78,6 +78,7 @@ SIGNATURES = {
     "tkv_ensure_write_pages": (C.c_int, [P, I32, P, P, P, I32, P, I32, P, P]),
     "tkv_store_kv_mirror": (C.c_int, [P, I32, P, P, I32, P, P, P, P, I32, P, I32, P]),
     "tkv_store_kv_mirror_split": (C.c_int, [P, I32, P, P, I32, P, P, P, P, I32, P, I32, P, P]),
+    "tkv_mirror_flush": (C.c_int, [P, P]),
     "tkv_read_counters": (C.c_int, [P, C.POINTER(Counters), P]),
     "tkv_debug_read_state": (C.c_int, [P, P, P, P, C.POINTER(C.c_int64), P]),
     "tkv_debug_e4m3_encode": (C.c_int, [P, P, I64, P]),

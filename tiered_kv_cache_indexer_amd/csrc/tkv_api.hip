@@ -46,10 +46,17 @@ struct tkv_ctx {
   unsigned long long rest_cap = 0;
   // Split store (tkv_store_kv_mirror_split): the staged mirror blocks are
   // copied on the caller's copy stream; ev_mirror follows the latest copy,
-  // recorded in capture sequence mirror_cap (0: none).
+  // recorded in capture sequence mirror_cap (0: none).  An eager split
+  // store defers that copy (mdefer): the next attention call enqueues it
+  // beside itself, any call that needs the mirror before that enqueues it
+  // first; dev.stage_layer stays set until the next store, so that ensures
+  // meanwhile patch staged blocks into the rows they fetch.
   hipEvent_t ev_mstage = nullptr, ev_mirror = nullptr;
   bool mirror_pending = false;
   unsigned long long mirror_cap = 0;
+  bool mdefer = false;
+  int mdefer_layer = 0, mdefer_blocks = 0;
+  hipStream_t mdefer_s = nullptr, mdefer_cs = nullptr;
   int rest_last = 0, chain_len = 0, prev_layer = -1, prev_width = 0;
 };
 
@@ -235,7 +242,8 @@ void tkv_destroy(tkv_ctx* c) {
   if (c->ev_copy) hipEventDestroy(c->ev_copy);
   for (hipEvent_t e : c->ev_rest)
     if (e) hipEventSynchronize(e);
-  if (c->ev_mirror) hipEventSynchronize(c->ev_mirror);
+  // a deferred mirror copy is dropped with the mirror
+  if (c->ev_mirror && c->mirror_pending) hipEventSynchronize(c->ev_mirror);
   for (hipEvent_t e : {c->ev_slice, c->ev_rest[0], c->ev_rest[1], c->ev_mstage, c->ev_mirror})
     if (e) hipEventDestroy(e);
   if (c->mirror_host) hipHostFree(c->mirror_host);
@@ -295,6 +303,8 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.stage = ws + L.ws_stage;
   d.stage_page = (int32_t*)(ws + L.ws_stage_page);
   d.stage_blocks = (int)L.stage_blocks;
+  d.stage_layer = -1;
+  d.stage_n = 0;
   d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;
   d.attn_range_pages = ATTN_RANGE_PAGES_DEFAULT;
   d.max_rows = f.max_rows; d.max_pages = f.max_pages_per_req; d.max_topk = f.max_topk;
@@ -359,19 +369,53 @@ static unsigned long long capture_id(hipStream_t s) {
 // It also orders `s` after the latest staged mirror copy of a split store:
 // every call that waits here reads or writes the mirror or the pool (the
 // selection and the ensure do neither and run beside that copy).
+// Enqueues a deferred mirror copy on the copy stream of its store, ordered
+// after `s` when `s` is the store's stream and records eagerly (then the copy
+// starts where the caller is now, e.g. beside the attention it is about to
+// launch), else after the store's stream as it stands.
+static int launch_deferred_mirror(tkv_ctx* c, hipStream_t s) {
+  if (!c->mdefer) return TKV_OK;
+  hipStream_t rs = (s == c->mdefer_s && capture_id(s) == 0) ? s : c->mdefer_s;
+  if (capture_id(rs) != 0)
+    return fail(TKV_E_STATE, "a split store's mirror copy is pending on a stream now being captured "
+                             "(call tkv_mirror_flush before the capture)");
+  c->mdefer = false;
+  HIPCHECK(hipEventRecord(c->ev_mstage, rs), "hipEventRecord");
+  HIPCHECK(hipStreamWaitEvent(c->mdefer_cs, c->ev_mstage, 0), "hipStreamWaitEvent");
+  HIPCHECK(launch_mirror_copy(c->dev, c->mdefer_layer, c->mdefer_blocks, c->mdefer_cs), "mirror copy launch");
+  HIPCHECK(hipEventRecord(c->ev_mirror, c->mdefer_cs), "hipEventRecord");
+  c->mirror_pending = true;
+  c->mirror_cap = 0;
+  return TKV_OK;
+}
+
 static int wait_mirror(tkv_ctx* c, hipStream_t s) {
-  if (c->mirror_pending && capture_id(s) == c->mirror_cap)
+  int rc = launch_deferred_mirror(c, s);
+  if (rc) return rc;
+  if (c->mirror_pending && capture_id(s) == c->mirror_cap) {
     HIPCHECK(hipStreamWaitEvent(s, c->ev_mirror, 0), "hipStreamWaitEvent(mirror copy)");
+    // from here on `s` sees the staged blocks in the mirror (which a later
+    // prefix restore may overwrite): nothing left to patch
+    c->dev.stage_layer = -1;
+    c->dev.stage_n = 0;
+  }
+  return TKV_OK;
+}
+
+// Orders `s` after the last rest-of-rows copy only: for fetches (the ensure
+// that produced their miss list patched any staged block into the rows they
+// read) and attention that reads the pool only.
+static int wait_rest_copy(tkv_ctx* c, hipStream_t s) {
+  c->last_split = false;
+  if (!c->rest_pending || capture_id(s) != c->rest_cap) return TKV_OK;
+  HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last], 0), "hipStreamWaitEvent(rest copy)");
   return TKV_OK;
 }
 
 static int wait_rest(tkv_ctx* c, hipStream_t s) {
-  c->last_split = false;
   int rc = wait_mirror(c, s);
   if (rc) return rc;
-  if (!c->rest_pending || capture_id(s) != c->rest_cap) return TKV_OK;
-  HIPCHECK(hipStreamWaitEvent(s, c->ev_rest[c->rest_last], 0), "hipStreamWaitEvent(rest copy)");
-  return TKV_OK;
+  return wait_rest_copy(c, s);
 }
 
 // The copies of a split decode call, issued after its selection and ensure
@@ -404,10 +448,8 @@ static int split_copies(tkv_ctx* c, int layer, const int32_t* miss, const int32_
   }
   const int k = c->chain_len & 1;
   int32_t* keep = c->dev.bg_miss + (size_t)k * (1 + 2 * (size_t)c->cfg.max_width);
-  {
-    int rc = wait_mirror(c, s);   // the copies read mirror rows a split store may still be writing
-    if (rc) return rc;
-  }
+  // (the copies read the mirror rows of this call's misses, which its
+  // ensure completed from any staged blocks: no wait for a mirror copy)
   const int nxt = (layer + 1) % L;
   HIPCHECK(launch_fetch_slice(c->dev, miss, miss_count, W, layer, nxt, keep, s), "decode slice fetch launch");
   HIPCHECK(hipEventRecord(c->ev_slice, s), "hipEventRecord");
@@ -427,6 +469,12 @@ static int split_copies(tkv_ctx* c, int layer, const int32_t* miss, const int32_
 #define WAIT_REST(c, s)                                \
   do {                                                 \
     int rc_ = wait_rest((c), (hipStream_t)(s));        \
+    if (rc_) return rc_;                               \
+  } while (0)
+
+#define WAIT_REST_COPY(c, s)                           \
+  do {                                                 \
+    int rc_ = wait_rest_copy((c), (hipStream_t)(s));   \
     if (rc_) return rc_;                               \
   } while (0)
 
@@ -509,7 +557,7 @@ int tkv_fetch_pages(tkv_ctx* c, const int32_t* miss, const int32_t* miss_count, 
   int rc = need_attached(c);
   if (rc) return rc;
   if (width < 1 || !miss || !miss_count) return fail(TKV_E_INVALID_ARG, "miss, miss_count or width invalid");
-  WAIT_REST(c, stream);
+  WAIT_REST_COPY(c, stream);
   HIPCHECK(launch_fetch(c->dev, miss, miss_count, width, (hipStream_t)stream), "fetch_pages launch");
   return TKV_OK;
 }
@@ -522,7 +570,7 @@ int tkv_fetch_pages_layer(tkv_ctx* c, const int32_t* miss, const int32_t* miss_c
     return fail(TKV_E_INVALID_ARG, "miss, miss_count or width (must be in [1, max_width=%d]) invalid",
                 c->cfg.max_width);
   if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
-  WAIT_REST(c, stream);
+  WAIT_REST_COPY(c, stream);
   HIPCHECK(launch_fetch_slice(c->dev, miss, miss_count, width, layer, layer, c->dev.bg_miss, (hipStream_t)stream),
            "fetch_pages_layer launch");
   return TKV_OK;
@@ -534,7 +582,7 @@ int tkv_fetch_pages_rest(tkv_ctx* c, int32_t width, int32_t layer, void* stream)
   if (width < 1 || width > c->cfg.max_width)
     return fail(TKV_E_INVALID_ARG, "width=%d out of [1, max_width=%d]", width, c->cfg.max_width);
   if (layer < 0 || layer >= c->cfg.num_layers) return fail(TKV_E_INVALID_ARG, "layer=%d out of range", layer);
-  WAIT_REST(c, stream);
+  WAIT_REST_COPY(c, stream);
   HIPCHECK(launch_fetch_rest(c->dev, c->dev.bg_miss, width, layer, layer, (hipStream_t)stream),
            "fetch_pages_rest launch");
   return TKV_OK;
@@ -556,7 +604,13 @@ static int attn_call(tkv_ctx* c, int32_t layer, const uint16_t* q, int32_t rows,
   a.layer = layer; a.q = q; a.rows = rows; a.row_start = row_start; a.row_pos = row_pos;
   a.ctx_len = ctx_len; a.sel = sel_local; a.bt = block_table; a.max_pages = max_pages; a.topk = topk;
   a.B = B; a.out = out; a.host_tail = host_tail;
-  WAIT_REST(c, stream);
+  if (host_tail) {
+    WAIT_REST(c, stream);                        // reads mirror rows
+  } else {
+    // reads the pool only: a deferred mirror copy starts beside it
+    if ((rc = launch_deferred_mirror(c, (hipStream_t)stream))) return rc;
+    WAIT_REST_COPY(c, stream);
+  }
   HIPCHECK(launch_attn(c->dev, a, (hipStream_t)stream), "sparse_paged_attn launch");
   return TKV_OK;
 }
@@ -636,9 +690,10 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   } else {
     // the selection and ensure ran beside a split call's copies (they touch
     // no pool bytes and no kept miss list); the copy waits for them
-    WAIT_REST(c, s);
+    WAIT_REST_COPY(c, s);
     HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
   }
+  if ((rc = launch_deferred_mirror(c, s))) return rc;   // beside the attention
   AttnArgs t{};
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
   t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
@@ -713,6 +768,8 @@ static int store_impl(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16
   a.run_len = run_len; a.run_tok_off = run_tok_off; a.bt = block_table; a.max_pages = max_pages;
   hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
   WAIT_REST(c, s);   // also the previous split store's copy, which read the staging buffer
+  c->dev.stage_layer = -1;   // ... so its staged blocks are in the mirror from here on
+  c->dev.stage_n = 0;
   if (!split || !cs || cs == s) {
     HIPCHECK(launch_store(c->dev, a, max_run_len, s), "store_kv_mirror launch");
     return TKV_OK;
@@ -727,13 +784,25 @@ static int store_impl(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16
   a.stage_page = c->dev.stage_page;
   a.stage_blocks = c->dev.stage_blocks;
   HIPCHECK(launch_store(c->dev, a, max_run_len, s), "store_kv_mirror_split launch");
+  const int nb = (int)std::min<int64_t>(blocks, c->dev.stage_blocks);
+  c->dev.stage_layer = layer;
+  c->dev.stage_n = nb;
+  const unsigned long long cap = capture_id(s);
+  if (cap == 0) {
+    // eager: the copy waits for the next attention call (or a call that needs the mirror)
+    c->mdefer = true;
+    c->mdefer_layer = layer;
+    c->mdefer_blocks = nb;
+    c->mdefer_s = s;
+    c->mdefer_cs = cs;
+    return TKV_OK;
+  }
   HIPCHECK(hipEventRecord(c->ev_mstage, s), "hipEventRecord");
   HIPCHECK(hipStreamWaitEvent(cs, c->ev_mstage, 0), "hipStreamWaitEvent");
-  HIPCHECK(launch_mirror_copy(c->dev, layer, (int)std::min<int64_t>(blocks, c->dev.stage_blocks), cs),
-           "mirror copy launch");
+  HIPCHECK(launch_mirror_copy(c->dev, layer, nb, cs), "mirror copy launch");
   HIPCHECK(hipEventRecord(c->ev_mirror, cs), "hipEventRecord");
   c->mirror_pending = true;
-  c->mirror_cap = capture_id(s);
+  c->mirror_cap = cap;
   return TKV_OK;
 }
 
@@ -743,6 +812,12 @@ int tkv_store_kv_mirror(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint
                         int32_t max_pages, void* stream) {
   return store_impl(c, layer, k, v, n_runs, run_req, run_start, run_len, run_tok_off, max_run_len, block_table,
                     max_pages, stream, nullptr, false);
+}
+
+int tkv_mirror_flush(tkv_ctx* c, void* stream) {
+  int rc = need_attached(c);
+  if (rc) return rc;
+  return wait_mirror(c, (hipStream_t)stream);
 }
 
 int tkv_store_kv_mirror_split(tkv_ctx* c, int32_t layer, const uint16_t* k, const uint16_t* v, int32_t n_runs,

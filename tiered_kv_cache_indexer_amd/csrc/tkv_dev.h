@@ -69,6 +69,9 @@ struct DevCtx {
   uint8_t* stage;           // [stage_blocks][layer_bytes] mirror blocks of the split store, copied later
   int32_t* stage_page;      // [stage_blocks] logical page of each staged block (-1: none)
   int stage_blocks;
+  int stage_layer;          // layer of the staged blocks a split store's mirror copy may not have
+                            // moved yet (-1: none); the ensure patches them into fetched rows
+  int stage_n;              // staged blocks of that store
   int max_rows, max_pages, max_topk, max_batch, max_width;
   int attn_impl;            // ATTN_AUTO / ATTN_VECTOR / ATTN_MATRIX
   int attn_range_pages;     // pages per range of the multi-pass prefill attention (0 = one pass)

@@ -491,9 +491,59 @@ __device__ void lru_ensure_lds(const DevCtx& c, const int32_t* needed, int W, co
   }
 }
 
+// A split store leaves the layer's blocks of the pages it began in a
+// staging copy; a copy kernel moves them to the mirror rows later (beside
+// the next attention).  A page this ensure has to fetch may be one of them
+// -- written, evicted and needed again before that copy ran -- so its
+// staged block is copied to its mirror row here, and the fetch that follows
+// reads the row the pool held (the same bytes the later copy writes there).
+// Misses are matched against the staged pages 256 at a time, the staged
+// page list read through LDS in tiles.
+__device__ void patch_staged_misses(const DevCtx& c, const EnsureOut& o) {
+  constexpr int TILE = 1024;
+  __shared__ int tile[TILE];
+  __shared__ int hit[TKV_BLOCK];
+  __syncthreads();                                         // the miss count and list are written
+  const int m = *o.miss_count;
+  const int L = c.stage_layer;
+  bool patched = false;                                    // uniform
+  for (int base = 0; base < m; base += TKV_BLOCK) {
+    const int i = base + threadIdx.x;
+    const int page = i < m ? o.miss[2 * i + 1] : -1;
+    int found = -1;
+    for (int t0 = 0; t0 < c.stage_n; t0 += TILE) {
+      const int tn = min(TILE, c.stage_n - t0);
+      __syncthreads();
+      for (int u = threadIdx.x; u < tn; u += TKV_BLOCK) tile[u] = c.stage_page[t0 + u];
+      __syncthreads();
+      if (page >= 0 && found < 0)
+        for (int u = 0; u < tn; ++u)
+          if (tile[u] == page) {
+            found = t0 + u;
+            break;
+          }
+    }
+    hit[threadIdx.x] = found;
+    __syncthreads();
+    const int nb = min(TKV_BLOCK, m - base);
+    for (int k = 0; k < nb; ++k) {
+      const int b = hit[k];                                // uniform
+      if (b < 0) continue;
+      patched = true;
+      const int pg = o.miss[2 * (base + k) + 1];
+      const uint4* src = reinterpret_cast<const uint4*>(c.stage + (size_t)b * c.layer_bytes);
+      uint4* dst = reinterpret_cast<uint4*>(c.mirror + (size_t)pg * c.row_bytes + (size_t)L * c.layer_bytes);
+      for (int64_t v = threadIdx.x; v < c.layer_bytes / 16; v += TKV_BLOCK) dst[v] = src[v];
+    }
+    __syncthreads();
+  }
+  if (patched) __threadfence_system();                     // the rows reach host memory before the fetch
+}
+
 // `dyn`: at least lru_lds_words(S) words of dynamic LDS.
 __device__ void lru_ensure_block(const DevCtx& c, const int32_t* needed, int W,
                                  const uint8_t* no_fetch, EnsureOut o, int* sm_scan, uint32_t* dyn) {
   if (W <= LRU_LDS_W && lru_lds_fast_ok(c.S)) lru_ensure_lds(c, needed, W, no_fetch, o, sm_scan, dyn);
   else lru_ensure_global(c, needed, W, no_fetch, o, sm_scan, dyn);
+  if (c.stage_layer >= 0) patch_staged_misses(c, o);
 }

@@ -326,7 +326,9 @@ __global__ __launch_bounds__(store_block<E8>()) void k_store(DevCtx c, StoreArgs
 // thread: like the rest-of-rows copy's host reads, host writes from a grid
 // spread over every CU slow the kernels running beside them (the selection
 // of a 4,096-row chunk took 0.13 ms a layer instead of 0.06 with 260
-// workgroups writing).
+// workgroups writing).  The library enqueues it beside the layer's
+// attention, which it slows by about 2% (8.95 -> 9.1-9.2 ms a 4,096-token
+// chunk), where beside the selection 16 workgroups still doubled that.
 #ifndef MIRROR_COPY_GRID
 #define MIRROR_COPY_GRID 16
 #endif

@@ -188,7 +188,7 @@ class TieredKV:
     def store_kv_mirror(self, layer, k, v, run_req, run_start, run_len, run_tok_off, max_run_len,
                         block_table, stream=None, copy_stream=None):
         """With `copy_stream`: tkv_store_kv_mirror_split (the mirror writes of
-        whole pages on that stream, after the pool's)."""
+        whole pages on that stream, enqueued beside the next attention call)."""
         args = (self.ctx, layer, _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), run_req.numel(),
                 _ptr(run_req, torch.int32, "run_req"), _ptr(run_start, torch.int32, "run_start"),
                 _ptr(run_len, torch.int32, "run_len"), _ptr(run_tok_off, torch.int32, "run_tok_off"),
@@ -213,6 +213,10 @@ class TieredKV:
         check(self.lib.tkv_debug_read_state(self.ctx, p2s.ctypes.data, s2p.ctypes.data, stamp.ctypes.data,
                                             C.byref(clock), _stream(stream)))
         return dict(page_to_slot=p2s, slot_to_page=s2p, stamp=stamp, clock=clock.value)
+
+    def mirror_flush(self, stream=None):
+        """Enqueue a split store's deferred mirror copy and order `stream` after it."""
+        check(self.lib.tkv_mirror_flush(self.ctx, _stream(stream)))
 
     def mirror(self) -> np.ndarray:
         """Read-only view [num_logical_pages][row_bytes] of the pinned mirror."""

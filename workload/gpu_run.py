@@ -198,7 +198,7 @@ class GpuWorkload:
         """The prefill chunk of request 0: one write-ensure, then per layer
         store -> select (causal rows) -> ensure -> fetch -> attention.  With
         `copy_stream`, the stores are split: whole pages' mirror writes run on
-        that stream beside the selection and the ensure."""
+        that stream beside the layer's attention."""
         wl, t = self.wl, self.tier
         bufs = bufs or self.prefill_buffers()
         start, n = wl.contexts[0], wl.prefill_tokens
