@@ -680,7 +680,11 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   a.out_slots = out_slots;
   a.miss = miss;
   a.miss_count = miss_count;
-  a.sel_slots = c->dev.sel_slots;
+  // one row per request: with topk <= C a row's selection is its request's
+  // needed list in order, so the ensure's out_slots are the slots the
+  // attention reads (row stride C); otherwise a translated copy
+  const bool direct = topk <= c->C;
+  a.sel_slots = direct ? nullptr : c->dev.sel_slots;
   HIPCHECK(launch_select_scan(c->dev, a, s), "decode select+ensure launch");
   // the layer's ensure may have rebound a slot the preload copy still writes:
   // its own fetch (and the attention) wait for that copy
@@ -698,7 +702,8 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
   t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
   t.B = B; t.out = out;
-  t.slots = c->dev.sel_slots;
+  t.slots = direct ? out_slots : c->dev.sel_slots;
+  t.slots_stride = direct ? c->C : 0;
   HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");
   return TKV_OK;
 }

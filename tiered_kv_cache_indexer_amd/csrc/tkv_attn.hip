@@ -74,7 +74,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
     const uint8_t* base = nullptr;
     int nt = 0;
     if (a.slots) {
-      const int s = a.slots[(size_t)r * a.topk + j0 + jj];
+      const int s = a.slots[(size_t)r * (a.slots_stride > 0 ? a.slots_stride : a.topk) + j0 + jj];
       if (i >= 0 && s >= 0 && s < c.S) {
         base = c.pool + (size_t)s * c.row_bytes;
         nt = min(PS, limit - i * PS);

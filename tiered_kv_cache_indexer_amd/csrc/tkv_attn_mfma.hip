@@ -385,7 +385,7 @@ __device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, i
     if (j < jend) {
       const int i = a.sel[(size_t)r * a.topk + j];
       if (a.slots) {
-        const int s = a.slots[(size_t)r * a.topk + j];
+        const int s = a.slots[(size_t)r * (a.slots_stride > 0 ? a.slots_stride : a.topk) + j];
         if (i >= 0 && s >= 0 && s < c.S) {
           row = c.pool + (size_t)s * c.row_bytes;
           nt = min(MPS, limit - i * MPS);

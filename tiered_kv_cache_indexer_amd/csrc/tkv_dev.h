@@ -141,6 +141,7 @@ struct AttnArgs {
   int B;
   uint16_t* out;
   const int32_t* slots;  // optional: slots of sel (skips the page->slot translation)
+  int slots_stride;      // row stride of `slots` (0: topk)
   int host_tail;         // read pages that are not resident from their mirror row
   int splits;
   int pages_per_split;

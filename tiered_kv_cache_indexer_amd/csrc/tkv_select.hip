@@ -269,8 +269,33 @@ __device__ void compact_single_rows(const DevCtx& c, const SelArgs& a, int* sm_s
   __syncthreads();
 }
 
-__device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan) {
-  compact_single_rows(c, a, sm_scan);
+// One request with one row r, in the row's last workgroup: the batch's rows
+// compact in parallel, ahead of the call's tail.
+__device__ void compact_one_row(const DevCtx& c, const SelArgs& a, int b, int r, int* sm_scan) {
+  __syncthreads();                                          // the row's selection is written
+  const int J = a.topk > a.C ? a.topk : a.C;
+  int drops = 0;
+  for (int j = threadIdx.x; j < J; j += TKV_BLOCK) {
+    const int i = j < a.topk ? a.sel_local[(size_t)r * a.topk + j] : -1;
+    if (j < a.C) {
+      int v = -1;
+      if (i >= 0 && i < a.max_pages) v = a.bt[(size_t)b * a.max_pages + i];
+      a.needed[(size_t)b * a.C + j] = v;
+    } else if (i >= 0) {
+      ++drops;
+    }
+  }
+  drops = block_sum(drops, sm_scan);
+  if (threadIdx.x == 0 && drops > 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&c.hdr->counters[CNT_DROPS]), (unsigned long long)drops);
+  __syncthreads();
+}
+
+// `rows_compacted`: the one-row requests were compacted by their rows' last
+// workgroups.
+__device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan,
+                              bool rows_compacted) {
+  if (!rows_compacted) compact_single_rows(c, a, sm_scan);
   for (int b = 0; b < a.B; ++b)
     if (a.row_start[b + 1] - a.row_start[b] != 1) compact_block(c, a, b, dyn, sm_scan);
   if (a.do_ensure) {
@@ -407,9 +432,10 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
     row_topk_block(sc, visible, a.topk, out_r, dyn, hist, sm_scan, sm_misc);
   }
   mark_row_pages(c, a, b, r);
+  if (a.row_start[b + 1] - a.row_start[b] == 1) compact_one_row(c, a, b, r, sm_scan);
   // a single row's last workgroup is the last workgroup of the launch
   if (a.rows > 1 && !last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
-  select_finish(c, a, dyn, sm_scan);
+  select_finish(c, a, dyn, sm_scan, true);
 }
 
 // Tail-only launch: scores already in the workspace (prefill scoring kernel).
@@ -582,7 +608,7 @@ __global__ __launch_bounds__(RW_BLOCK) void k_select_rows_wave(DevCtx c, SelArgs
 __global__ __launch_bounds__(TKV_BLOCK) void k_select_finish(DevCtx c, SelArgs a) {
   extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ int sm_scan[8];
-  select_finish(c, a, dyn, sm_scan);
+  select_finish(c, a, dyn, sm_scan, false);
 }
 
 __global__ __launch_bounds__(TKV_BLOCK) void k_ensure(DevCtx c, const int32_t* needed, int W,
