@@ -108,7 +108,7 @@ def test_c5_fullsize_prefill():
     def on_layer(layer, bufs):
         got.append({k: bufs[k].clone() for k in ("sel", "needed", "out_slots", "miss", "miss_count", "out")})
 
-    g.prefill(on_layer=on_layer)
+    g.prefill(on_layer=on_layer, copy_stream=torch.cuda.Stream())   # split stores, as the bench runs the chunk
     torch.cuda.synchronize()
     say("[fullsize] c5: gpu chunk done")
     o = run.make_tier(wl, materialize=False)
