@@ -677,6 +677,7 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   SelArgs a = make_sel(c, layer, q, B, c->dev.iota, nullptr, block_table, max_pages, n_pages, B,
                        page_bias, topk, sel_local, needed);
   a.do_ensure = 1;
+  a.one_row_each = 1;
   a.out_slots = out_slots;
   a.miss = miss;
   a.miss_count = miss_count;
@@ -702,6 +703,7 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   t.layer = layer; t.q = q; t.rows = B; t.row_start = c->dev.iota; t.row_pos = nullptr;
   t.ctx_len = ctx_len; t.sel = sel_local; t.bt = block_table; t.max_pages = max_pages; t.topk = topk;
   t.B = B; t.out = out;
+  t.one_row_each = 1;
   t.slots = direct ? out_slots : c->dev.sel_slots;
   t.slots_stride = direct ? c->C : 0;
   HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");

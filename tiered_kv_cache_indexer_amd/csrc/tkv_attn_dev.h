@@ -69,6 +69,7 @@ __device__ __forceinline__ void attn_merge_splits(const DevCtx& c, const AttnArg
 
 // Request of row r: the last b with row_start[b] <= r.
 __device__ __forceinline__ int attn_row_request(const AttnArgs& a, int r) {
+  if (a.one_row_each) return r;
   int b = 0;
   while (b + 1 < a.B && a.row_start[b + 1] <= r) ++b;
   return b;

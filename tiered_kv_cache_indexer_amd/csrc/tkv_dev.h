@@ -109,6 +109,7 @@ struct SelArgs {
   int32_t* miss;
   int32_t* miss_count;
   int32_t* sel_slots;   // fused path: translated slots of sel_local (or null)
+  int one_row_each;     // 1: row r is request r's only row (row_start = 0, 1, ..., B)
 };
 
 struct StoreArgs {
@@ -142,6 +143,7 @@ struct AttnArgs {
   uint16_t* out;
   const int32_t* slots;  // optional: slots of sel (skips the page->slot translation)
   int slots_stride;      // row stride of `slots` (0: topk)
+  int one_row_each;      // 1: row r is request r's only row (row_start = 0, 1, ..., B)
   int host_tail;         // read pages that are not resident from their mirror row
   int splits;
   int pages_per_split;

@@ -296,8 +296,9 @@ __device__ void compact_one_row(const DevCtx& c, const SelArgs& a, int b, int r,
 __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, int* sm_scan,
                               bool rows_compacted) {
   if (!rows_compacted) compact_single_rows(c, a, sm_scan);
-  for (int b = 0; b < a.B; ++b)
-    if (a.row_start[b + 1] - a.row_start[b] != 1) compact_block(c, a, b, dyn, sm_scan);
+  if (!a.one_row_each)
+    for (int b = 0; b < a.B; ++b)
+      if (a.row_start[b + 1] - a.row_start[b] != 1) compact_block(c, a, b, dyn, sm_scan);
   if (a.do_ensure) {
     EnsureOut o{a.out_slots, a.miss, a.miss_count};
     lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan, dyn);   // dyn is free after the compaction
@@ -322,9 +323,10 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   constexpr int SPL = E8 >= 64 ? E8 / 64 : 1;         // 16-byte segments per lane
   constexpr int LANES = E8 >= 64 ? 64 : E8;           // lanes per page
   constexpr int PASSES = SEL_CHUNK / 4 / PPW;         // wave passes per chunk
-  if (tid == 0) sm_b = request_of_row(a.row_start, a.B, r);
+  // (decode calls: row r is request r, no lookup before the loads below)
+  if (tid == 0 && !a.one_row_each) sm_b = request_of_row(a.row_start, a.B, r);
   __syncthreads();
-  const int b = sm_b;
+  const int b = a.one_row_each ? r : sm_b;
   const int p_begin = chunk * SEL_CHUNK;
   const int32_t* btb = a.bt + (size_t)b * a.max_pages;
   const int sub = lane / LANES, seg0 = lane % LANES;
@@ -431,8 +433,11 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_select_scan(DevCtx c, SelArgs a) 
   } else {
     row_topk_block(sc, visible, a.topk, out_r, dyn, hist, sm_scan, sm_misc);
   }
-  mark_row_pages(c, a, b, r);
-  if (a.row_start[b + 1] - a.row_start[b] == 1) compact_one_row(c, a, b, r, sm_scan);
+  if (a.one_row_each || a.row_start[b + 1] - a.row_start[b] == 1) {
+    compact_one_row(c, a, b, r, sm_scan);
+  } else {
+    mark_row_pages(c, a, b, r);
+  }
   // a single row's last workgroup is the last workgroup of the launch
   if (a.rows > 1 && !last_block_arrive(&c.glob_done[0], a.rows, &sm_misc[2])) return;
   select_finish(c, a, dyn, sm_scan, true);
