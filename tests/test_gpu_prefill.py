@@ -193,3 +193,70 @@ def test_split_store_page_evicted_and_fetched_before_its_mirror_copy():
         assert s >= 0, f"page {p} not resident in the oracle"
         assert np.array_equal(pool[s].cpu().numpy(), o.pool_row(s)), f"pool row of page {p} (slot {s})"
     compare_state(g, o, "after the mirror copy")
+
+
+def test_split_store_pending_rows_reach_host_tail_and_flush():
+    """A split store's deferred mirror copy reached before any attention over
+    the pool: host-tail attention over pages the pool no longer holds (it
+    enqueues the copy and waits for it, then reads the stored rows from the
+    mirror), and tkv_mirror_flush (after which the mirror, read directly,
+    holds the stored rows)."""
+    from dataclasses import replace
+
+    from workload import gpu_gen
+    from workload.gpu_run import GpuWorkload
+    wl = replace(get_workload("c5s"), name="c5_small_prefill_tiny_pool", num_slots=24, setup_chunk=1024)
+    say(f"[prefill] {wl.name}: split store, then host-tail attention and a flush before the mirror copy")
+    g = GpuWorkload(wl)
+    g.setup()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    t = g.tier
+    PS = wl.page_size
+    start, n = wl.contexts[0], wl.prefill_tokens
+    bt, _ = gen.block_tables(wl)
+    i32 = lambda xs: torch.tensor(list(xs), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    chunk = [int(p) for p in bt[0, start // PS:(start + n) // PS]]
+    others = [int(p) for p in bt[0, :start // PS]][:wl.num_slots]
+
+    def split_store(layer, old):
+        t.ensure_write_pages(i32([0]), i32([start]), i32([n]), n, g.bt, i32([old]))
+        o.ensure_write_pages([(0, start, n)], bt, [old])
+        k = gpu_gen.tokens(wl, gen.KIND_K, layer, 0, start, n)
+        v = gpu_gen.tokens(wl, gen.KIND_V, layer, 0, start, n)
+        t.store_kv_mirror(layer, k, v, i32([0]), i32([start]), i32([n]), i32([0]), n, g.bt, copy_stream=side)
+        run.store_run(o, layer, 0, start, n, gen.kv_tokens(wl, gen.KIND_K, layer, 0, start, n),
+                      gen.kv_tokens(wl, gen.KIND_V, layer, 0, start, n), bt)
+
+    layer = 1
+    split_store(layer, start)
+    out_slots = torch.full((len(others),), -1, dtype=torch.int32, device="cuda")
+    miss = torch.zeros((len(others), 2), dtype=torch.int32, device="cuda")
+    miss_count = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t.lru_ensure(i32(others), out_slots, miss, miss_count)        # the chunk's pages leave the pool
+    t.fetch_pages(miss, miss_count)
+    _, misses = o.ensure(np.array(others, dtype=np.int64))
+    o.fetch(misses)
+    assert not any(o.lru.page_to_slot[p] >= 0 for p in chunk)
+    # rows at the chunk's last position, each selecting the chunk's pages
+    rows = 8
+    q = gen.prefill_queries(wl, layer, 0, n)[:rows]
+    qd = torch.from_numpy(gen.to_bf16_bits(q).view(np.int16)).cuda().view(torch.bfloat16)
+    sel = np.full((rows, wl.topk), -1, dtype=np.int32)
+    sel[:, :len(chunk)] = np.arange(start // PS, start // PS + len(chunk))
+    pos = np.full(rows, start + n - 1)
+    out = torch.zeros((rows, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    t.sparse_paged_attn(layer, qd, i32([0, rows]), i32([start + n]), torch.from_numpy(sel).cuda(), g.bt, out,
+                        row_pos=i32(pos), host_tail=True)
+    torch.cuda.synchronize()
+    ref = o.attention(layer, q, np.array([0, rows]), pos, np.array([start + n]), sel, bt, host_tail=True)
+    assert_close(bf16_to_f64(out), ref, "host-tail attention over the split-stored pages")
+    # the chunk's pages back (their rows fetched), another split store, then a flush
+    split_store(0, start + n)
+    t.mirror_flush()
+    torch.cuda.synchronize()
+    mir = t.mirror()
+    for p in chunk:
+        assert np.array_equal(mir[p], o.mirror_row(p)), f"mirror row {p} after the flush"
+    compare_state(g, o, "after the flush")
