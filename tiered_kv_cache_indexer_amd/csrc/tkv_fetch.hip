@@ -70,13 +70,16 @@ hipError_t launch_fetch(const DevCtx& c, const int32_t* miss, const int32_t* mis
 // grid-stride walk over the 16-byte vectors of all of them on SLICE_GRID
 // workgroups.  With `keep` set, block 0 also stores the miss count and list
 // there ([0] = count, then the pairs) for the part that follows.  The grid
-// is a quarter of k_fetch's: this copy shares the link with the previous
+// is an eighth of k_fetch's: this copy shares the link with the previous
 // call's rest copy, and with 1,024 workgroups (every vector of a few dozen
 // misses in flight at once) the two together moved 52.3 GB/s on MI355X; with
 // 64-384 workgroups 53.7-54.4 GB/s (+3.5% decode steps at 196k context, with
 // 16 or 12 rest workgroups alike); more loads per thread gained nothing.
+// Decode steps by grid (batch-4 / 196k thrash, ms): 64 1.354 / 5.08, 96-128
+// 1.36 / 5.066, 192 1.38 / 5.07, 256 1.39 / 5.08, 512 1.39 / 5.13, 1,024
+// 1.39 / 5.23.
 #ifndef SLICE_GRID
-#define SLICE_GRID 256
+#define SLICE_GRID 128
 #endif
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32_t* miss, const int32_t* miss_count,
                                                            int width, int s0, int s1, int32_t* keep) {
