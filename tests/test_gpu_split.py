@@ -52,6 +52,44 @@ def test_split_chain(key):
     assert g.tier.read_counters()["error_word"] == 0
 
 
+def test_split_chain_from_an_empty_pool():
+    """A 12-layer chain (top-24, a pool of three call widths) whose pool is
+    emptied after setup: the first call misses every page it selects (24
+    misses of 11 parts of 64 KiB each, enough for the rest copy's
+    claimed-pieces path), later calls fewer (its dealt-items path); every
+    layer against the oracle, pool and mirror rows included."""
+    from dataclasses import replace
+
+    from workload.gpu_run import GpuWorkload
+    wl = replace(get_workload("c3sc"), name="c3_small_thrash_chain_12_layers", num_layers=12, steps=2, topk=24,
+                 num_slots=168)
+    say(f"[split] {wl.name} from an empty pool")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    o = _oracle(wl)
+    g.tier.reset_residency()
+    o.reset_residency()
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    side = torch.cuda.Stream()
+    misses = []
+    for s in range(wl.steps):
+        g.decode_step_split(s, side)
+        torch.cuda.current_stream().synchronize()
+        for layer in range(wl.num_layers):
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+            compare_layer(g, rec, layer, f"{wl.name} step {s} layer {layer}")
+            misses.append(len(rec["misses"]))
+        compare_state(g, o, f"{wl.name} step {s}", check_rows=True)
+    assert misses[0] == wl.topk and max(misses) * 11 >= 12 * 16   # claimed pieces (12 items per workgroup)
+    assert min(misses) * 11 < 12 * 16                                # dealt items
+    assert g.tier.read_counters()["error_word"] == 0
+
+
 def test_split_then_plain_calls_wait_for_the_rest_copy():
     """Split calls for all but the last layer, no join by the caller; the last
     layer through the plain decode_layer, which orders its copy after the

@@ -92,7 +92,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_stage, ws_stage_page, ws_attn_state, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_stage, ws_stage_page, ws_rest_ctr, ws_attn_state, ws_total;
   size_t stage_blocks;
 };
 
@@ -178,6 +178,7 @@ static Layout make_layout(const tkv_config* c) {
   L.stage_blocks = (R + PS - 1) / PS + 1;
   L.ws_stage = o; o = align256(o + L.stage_blocks * L.layer);
   L.ws_stage_page = o; o = align256(o + L.stage_blocks * 4);
+  L.ws_rest_ctr = o; o = align256(o + 8);
   // records of the page-range prefill attention: only configs with more rows than requests
   L.ws_attn_state = o;
   if (c->max_rows > c->max_batch) o = align256(o + R * (size_t)H * ATTN_STATE_FLOATS * 4);
@@ -303,6 +304,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.stage = ws + L.ws_stage;
   d.stage_page = (int32_t*)(ws + L.ws_stage_page);
   d.stage_blocks = (int)L.stage_blocks;
+  d.rest_ctr = (int32_t*)(ws + L.ws_rest_ctr);
   d.stage_layer = -1;
   d.stage_n = 0;
   d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;

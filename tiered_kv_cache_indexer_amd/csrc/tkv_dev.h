@@ -66,6 +66,7 @@ struct DevCtx {
   int32_t* pmiss_count;     // [1]
   float* attn_state;        // [max_rows][Hkv][ATTN_STATE_FLOATS] page-range attention records (or null)
   int32_t* bg_miss;         // [2][1 + 2*max_width] miss count and list kept for the split copy's later parts
+  int32_t* rest_ctr;        // [2] work counter and finished waves of the rest-of-rows copy (zero between launches)
   uint8_t* stage;           // [stage_blocks][layer_bytes] mirror blocks of the split store, copied later
   int32_t* stage_page;      // [stage_blocks] logical page of each staged block (-1: none)
   int stage_blocks;

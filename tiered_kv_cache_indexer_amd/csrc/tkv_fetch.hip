@@ -109,9 +109,8 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
   }
 }
 
-// Every slice of the kept rows but slices `sa` <= `sb` (equal: one skipped).
-// (miss, 64 KiB item) work items as in k_fetch, on a small grid with eight
-// loads in flight per thread: the copy runs beside the decode's kernels, and
+// Every slice of the kept rows but slices `sa` <= `sb` (equal: one skipped),
+// on a small grid: the copy runs beside the decode's kernels, and
 // a grid spread over every CU holds enough host reads in flight to stall
 // their memory accesses (measured: attention 10 -> 200+ us), while 16
 // workgroups still keep the link busy.  Timed call by call on MI355X: 8-16
@@ -131,8 +130,15 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 #ifndef REST_GRID
 #define REST_GRID 16
 #endif
+// Calls with at least REST_MIN_ITEMS 64 KiB items per workgroup: each wave
+// claims (miss, 16 KiB) pieces from a counter (the next claim in flight while
+// it copies) with REST_UNROLL loads in flight per thread, so the waves finish
+// together (static (miss, 64 KiB) items per workgroup left the last items to
+// a few workgroups: the 196k thrash 5.06-5.10 -> 4.99 ms per step with 16
+// loads, 5.00-5.01 with 8).  Smaller calls: (miss, 16 KiB) items dealt to
+// the workgroups in turn, REST_SMALL_UNROLL loads in flight.
 #ifndef REST_UNROLL
-#define REST_UNROLL 8
+#define REST_UNROLL 16
 #endif
 #ifndef REST_CHUNK
 #define REST_CHUNK FETCH_CHUNK
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_slice(DevCtx c, const int32
 #ifndef REST_SMALL_UNROLL
 #define REST_SMALL_UNROLL 2
 #endif
+
 
 // Vectors [v_begin, v_end) of the rest of one row, U loads in flight per
 // thread: rest vector x is row vector x, stepped over slice sa, then sb.
@@ -170,6 +177,27 @@ __device__ __forceinline__ void rest_copy_vectors(const u32x4* src, u32x4* dst, 
   }
 }
 
+// As rest_copy_vectors, for one wave over its own piece.
+template <int U>
+__device__ __forceinline__ void wave_copy_vectors(const u32x4* src, u32x4* dst, int64_t v_begin, int64_t v_end,
+                                                  int64_t a, int64_t b, int64_t nvl, bool two, int lane) {
+  for (int64_t v0 = v_begin + lane; v0 < v_end; v0 += 64 * U) {
+    u32x4 t[U];
+    int64_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t x = v0 + u * 64;
+      if (x >= a) x += nvl;
+      if (two && x >= b) x += nvl;
+      r[u] = x;
+      if (v0 + u * 64 < v_end) t[u] = __builtin_nontemporal_load(src + x);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * 64 < v_end) dst[r[u]] = t[u];
+  }
+}
+
 __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_t* keep, int width, int sa, int sb) {
   int m = keep[0];
   if (m > width) m = width;
@@ -177,12 +205,44 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
   const int64_t nvl = c.layer_bytes / 16;
   const int64_t a = (int64_t)sa * nvl, b = (int64_t)sb * nvl;
   const int64_t nvec = c.row_bytes / 16 - (sa == sb ? 1 : 2) * nvl;
-  // item size from the call's volume: REST_CHUNK items when there are at
-  // least REST_MIN_ITEMS per workgroup, a quarter of that otherwise (few
-  // misses: more, smaller items balance the workgroups)
+  // the call's volume in REST_CHUNK items decides the path
   const int64_t big = (int64_t)m * ((nvec + REST_CHUNK / 16 - 1) / (REST_CHUNK / 16));
   const bool large = big >= (int64_t)REST_MIN_ITEMS * gridDim.x;
-  const int64_t cvec = large ? REST_CHUNK / 16 : REST_CHUNK / 64;
+  if (large) {
+    // pieces claimed by waves; the last wave to finish resets the counters
+    constexpr int PV = 1024;                                 // vectors per piece
+    const int ppr = (int)((nvec + PV - 1) / PV);
+    const int64_t pieces = (int64_t)m * ppr;
+    const int lane = threadIdx.x & 63;
+    int32_t* q = c.rest_ctr;
+    int it = 0;
+    if (lane == 0) it = __hip_atomic_fetch_add(&q[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    it = __builtin_amdgcn_readfirstlane(it);
+    while (it < pieces) {
+      int nxt = 0;
+      if (lane == 0) nxt = __hip_atomic_fetch_add(&q[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int mi = (int)(it / ppr), ch = it - mi * ppr;
+      const int slot = miss[2 * mi], page = miss[2 * mi + 1];
+      if (slot < 0 || slot >= c.S || page < 0 || (int64_t)page >= c.N) {
+        if (lane == 0) set_error(c.hdr, DERR_BAD_MISS);
+      } else {
+        const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
+        u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
+        const int64_t v_end = min(nvec, (int64_t)(ch + 1) * PV);
+        wave_copy_vectors<REST_UNROLL>(src, dst, (int64_t)ch * PV, v_end, a, b, nvl, sb != sa, lane);
+      }
+      it = __builtin_amdgcn_readfirstlane(nxt);
+    }
+    if (lane == 0) {
+      const int waves = (int)gridDim.x * (TKV_BLOCK / 64);
+      if (__hip_atomic_fetch_add(&q[1], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == waves - 1) {
+        __hip_atomic_store(&q[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&q[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  }
+  const int64_t cvec = REST_CHUNK / 64;
   const int cpr = (int)((nvec + cvec - 1) / cvec);
   const int64_t items = (int64_t)m * cpr;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
@@ -195,8 +255,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_fetch_rest(DevCtx c, const int32_
     const u32x4* src = reinterpret_cast<const u32x4*>(c.mirror + (size_t)page * c.row_bytes);
     u32x4* dst = reinterpret_cast<u32x4*>(c.pool + (size_t)slot * c.row_bytes);
     const int64_t v_begin = (int64_t)ch * cvec, v_end = min(nvec, v_begin + cvec);
-    if (large) rest_copy_vectors<REST_UNROLL>(src, dst, v_begin, v_end, a, b, nvl, sb != sa);
-    else rest_copy_vectors<REST_SMALL_UNROLL>(src, dst, v_begin, v_end, a, b, nvl, sb != sa);
+    rest_copy_vectors<REST_SMALL_UNROLL>(src, dst, v_begin, v_end, a, b, nvl, sb != sa);
   }
 }
 
@@ -317,6 +376,7 @@ hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st) {
     if ((e = launch_fill_bytes(c.slab_acc, E * 8, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.row_done, c.max_rows, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.glob_done, 4, 0, st)) != hipSuccess) return e;
+    if ((e = fill_i32(c.rest_ctr, 2, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(c.attn_done, (int64_t)c.max_batch * c.Hkv, 0, st)) != hipSuccess) return e;
     if ((e = fill_i32(reinterpret_cast<int32_t*>(c.sel_bm),
                       (int64_t)sel_bm_words(c.max_rows, c.max_batch, c.max_pages), 0, st)) != hipSuccess)
