@@ -113,7 +113,13 @@ def test_c5_fullsize_prefill():
     say("[fullsize] c5: gpu chunk done")
     o = run.make_tier(wl, materialize=False)
     run.setup(wl, o)
-    rows = [0, 1, 63, 64, 1000, 2047, 3000, 4095]
+    # chunk edges, 64-row block edges and a seeded spread: every row holds
+    # its own top-32 pages over the whole cached range plus the causal tail
+    rng = np.random.default_rng(5)
+    edges = {0, 1, 62, 63, 64, 65, 127, 128, 1000, 2047, 2048, 3000, 4094, 4095}
+    rest = np.array(sorted(set(range(wl.prefill_tokens)) - edges))
+    rows = sorted(edges | set(int(x) for x in rng.choice(rest, 34, replace=False)))
+    assert len(rows) == 48
     recs = run.prefill(wl, o, attention_rows=rows)
     for layer, (gg, rec) in enumerate(zip(got, recs)):
         where = f"c5 layer {layer}"
@@ -122,10 +128,9 @@ def test_c5_fullsize_prefill():
         assert np.array_equal(gg["out_slots"].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
         m = int(gg["miss_count"].item())
         assert np.array_equal(gg["miss"].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
-        if layer in (0, wl.num_layers - 1):
-            out = bf16_to_f64(gg["out"][rows])
-            ref = np.stack([rec["out"][r] for r in rows])
-            assert_close(out, ref, f"{where}: attention")
+        out = bf16_to_f64(gg["out"][rows])
+        ref = np.stack([rec["out"][r] for r in rows])
+        assert_close(out, ref, f"{where}: attention")
     new_pages = list(range(wl.contexts[0] // wl.page_size, wl.num_logical_pages))
     compare_state(g, o, "c5 after the chunk", sample_pages=new_pages[:3] + new_pages[-2:])
 
