@@ -422,25 +422,31 @@ __device__ __forceinline__ void init_state(WaveAttn& st) {
 }  // namespace
 
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  When
-// the KV heads divide the XCDs evenly, a workgroup covers 4 rows of one KV
-// head and XCD x only ever serves head x / (8 / Hkv): each L2 then caches one
-// head's blocks of the pages instead of all of them.
+// the KV heads divide the XCDs evenly, a workgroup covers consecutive rows
+// (one per wave) of one KV head and XCD x only ever serves head x / (8 / Hkv):
+// each L2 then caches one head's blocks of the pages instead of all of them.
 constexpr int NXCD = 8;
 
 __host__ __device__ __forceinline__ bool attn_rows_by_xcd(int Hkv) { return Hkv <= NXCD && NXCD % Hkv == 0; }
 
-// one wave per (row, KV head), all of the row's pages
-__global__ __launch_bounds__(TKV_BLOCK, 2) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
-  __shared__ __align__(16) uint8_t pbuf[MWAVES][PBUF];
+// One wave per (row, KV head), all of the row's pages; RW waves per
+// workgroup.  Eight waves in one workgroup (8 LDS page buffers, 136 KiB: one
+// workgroup per CU) beat two workgroups of four per CU: on MI355X a 4,096-row
+// chunk's attention took 8.52-8.55 ms over 12 layers against 9.15-9.22 ms
+// (6 or 7 waves: 9.05-9.24 ms).  A loads-only probe of the same gather gave
+// the same ordering (620 against 755 us per layer).
+constexpr int RW = 8;
+__global__ __launch_bounds__(RW * 64, 2) void k_attn_mfma_rows(DevCtx c, AttnArgs a) {
+  __shared__ __align__(16) uint8_t pbuf[RW][PBUF];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int r, g;
   if (attn_rows_by_xcd(c.Hkv)) {
     const int per = NXCD / c.Hkv;                       // XCDs per KV head
     const int x = blockIdx.x % NXCD, k = blockIdx.x / NXCD;
     g = x / per;
-    r = (k * per + x % per) * MWAVES + wave;
+    r = (k * per + x % per) * RW + wave;
   } else {
-    const int u = blockIdx.x * MWAVES + wave;
+    const int u = blockIdx.x * RW + wave;
     r = u / c.Hkv;
     g = u - r * c.Hkv;
   }
@@ -647,14 +653,17 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
   if (a.rows > c.max_batch || units >= 256) {
     a.splits = 1;
     a.pages_per_split = a.topk;
-    int blocks = (int)((units + MWAVES - 1) / MWAVES);
-    if (attn_rows_by_xcd(c.Hkv)) {
+    // workgroups of `w` waves, one (row, KV head) each; with the XCD mapping
+    // each KV head takes groups of w rows on its own XCDs
+    auto grid_of = [&](int w) {
+      if (!attn_rows_by_xcd(c.Hkv)) return (int)((units + w - 1) / w);
       const int per = NXCD / c.Hkv;
-      const int groups = (a.rows + MWAVES - 1) / MWAVES;   // row groups per head
-      blocks = NXCD * ((groups + per - 1) / per);
-    }
+      const int groups = (a.rows + w - 1) / w;             // row groups per head
+      return NXCD * ((groups + per - 1) / per);
+    };
     const int RP = c.attn_range_pages;
     if (RP > 0 && c.attn_state && a.topk <= 64 && a.rows <= c.max_rows && a.max_pages > RP) {
+      const int blocks = grid_of(MWAVES);
       const int nr = (a.max_pages + RP - 1) / RP;
       for (int r = 0; r < nr; ++r) {
         hipLaunchKernelGGL(k_attn_mfma_range, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a, r, RP);
@@ -663,7 +672,7 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
       }
       return hipSuccess;
     }
-    hipLaunchKernelGGL(k_attn_mfma_rows, dim3(blocks), dim3(TKV_BLOCK), 0, st, c, a);
+    hipLaunchKernelGGL(k_attn_mfma_rows, dim3(grid_of(RW)), dim3(RW * 64), 0, st, c, a);
     return hipGetLastError();
   }
   // one page per wave
