@@ -78,7 +78,8 @@ def test_multi_row_requests_union_and_drops():
     """Several requests with several causal rows each in one select call (the
     scan path): per-row selections, the per-request unions (ascending, first C
     kept) and the drop counter equal the oracle's.  Row counts straddle the
-    64-row groups of the union bitmaps."""
+    64-row groups of the union bitmaps.  Then the unions' ensure and fetch and
+    every row's attention."""
     from workload.gpu_run import GpuWorkload
     wl = get_workload("c4s")
     counts = [70, 1, 130, 65]
@@ -114,6 +115,25 @@ def test_multi_row_requests_union_and_drops():
         assert np.array_equal(needed.cpu().numpy(), ref_needed), f"call {rep}: needed"
     drops = t.read_counters()["drops"] - drops0
     assert drops == o.drops > 0
+    # the unions made resident, then every row's attention through the rows
+    # kernel (266 rows: the last row group of its workgroups is ragged);
+    # pages dropped from a union are not resident and are skipped
+    W = wl.batch * C
+    out_slots = torch.full((W,), -7, dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W, 2), dtype=torch.int32, device="cuda")
+    miss_count = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    t.lru_ensure(needed.view(-1), out_slots, miss, miss_count)
+    t.fetch_pages(miss, miss_count)
+    out = torch.zeros((rows, wl.num_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    t.sparse_paged_attn(layer, qd, dev(row_start), g.ctx_len, sel, g.bt, out, row_pos=dev(row_pos))
+    torch.cuda.synchronize()
+    ref_slots, ref_misses = o.ensure(ref_needed)
+    o.fetch(ref_misses)
+    assert np.array_equal(out_slots.cpu().numpy(), ref_slots), "out_slots"
+    m = int(miss_count.item())
+    assert np.array_equal(miss.cpu().numpy()[:m], ref_misses), "misses"
+    ref = o.attention(layer, q, row_start, row_pos, ctx, ref_sel, bt)
+    assert_close(bf16_to_f64(out), ref, "multi-row attention")
 
 
 @pytest.mark.parametrize("pages", [7, 16, 64])
