@@ -441,7 +441,12 @@ int tkv_debug_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream
 /* Host pointer to the pinned mirror (read-only view for tests). */
 const void* tkv_mirror_host_ptr(const tkv_ctx* ctx);
 
-/* Frees the mirror and the ctx.  Device buffers stay with the caller. */
+/* Frees the mirror and the ctx.  Device buffers stay with the caller.  The
+ * caller first synchronises the streams it passed to this ctx's calls:
+ * kernels still running may read or write the mirror (a plain store writes
+ * it directly).  The ctx's own copies (rest-of-rows copies, a launched
+ * mirror copy) are waited for here; a split store's copy not yet launched
+ * is dropped with the mirror. */
 void tkv_destroy(tkv_ctx* ctx);
 
 const char* tkv_last_error(void);
