@@ -254,7 +254,11 @@ int tkv_sparse_paged_attn_host_tail(tkv_ctx* ctx, int32_t layer, const uint16_t*
  * select + compact + ensure in one launch, then fetch, then attention.
  * Same semantics as tkv_select_pages -> tkv_lru_ensure(needed, B*C) ->
  * tkv_fetch_pages -> tkv_sparse_paged_attn.  out_slots int32 [B*C],
- * miss int32 [B*C][2], miss_count int32 [1]. */
+ * miss int32 [B*C][2], miss_count int32 [1].  With topk <= C and the
+ * matrix-core decode attention (fp8, 64-token pages, B*Hkv < 256) the fetch
+ * runs inside the attention launch: the pages it brings in are read for
+ * this layer from their mirror rows, and the pool and mirror end the call
+ * as after the separate fetch. */
 int tkv_decode_layer(tkv_ctx* ctx, int32_t layer, const uint16_t* q, int32_t B,
                      const int32_t* block_table, int32_t max_pages, const int32_t* n_pages,
                      const int32_t* ctx_len, const float* page_bias, int32_t topk,

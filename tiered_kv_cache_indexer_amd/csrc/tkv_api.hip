@@ -92,7 +92,7 @@ struct Layout {
   size_t st_hdr, st_p2s, st_mark, st_s2p, st_stamp, st_order, st_acc, st_total;
   // workspace offsets
   size_t ws_scores, ws_sel_slots, ws_qg, ws_row_done, ws_glob, ws_slot_of_j, ws_miss_j, ws_victims, ws_wneeded,
-      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_stage, ws_stage_page, ws_rest_ctr, ws_attn_state, ws_total;
+      ws_wnofetch, ws_wmiss, ws_wmiss_count, ws_part, ws_attn_done, ws_iota, ws_sel_bm, ws_pout, ws_pmiss, ws_pmiss_count, ws_bg_miss, ws_stage, ws_stage_page, ws_rest_ctr, ws_miss_flag, ws_attn_state, ws_total;
   size_t stage_blocks;
 };
 
@@ -179,6 +179,7 @@ static Layout make_layout(const tkv_config* c) {
   L.ws_stage = o; o = align256(o + L.stage_blocks * L.layer);
   L.ws_stage_page = o; o = align256(o + L.stage_blocks * 4);
   L.ws_rest_ctr = o; o = align256(o + 8);
+  L.ws_miss_flag = o; o = align256(o + W);
   // records of the page-range prefill attention: only configs with more rows than requests
   L.ws_attn_state = o;
   if (c->max_rows > c->max_batch) o = align256(o + R * (size_t)H * ATTN_STATE_FLOATS * 4);
@@ -305,6 +306,7 @@ int tkv_attach_device(tkv_ctx* c, const tkv_device_buffers* b, void* stream) {
   d.stage_page = (int32_t*)(ws + L.ws_stage_page);
   d.stage_blocks = (int)L.stage_blocks;
   d.rest_ctr = (int32_t*)(ws + L.ws_rest_ctr);
+  d.miss_flag = ws + L.ws_miss_flag;
   d.stage_layer = -1;
   d.stage_n = 0;
   d.attn_state = f.max_rows > f.max_batch ? (float*)(ws + L.ws_attn_state) : nullptr;
@@ -688,6 +690,10 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   // attention reads (row stride C); otherwise a translated copy
   const bool direct = topk <= c->C;
   a.sel_slots = direct ? nullptr : c->dev.sel_slots;
+  // one stream, matrix-core split attention: the fetch is folded into the
+  // attention launch (its pages of this layer read from their mirror rows)
+  const bool fold = !split && direct && attn_mfma_split_applies(c->dev, B);
+  a.miss_flag = fold ? c->dev.miss_flag : nullptr;
   HIPCHECK(launch_select_scan(c->dev, a, s), "decode select+ensure launch");
   // the layer's ensure may have rebound a slot the preload copy still writes:
   // its own fetch (and the attention) wait for that copy
@@ -698,7 +704,7 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
     // the selection and ensure ran beside a split call's copies (they touch
     // no pool bytes and no kept miss list); the copy waits for them
     WAIT_REST_COPY(c, s);
-    HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
+    if (!fold) HIPCHECK(launch_fetch(c->dev, miss, miss_count, B * c->C, s), "decode fetch launch");
   }
   if ((rc = launch_deferred_mirror(c, s))) return rc;   // beside the attention
   AttnArgs t{};
@@ -708,7 +714,14 @@ static int decode_layer_impl(tkv_ctx* c, int32_t layer, const uint16_t* q, int32
   t.one_row_each = 1;
   t.slots = direct ? out_slots : c->dev.sel_slots;
   t.slots_stride = direct ? c->C : 0;
-  HIPCHECK(launch_attn(c->dev, t, s), "decode attention launch");
+  if (fold) {
+    t.fmiss = miss;
+    t.fmiss_count = miss_count;
+    t.fwidth = B * c->C;
+    t.slot_miss = c->dev.miss_flag;
+    t.slot_page = needed;   // a row's selection is its request's needed list, in order
+  }
+  HIPCHECK(launch_attn(c->dev, t, s), fold ? "decode attention+fetch launch" : "decode attention launch");
   return TKV_OK;
 }
 

@@ -276,6 +276,7 @@ __global__ __launch_bounds__(TKV_BLOCK) void k_attn(DevCtx c, AttnArgs a) {
 hipError_t launch_attn(const DevCtx& c, AttnArgs a, hipStream_t st) {
   if (c.attn_impl != ATTN_VECTOR && attn_mfma_supported(c)) return launch_attn_mfma(c, a, st);
   if (c.attn_impl == ATTN_MATRIX) return hipErrorInvalidValue;
+  if (a.fmiss || a.slot_miss) return hipErrorInvalidValue;   // a folded fetch: matrix-core split launches only
   // splits: enough workgroups to cover the chip for small batches; one split
   // (no merge) when rows exceed the merge scratch (prefill chunks)
   int per = 1;

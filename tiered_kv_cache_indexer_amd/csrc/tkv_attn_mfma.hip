@@ -188,6 +188,33 @@ __device__ __forceinline__ void load_page(const uint8_t* blk, size_t cb, int g, 
   }
 }
 
+// The block `load_page` read, written to `blk` (a pool slot's block of this
+// layer): every lane stores what it loaded; the scales (one pair per token,
+// shared by the KV heads) from head 0's wave, one lane per 16.
+__device__ __forceinline__ void store_page(uint8_t* blk, size_t cb, int g, int lane, const PageRegs& pr) {
+  const int m = lane & 15, q = lane >> 4;
+  uint8_t* kb = blk + (size_t)g * MPS * MD;
+  uint8_t* vb = blk + cb + (size_t)g * MPS * MD;
+  uint8_t* sc = blk + 2 * cb;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int t = 16 * (m >> 2) + 4 * mt + (m & 3);
+    const i32x8 k = pr.ka[mt];
+    *reinterpret_cast<uint4*>(kb + t * MD + 32 * q) = make_uint4((uint32_t)k[0], (uint32_t)k[1], (uint32_t)k[2], (uint32_t)k[3]);
+    *reinterpret_cast<uint4*>(kb + t * MD + 32 * q + 16) =
+        make_uint4((uint32_t)k[4], (uint32_t)k[5], (uint32_t)k[6], (uint32_t)k[7]);
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint4*>(vb + (16 * dt + m) * MPS + 16 * q) = pr.vr[dt];
+  if (g == 0 && m == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4*>(sc + 4 * (16 * q + 4 * i)) = pr.ks4[i];
+      *reinterpret_cast<float4*>(sc + 4 * MPS + 4 * (16 * q + 4 * i)) = pr.vs4[i];
+    }
+  }
+}
+
 // Fold one loaded page (nt >= 1 visible tokens) into the wave's running state.
 __device__ __forceinline__ void fold_page(const PageRegs& pr, int nt, int lane, const QOp& qo, float qscale,
                                           WaveAttn& st) {
@@ -264,17 +291,22 @@ __device__ __forceinline__ void fold_page(const PageRegs& pr, int nt, int lane, 
 // Fold the pages flagged in `mask` (wave-uniform; bit j = lane j's page:
 // row pointer rows_lo/hi, visible tokens nt) in ascending lane order,
 // loading each page straight into registers (decode: about one page per
-// wave).
-__device__ __forceinline__ void fold_pages(uint64_t mask, uint32_t rows_lo, uint32_t rows_hi, int nt,
-                                           size_t layer_off, size_t cb, int g, int lane, QOp& qo, bool& have_q,
-                                           const uint4 (&qraw)[4], float qscale, WaveAttn& st) {
+// wave).  A page with a write-back row (wb_lo/hi nonzero: read from its
+// mirror row) is stored to that pool row's block too.
+__device__ __forceinline__ void fold_pages(uint64_t mask, uint32_t rows_lo, uint32_t rows_hi, uint32_t wb_lo,
+                                           uint32_t wb_hi, int nt, size_t layer_off, size_t cb, int g, int lane,
+                                           QOp& qo, bool& have_q, const uint4 (&qraw)[4], float qscale,
+                                           WaveAttn& st) {
   while (mask) {
     const int j = __builtin_ctzll(mask);
     mask &= mask - 1;
     const uint64_t pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)rows_hi, j) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane((int)rows_lo, j);
+    const uint64_t wv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)wb_hi, j) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)wb_lo, j);
     PageRegs cur;
     load_page(reinterpret_cast<const uint8_t*>(pv) + layer_off, cb, g, lane, cur);
+    if (wv) store_page(reinterpret_cast<uint8_t*>(wv) + layer_off, cb, g, lane, cur);
     if (!have_q) {                 // built while the first page's loads are in flight
       make_qop(qraw, qo);
       have_q = true;
@@ -364,6 +396,41 @@ __device__ __forceinline__ void fold_pages_lds(uint64_t mask, uint32_t rows_lo, 
   }
 }
 
+// Selected entry j of row r (request b): local id -> pool slot (or, for the
+// host tail, the page's mirror row) and the page's visible tokens (0: none).
+// An entry the launch's own fetch brings in is read from its mirror row and
+// `wb` is its slot's row (else null).
+__device__ __forceinline__ void resolve_page(const DevCtx& c, const AttnArgs& a, int r, int b, int j, int limit,
+                                             const uint8_t*& row, int& nt, uint8_t*& wb) {
+  row = nullptr;
+  nt = 0;
+  wb = nullptr;
+  const int i = a.sel[(size_t)r * a.topk + j];
+  if (a.slots) {
+    const size_t idx = (size_t)r * (a.slots_stride > 0 ? a.slots_stride : a.topk) + j;
+    const int s = a.slots[idx];
+    const int fetched = a.slot_miss ? (int)a.slot_miss[idx] : 0;
+    const int pg = fetched ? a.slot_page[idx] : -1;
+    if (i >= 0 && s >= 0 && s < c.S) {
+      row = c.pool + (size_t)s * c.row_bytes;
+      nt = min(MPS, limit - i * MPS);
+      if (fetched && pg >= 0 && (int64_t)pg < c.N) {
+        wb = c.pool + (size_t)s * c.row_bytes;
+        row = c.mirror + (size_t)pg * c.row_bytes;
+      }
+    }
+  } else if (i >= 0 && i < a.max_pages) {
+    const int page = a.bt[(size_t)b * a.max_pages + i];
+    if (page >= 0 && (int64_t)page < c.N) {
+      const int slot = c.page_to_slot[page];
+      if (slot >= 0) row = c.pool + (size_t)slot * c.row_bytes;
+      else if (a.host_tail) row = c.mirror + (size_t)page * c.row_bytes;
+    }
+    nt = min(MPS, limit - i * MPS);
+  }
+  if (!row) nt = 0;
+}
+
 // Pages j = jbeg, jbeg + jstep, ... < jend of row r (request b), KV head g.
 // The query operand: ready (STAGED) or built by the register path from the
 // raw query once the first page's loads are in flight.
@@ -381,34 +448,17 @@ __device__ __forceinline__ void wave_pages(const DevCtx& c, const AttnArgs& a, i
     // the host tail, the page's mirror row), visible tokens
     const int j = base + lane * jstep;
     const uint8_t* row = nullptr;
+    uint8_t* wb = nullptr;
     int nt = 0;
-    if (j < jend) {
-      const int i = a.sel[(size_t)r * a.topk + j];
-      if (a.slots) {
-        const int s = a.slots[(size_t)r * (a.slots_stride > 0 ? a.slots_stride : a.topk) + j];
-        if (i >= 0 && s >= 0 && s < c.S) {
-          row = c.pool + (size_t)s * c.row_bytes;
-          nt = min(MPS, limit - i * MPS);
-        }
-      } else if (i >= 0 && i < a.max_pages) {
-        const int page = a.bt[(size_t)b * a.max_pages + i];
-        if (page >= 0 && (int64_t)page < c.N) {
-          const int slot = c.page_to_slot[page];
-          if (slot >= 0) row = c.pool + (size_t)slot * c.row_bytes;
-          else if (a.host_tail) row = c.mirror + (size_t)page * c.row_bytes;
-        }
-        nt = min(MPS, limit - i * MPS);
-      }
-      if (!row) nt = 0;
-    }
-    const uint64_t rowv = reinterpret_cast<uint64_t>(row);
+    if (j < jend) resolve_page(c, a, r, b, j, limit, row, nt, wb);
+    const uint64_t rowv = reinterpret_cast<uint64_t>(row), wbv = reinterpret_cast<uint64_t>(wb);
     const uint64_t mask = __ballot(nt > 0);
-    if constexpr (STAGED)
+    if constexpr (STAGED)   // (no write-back rows: the launcher folds the fetch into split launches only)
       fold_pages_lds(mask, (uint32_t)rowv, (uint32_t)(rowv >> 32), nt, (size_t)a.layer * c.layer_bytes, cb, g,
                      lane, qop, qscale, st, lds);
     else
-      fold_pages(mask, (uint32_t)rowv, (uint32_t)(rowv >> 32), nt, (size_t)a.layer * c.layer_bytes, cb, g, lane,
-                 qop, have_q, qraw, qscale, st);
+      fold_pages(mask, (uint32_t)rowv, (uint32_t)(rowv >> 32), (uint32_t)wbv, (uint32_t)(wbv >> 32), nt,
+                 (size_t)a.layer * c.layer_bytes, cb, g, lane, qop, have_q, qraw, qscale, st);
   }
 }
 
@@ -582,10 +632,53 @@ __global__ __launch_bounds__(TKV_BLOCK, 2) void k_attn_mfma_range(DevCtx c, Attn
 }
 
 // a workgroup per (row, KV head, page range); wave w takes every 4th page
+// The fetch folded into a split launch: workgroups past the attention's rows
+// copy the miss list's rows host -> device, every layer's block but this
+// launch's (which the waves that fold those pages write back), in 16 KiB
+// items dealt to them in turn, two 16-byte loads in flight per thread.
+constexpr int FUSED_FETCH_WGS = 64;
+__device__ void attn_fused_fetch(const DevCtx& c, const AttnArgs& a) {
+  const int F = (int)gridDim.x * ((int)gridDim.y - a.rows);
+  const int f = ((int)blockIdx.y - a.rows) * (int)gridDim.x + (int)blockIdx.x;
+  int m = *a.fmiss_count;
+  if (m > a.fwidth) m = a.fwidth;
+  if (f == 0 && threadIdx.x == 0 && m > 0) c.hdr->counters[CNT_BYTES_FETCHED] += (int64_t)m * c.row_bytes;
+  const int64_t nvl = c.layer_bytes / 16, la = (int64_t)a.layer * nvl;
+  const int64_t nvec = c.row_bytes / 16 - nvl;          // the row without this layer's block
+  constexpr int64_t IV = 1024;                          // vectors per item
+  const int64_t ipr = (nvec + IV - 1) / IV;
+  const int64_t items = (int64_t)m * ipr;
+  for (int64_t it = f; it < items; it += F) {
+    const int mi = (int)(it / ipr);
+    const int64_t ch = it - (int64_t)mi * ipr;
+    const int slot = a.fmiss[2 * mi], page = a.fmiss[2 * mi + 1];
+    if (slot < 0 || slot >= c.S || page < 0 || (int64_t)page >= c.N) {
+      if (threadIdx.x == 0) set_error(c.hdr, DERR_BAD_MISS);
+      continue;
+    }
+    const u32x4v* src = reinterpret_cast<const u32x4v*>(c.mirror + (size_t)page * c.row_bytes);
+    u32x4v* dst = reinterpret_cast<u32x4v*>(c.pool + (size_t)slot * c.row_bytes);
+    const int64_t v_end = min(nvec, (ch + 1) * IV);
+    for (int64_t v0 = ch * IV + threadIdx.x; v0 < v_end; v0 += 2 * TKV_BLOCK) {
+      u32x4v t0, t1;
+      const int64_t x0 = v0, x1 = v0 + TKV_BLOCK;
+      const int64_t r0 = x0 >= la ? x0 + nvl : x0, r1 = x1 >= la ? x1 + nvl : x1;
+      t0 = __builtin_nontemporal_load(src + r0);
+      if (x1 < v_end) t1 = __builtin_nontemporal_load(src + r1);
+      dst[r0] = t0;
+      if (x1 < v_end) dst[r1] = t1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(TKV_BLOCK) void k_attn_mfma_split(DevCtx c, AttnArgs a) {
   __shared__ __align__(16) float sO[MWAVES][MG][MD];
   __shared__ float sM[MWAVES][MG], sL[MWAVES][MG];
   __shared__ int sflag[2];
+  if ((int)blockIdx.y >= a.rows) {   // (only with a folded fetch)
+    attn_fused_fetch(c, a);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.y;
   const int g = blockIdx.x % c.Hkv;
@@ -651,6 +744,7 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
   if (!attn_mfma_supported(c)) return hipErrorInvalidValue;
   const long units = (long)a.rows * c.Hkv;
   if (a.rows > c.max_batch || units >= 256) {
+    if (a.fmiss || a.slot_miss) return hipErrorInvalidValue;   // a folded fetch: split launches only
     a.splits = 1;
     a.pages_per_split = a.topk;
     // workgroups of `w` waves, one (row, KV head) each; with the XCD mapping
@@ -675,10 +769,16 @@ hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st) {
     hipLaunchKernelGGL(k_attn_mfma_rows, dim3(grid_of(RW)), dim3(RW * 64), 0, st, c, a);
     return hipGetLastError();
   }
-  // one page per wave
+  // one page per wave; a folded fetch adds rows of workgroups past a.rows
   a.pages_per_split = MWAVES;
   a.splits = (a.topk + MWAVES - 1) / MWAVES;
-  dim3 grid(c.Hkv * a.splits, a.rows);
+  const int gx = c.Hkv * a.splits;
+  const int fy = a.fmiss ? (FUSED_FETCH_WGS + gx - 1) / gx : 0;
+  dim3 grid(gx, a.rows + fy);
   hipLaunchKernelGGL(k_attn_mfma_split, grid, dim3(TKV_BLOCK), 0, st, c, a);
   return hipGetLastError();
+}
+
+bool attn_mfma_split_applies(const DevCtx& c, int rows) {
+  return c.attn_impl != ATTN_VECTOR && attn_mfma_supported(c) && rows <= c.max_batch && (long)rows * c.Hkv < 256;
 }

@@ -67,6 +67,7 @@ struct DevCtx {
   float* attn_state;        // [max_rows][Hkv][ATTN_STATE_FLOATS] page-range attention records (or null)
   int32_t* bg_miss;         // [2][1 + 2*max_width] miss count and list kept for the split copy's later parts
   int32_t* rest_ctr;        // [2] work counter and finished waves of the rest-of-rows copy (zero between launches)
+  uint8_t* miss_flag;       // [max_width] decode_layer: per needed entry, fetched by this call
   uint8_t* stage;           // [stage_blocks][layer_bytes] mirror blocks of the split store, copied later
   int32_t* stage_page;      // [stage_blocks] logical page of each staged block (-1: none)
   int stage_blocks;
@@ -110,6 +111,7 @@ struct SelArgs {
   int32_t* miss;
   int32_t* miss_count;
   int32_t* sel_slots;   // fused path: translated slots of sel_local (or null)
+  uint8_t* miss_flag;   // fused path: per needed entry, 1 where this call fetches its page (or null)
   int one_row_each;     // 1: row r is request r's only row (row_start = 0, 1, ..., B)
 };
 
@@ -146,6 +148,17 @@ struct AttnArgs {
   int slots_stride;      // row stride of `slots` (0: topk)
   int one_row_each;      // 1: row r is request r's only row (row_start = 0, 1, ..., B)
   int host_tail;         // read pages that are not resident from their mirror row
+  // Fetch folded into the launch (decode_layer, split mode): extra
+  // workgroups copy the rows of the miss list (fmiss, *fmiss_count pairs of
+  // slot and page, at most fwidth) for every layer but this one; an entry
+  // whose slot_miss flag is set (same indexing as `slots`) is read from the
+  // mirror row of page slot_page[...] and its block of this layer is written
+  // to the slot by the wave that folds it.
+  const int32_t* fmiss;
+  const int32_t* fmiss_count;
+  int fwidth;
+  const uint8_t* slot_miss;
+  const int32_t* slot_page;
   int splits;
   int pages_per_split;
 };

@@ -25,6 +25,8 @@ hipError_t launch_mirror_copy(const DevCtx& c, int layer, int blocks, hipStream_
 hipError_t launch_attn(const DevCtx& c, AttnArgs a, hipStream_t st);
 bool attn_mfma_supported(const DevCtx& c);
 hipError_t launch_attn_mfma(const DevCtx& c, AttnArgs a, hipStream_t st);
+// the matrix-core split kernel serves `rows` decode rows (a folded fetch is possible)
+bool attn_mfma_split_applies(const DevCtx& c, int rows);
 hipError_t launch_reset(const DevCtx& c, int full, hipStream_t st);
 hipError_t launch_fill_bytes(void* p, int64_t n, uint8_t v, hipStream_t st);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t st);

@@ -23,6 +23,8 @@ struct EnsureOut {
   int32_t* out_slots;   // [W] or null
   int32_t* miss;        // [W][2]
   int32_t* miss_count;  // [1]
+  uint8_t* miss_flag;   // [W] or null: 1 where the entry's page is on this call's fetch list
+                        // (a duplicate takes its first occurrence's flag), else 0
 };
 
 __device__ __forceinline__ bool page_ok(const DevCtx& c, int p) { return p >= 0 && (int64_t)p < c.N; }
@@ -90,6 +92,7 @@ __device__ void lru_ensure_global(const DevCtx& c, const int32_t* needed, int W,
         } else {
           is_miss = 1;
         }
+        if (o.miss_flag) o.miss_flag[j] = (is_miss && !(no_fetch && no_fetch[j])) ? 1 : 0;
       }
     }
     int tot;
@@ -169,12 +172,19 @@ __device__ void lru_ensure_global(const DevCtx& c, const int32_t* needed, int W,
     MF += tot;
   }
 
-  // F: out_slots (a duplicate reads its first occurrence's slot)
+  // F: out_slots and fetch flags (a duplicate reads its first occurrence's)
   for (int j = tid; j < W; j += TKV_BLOCK) {
     int p = needed[j];
-    int s = -1;
-    if (page_ok(c, p)) s = c.slot_of_j[ld_acquire_i32(&c.page_mark[p])];
+    int s = -1, f = 0;
+    bool first = false;
+    if (page_ok(c, p)) {
+      const int j0 = ld_acquire_i32(&c.page_mark[p]);
+      s = c.slot_of_j[j0];
+      first = j0 == j;                         // its flag was written in C
+      if (o.miss_flag && !first) f = o.miss_flag[j0];
+    }
     if (o.out_slots) o.out_slots[j] = s;
+    if (o.miss_flag && !first) o.miss_flag[j] = f;
   }
   __syncthreads();
   // G: release the first-occurrence marks
@@ -438,12 +448,20 @@ __device__ void lru_ensure_lds(const DevCtx& c, const int32_t* needed, int W, co
     MF += tot;
   }
 
-  // F: out_slots (a duplicate reads its first occurrence's slot)
+  // F: out_slots (a duplicate reads its first occurrence's slot); fetch
+  // flags (the page was not resident before this call and is fetched)
   if (o.out_slots) {
 #pragma unroll
     for (int u = 0; u < JPT; ++u) {
       const int j = tid + u * TKV_BLOCK;
       if (j < W) o.out_slots[j] = hs[u] >= 0 ? slj[hv[hs[u]]] : -1;
+    }
+  }
+  if (o.miss_flag) {
+#pragma unroll
+    for (int u = 0; u < JPT; ++u) {
+      const int j = tid + u * TKV_BLOCK;
+      if (j < W) o.miss_flag[j] = (hs[u] >= 0 && p2s[u] < 0 && !(no_fetch && no_fetch[hv[hs[u]]])) ? 1 : 0;
     }
   }
 

@@ -300,7 +300,7 @@ __device__ void select_finish(const DevCtx& c, const SelArgs& a, uint32_t* dyn, 
     for (int b = 0; b < a.B; ++b)
       if (a.row_start[b + 1] - a.row_start[b] != 1) compact_block(c, a, b, dyn, sm_scan);
   if (a.do_ensure) {
-    EnsureOut o{a.out_slots, a.miss, a.miss_count};
+    EnsureOut o{a.out_slots, a.miss, a.miss_count, a.miss_flag};
     lru_ensure_block(c, a.needed, a.B * a.C, nullptr, o, sm_scan, dyn);   // dyn is free after the compaction
     __syncthreads();
     if (a.sel_slots) write_sel_slots(c, a);
@@ -662,7 +662,7 @@ hipError_t launch_select_rows(const DevCtx& c, const SelArgs& a, hipStream_t st)
 
 hipError_t launch_ensure(const DevCtx& c, const int32_t* needed, int W, const uint8_t* no_fetch,
                          int32_t* out_slots, int32_t* miss, int32_t* miss_count, hipStream_t st) {
-  EnsureOut o{out_slots, miss, miss_count};
+  EnsureOut o{out_slots, miss, miss_count, nullptr};
   hipLaunchKernelGGL(k_ensure, dim3(1), dim3(TKV_BLOCK), ensure_dyn_lds(c), st, c, needed, W, no_fetch, o);
   return hipGetLastError();
 }
