@@ -135,23 +135,32 @@ def test_c5_fullsize_prefill():
     compare_state(g, o, "c5 after the chunk", sample_pages=new_pages[:3] + new_pages[-2:])
 
 
-def test_c3_fullsize_steady_state_split():
-    """The bench's timed window at full size: steps 0-2 through decode_layer,
-    then decode_layer_split with the copy stream joined only where a step is
-    compared (as the bench joins it once, after its timed steps); every layer
-    of steps 5 and 24 (the first and last timed steps of the driver's
-    5 warmup + 20 timed steps) against the oracle -- selections, compaction,
-    slot maps, miss lists -- LRU state and counters at steps 5, 14 and 24,
-    attention on two layers of step 24, pool rows of pages copied then."""
+# bench.py's default decode run: 8 untimed steps (the first half through
+# decode_layer, then the split path it chose), 100 timed steps
+BENCH_WARMUP, BENCH_STEPS = 8, 100
+
+
+def _steady_state_split(key, check_layers, check_state, attn_step, attn_layers):
+    """The bench's decode window at full size, in its launch configuration:
+    steps 0..3 through decode_layer, then decode_layer_split with the copy
+    stream joined only where a step is compared (the bench joins it once,
+    after its timed steps).  Every layer of the steps in check_layers against
+    the oracle (selections, compaction, slot maps, miss lists), LRU state,
+    counters and the pool rows of sampled resident pages at check_state,
+    attention on attn_layers of attn_step."""
+    import dataclasses
+
     from workload.gpu_run import GpuWorkload
-    wl = get_workload("c3")
-    say(f"[fullsize] c3 steady state: {wl.description}")
+    base = get_workload(key)
+    last = max(check_layers | check_state | {attn_step})
+    wl = dataclasses.replace(base, steps=max(base.steps, BENCH_WARMUP + BENCH_STEPS))
+    say(f"[fullsize] {key} steady state to step {last}: {wl.description}")
     g = GpuWorkload(wl)
     g.setup()
     g.upload_queries()
     o = run.make_tier(wl, materialize=False)
     run.setup(wl, o)
-    say("[fullsize] c3 steady state: setups done")
+    say(f"[fullsize] {key} steady state: setups done")
     q = gen.decode_queries(wl)
     bt, npg = gen.block_tables(wl)
     ctx = gen.context_lengths(wl)
@@ -160,21 +169,21 @@ def test_c3_fullsize_steady_state_split():
     o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
     side = torch.cuda.Stream()
     stream = torch.cuda.current_stream()
-    check_layers, check_state, attn_step = {5, 24}, {5, 14, 24}, 24
     rng = np.random.default_rng(11)
-    for s in range(25):
-        if s < 3:
+    plain_steps = (BENCH_WARMUP + 1) // 2
+    for s in range(last + 1):
+        if s < plain_steps:
             g.decode_step(s)
         else:
             g.decode_step_split(s, side, join=False)
-        if s in check_state:
+        if s in check_state or s in check_layers:
             stream.wait_stream(side)
             torch.cuda.synchronize()
         for layer in range(wl.num_layers):
-            with_attn = s == attn_step and layer in (3, 10)
+            with_attn = s == attn_step and layer in attn_layers
             rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias, with_attention=with_attn)
             if s in check_layers:
-                where = f"c3 steady step {s} layer {layer}"
+                where = f"{key} steady step {s} layer {layer}"
                 assert np.array_equal(g.sel[layer].cpu().numpy(), rec["sel"]), f"{where}: sel"
                 assert np.array_equal(g.needed[layer].cpu().numpy(), rec["needed"]), f"{where}: needed"
                 assert np.array_equal(g.out_slots[layer].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
@@ -185,7 +194,21 @@ def test_c3_fullsize_steady_state_split():
         if s in check_state:
             resident = [int(p) for p in o.lru.slot_to_page if p >= 0]
             picked = sorted(rng.choice(resident, size=4, replace=False).tolist())
-            compare_state(g, o, f"c3 steady step {s}", sample_pages=picked)
-            say(f"[fullsize] c3 steady state: step {s} ok")
+            compare_state(g, o, f"{key} steady step {s}", sample_pages=picked)
+            say(f"[fullsize] {key} steady state: step {s} ok")
     c = g.tier.read_counters()
     assert c["error_word"] == 0 and c["drops"] == 0 and c["misses"] > 0
+
+
+def test_c3_fullsize_steady_state_split():
+    """The 196k-context thrash through the bench's whole default window: the
+    first and last timed steps (8 and 107) and one between, every layer."""
+    first, last = BENCH_WARMUP, BENCH_WARMUP + BENCH_STEPS - 1
+    _steady_state_split("c3", {first, 57, last}, {first, 57, last}, last, (3, 10))
+
+
+def test_c4_fullsize_steady_state_split():
+    """The batch-4 mixed-context decode through the bench's default window
+    (the workload's 64 query steps extended as the bench extends them)."""
+    first, last = BENCH_WARMUP, BENCH_WARMUP + BENCH_STEPS - 1
+    _steady_state_split("c4", {first, last}, {first, 60, last}, last, (2, 9))
