@@ -140,11 +140,11 @@ def test_c5_fullsize_prefill():
 BENCH_WARMUP, BENCH_STEPS = 8, 100
 
 
-def _steady_state_split(key, check_layers, check_state, attn_step, attn_layers):
+def _steady_state_split(key, check_layers, check_state, attn_step, attn_layers, split=True):
     """The bench's decode window at full size, in its launch configuration:
-    steps 0..3 through decode_layer, then decode_layer_split with the copy
-    stream joined only where a step is compared (the bench joins it once,
-    after its timed steps).  Every layer of the steps in check_layers against
+    steps 0..3 through decode_layer, then (split) decode_layer_split with the
+    copy stream joined only where a step is compared (the bench joins it
+    once, after its timed steps), else decode_layer throughout.  Every layer of the steps in check_layers against
     the oracle (selections, compaction, slot maps, miss lists), LRU state,
     counters and the pool rows of sampled resident pages at check_state,
     attention on attn_layers of attn_step."""
@@ -172,7 +172,7 @@ def _steady_state_split(key, check_layers, check_state, attn_step, attn_layers):
     rng = np.random.default_rng(11)
     plain_steps = (BENCH_WARMUP + 1) // 2
     for s in range(last + 1):
-        if s < plain_steps:
+        if s < plain_steps or not split:
             g.decode_step(s)
         else:
             g.decode_step_split(s, side, join=False)
@@ -197,7 +197,15 @@ def _steady_state_split(key, check_layers, check_state, attn_step, attn_layers):
             compare_state(g, o, f"{key} steady step {s}", sample_pages=picked)
             say(f"[fullsize] {key} steady state: step {s} ok")
     c = g.tier.read_counters()
-    assert c["error_word"] == 0 and c["drops"] == 0 and c["misses"] > 0
+    assert c["error_word"] == 0 and c["drops"] == 0 and (c["misses"] > 0 or not split)
+
+
+def test_c2_fullsize_steady_state():
+    """The every-page-resident 64k decode through the bench's default window,
+    all of it through decode_layer (the path the bench takes when the warmup
+    misses nothing; the fetch folded into the attention launch)."""
+    first, last = BENCH_WARMUP, BENCH_WARMUP + BENCH_STEPS - 1
+    _steady_state_split("c2", {first, last}, {first, last}, last, (0, 11), split=False)
 
 
 def test_c3_fullsize_steady_state_split():
