@@ -135,6 +135,50 @@ def test_c5_fullsize_prefill():
     compare_state(g, o, "c5 after the chunk", sample_pages=new_pages[:3] + new_pages[-2:])
 
 
+def test_c5_fullsize_cold_chunk():
+    """The chunk from an empty pool, as the bench's cold chunk runs it: the
+    context written, residency reset, then the chunk -- layer 0's ensure
+    misses every cached page its rows select and one fetch moves their rows
+    (every layer).  Selections, slot maps and misses of every layer, the
+    attention of sampled rows on every layer, LRU state, counters and the
+    pool rows of sampled fetched pages."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c5")
+    say(f"[fullsize] c5 cold chunk: {wl.description}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.tier.reset_residency()
+    torch.cuda.synchronize()
+    got = []
+
+    def on_layer(layer, bufs):
+        got.append({k: bufs[k].clone() for k in ("sel", "needed", "out_slots", "miss", "miss_count", "out")})
+
+    g.prefill(on_layer=on_layer, copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    say("[fullsize] c5 cold chunk: gpu chunk done")
+    o = run.make_tier(wl, materialize=False)
+    run.setup(wl, o)
+    o.reset_residency()
+    rng = np.random.default_rng(9)
+    rows = sorted({0, 63, 64, 2047, 4095} | set(int(x) for x in rng.choice(wl.prefill_tokens, 11, replace=False)))
+    recs = run.prefill(wl, o, attention_rows=rows)
+    for layer, (gg, rec) in enumerate(zip(got, recs)):
+        where = f"c5 cold layer {layer}"
+        assert np.array_equal(gg["sel"].cpu().numpy(), rec["sel"]), f"{where}: sel"
+        assert np.array_equal(gg["needed"].cpu().numpy(), rec["needed"]), f"{where}: needed"
+        assert np.array_equal(gg["out_slots"].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+        m = int(gg["miss_count"].item())
+        assert np.array_equal(gg["miss"].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+        out = bf16_to_f64(gg["out"][rows])
+        ref = np.stack([rec["out"][r] for r in rows])
+        assert_close(out, ref, f"{where}: attention")
+    misses0 = recs[0]["misses"]
+    assert len(misses0) > 900, len(misses0)            # layer 0 fetches the cached pages it selects
+    picked = sorted(int(misses0[i][1]) for i in rng.choice(len(misses0), 4, replace=False))
+    compare_state(g, o, "c5 cold chunk", sample_pages=picked)
+
+
 # bench.py's default decode run: 8 untimed steps (the first half through
 # decode_layer, then the split path it chose), 100 timed steps
 BENCH_WARMUP, BENCH_STEPS = 8, 100
