@@ -995,7 +995,8 @@ def bench_cold_step(torch, g, s0, reps):
     b = float(np.mean([r[2] for r in rec]))
     return {"ms_per_step": round(ms, 4), "misses_per_step": round(float(np.mean([r[1] for r in rec])), 1),
             "bytes_per_step": round(b),
-            "roofline": {"kernel": "k_fetch (each layer's whole-row copy of its misses), over the step",
+            "roofline": {"kernel": "each layer's whole-row copy of its misses (folded into the k_attn_mfma_split "
+                                   "launch), over the step",
                          "bound": "host_link", "achieved": round(b / (ms * 1e-3) / 1e9, 2),
                          "peak": LINK_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(b / (ms * 1e-3) / 1e9 / LINK_PEAK_GBPS, 4), "traffic": None},

@@ -179,6 +179,49 @@ def test_c5_fullsize_cold_chunk():
     compare_state(g, o, "c5 cold chunk", sample_pages=picked)
 
 
+def test_c3_fullsize_cold_steps():
+    """The bench's cold step: residency reset, then one decode step through
+    decode_layer (every selected page misses: the fetch folded into the
+    attention launch moves ~360 whole rows), twice.  Every layer against the
+    oracle, LRU state, counters and the pool rows of sampled fetched pages."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c3")
+    say(f"[fullsize] c3 cold steps: {wl.description}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    o = run.make_tier(wl, materialize=False)
+    run.setup(wl, o)
+    q = gen.decode_queries(wl)
+    bt, npg = gen.block_tables(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    rng = np.random.default_rng(13)
+    for s in (0, 1):
+        g.tier.reset_residency()
+        o.reset_residency()
+        g.decode_step(s)
+        torch.cuda.synchronize()
+        fetched = []
+        for layer in range(wl.num_layers):
+            where = f"c3 cold step {s} layer {layer}"
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias,
+                                 with_attention=layer in (0, 7))
+            assert np.array_equal(g.sel[layer].cpu().numpy(), rec["sel"]), f"{where}: sel"
+            assert np.array_equal(g.out_slots[layer].cpu().numpy(), rec["out_slots"]), f"{where}: out_slots"
+            m = int(g.miss_count[layer].item())
+            assert np.array_equal(g.miss[layer].cpu().numpy()[:m], rec["misses"]), f"{where}: misses"
+            if layer in (0, 7):
+                assert_close(bf16_to_f64(g.out[layer]), rec["out"], f"{where}: attention")
+            fetched += [int(p) for _, p in rec["misses"]]
+        assert len(fetched) > 300, len(fetched)
+        picked = sorted(int(fetched[i]) for i in rng.choice(len(fetched), 4, replace=False))
+        compare_state(g, o, f"c3 cold step {s}", sample_pages=picked)
+        say(f"[fullsize] c3 cold step {s} ok ({len(fetched)} misses)")
+
+
 # bench.py's default decode run: 8 untimed steps (the first half through
 # decode_layer, then the split path it chose), 100 timed steps
 BENCH_WARMUP, BENCH_STEPS = 8, 100
