@@ -303,7 +303,8 @@ def test_c3_fullsize_steady_state_split():
 
 
 def test_c4_fullsize_steady_state_split():
-    """The batch-4 mixed-context decode through the bench's default window
-    (the workload's 64 query steps extended as the bench extends them)."""
-    first, last = BENCH_WARMUP, BENCH_WARMUP + BENCH_STEPS - 1
-    _steady_state_split("c4", {first, last}, {first, 60, last}, last, (2, 9))
+    """The batch-4 mixed-context decode into the bench's default window: its
+    first 21 timed steps (the oracle takes a few seconds per step here, so
+    the whole window would hold the test for minutes)."""
+    first, last = BENCH_WARMUP, BENCH_WARMUP + 20
+    _steady_state_split("c4", {first, last}, {first, last}, last, (2, 9))
