@@ -15,7 +15,10 @@
   flags, capacity overruns) through both ensure paths: widths up to 512 on
   pools up to 2,048 slots (state reads up front, first occurrences from an
   LDS hash table) and wider calls or larger pools (global first-occurrence
-  marks).
+  marks);
+* requests sharing physical pages (a shared prefix) from an empty pool: a
+  page both select is one fetch, read by both rows in the step that fetches
+  it.
 """
 from dataclasses import replace
 
@@ -322,3 +325,50 @@ def test_corrupted_mirror_byte_is_caught_after_refetch():
     t.fetch_pages(i32([[slot, page]]), i32([1]))
     o.fetch(np.array([[slot, page]]))
     compare_state(g, o, "after the restore")
+
+
+def test_shared_prefix_pages_fetched_once_and_read_by_both_requests():
+    """Two requests whose block tables share physical pages (request 1's first
+    logical pages are request 0's pages: a shared prefix).  After a residency
+    reset every selected page misses: a page both requests select is fetched
+    once (its second needed entry is a duplicate, which takes the first
+    occurrence's slot and fetch flag) and both rows read it in the step that
+    fetches it -- through decode_layer, whose fetch rides in the attention
+    launch (the missed pages' block of the layer read from the mirror and
+    written back by every row that selected them), and through the split
+    decode.  Against the oracle with the same block table."""
+    from workload.gpu_run import GpuWorkload
+    wl = get_workload("c4s")
+    say(f"[edges] shared prefix pages on {wl.name}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    bt, npg = gen.block_tables(wl)
+    shared = int(npg[0])
+    bt2 = bt.copy()
+    bt2[1, :shared] = bt[0, :shared]
+    g.bt = torch.from_numpy(np.ascontiguousarray(bt2, dtype=np.int32)).cuda()
+    q = gen.decode_queries(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    side = torch.cuda.Stream()
+    dups = 0
+    for s in range(wl.steps):
+        g.tier.reset_residency()
+        o.reset_residency()
+        if s % 2 == 0:
+            g.decode_step(s)
+        else:
+            g.decode_step_split(s, side)
+        torch.cuda.synchronize()
+        for layer in range(wl.num_layers):
+            rec = o.decode_layer(layer, q[s, layer], rs, bt2, npg, ctx, wl.topk, bias=bias)
+            compare_layer(g, rec, layer, f"shared prefix step {s} layer {layer}")
+            need = rec["needed"]
+            dups += len((set(need[0].tolist()) & set(need[1].tolist())) - {-1})
+        compare_state(g, o, f"shared prefix step {s}")
+    assert dups > 0, "no page was selected by both requests"
