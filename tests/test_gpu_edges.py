@@ -18,7 +18,9 @@
   marks);
 * requests sharing physical pages (a shared prefix) from an empty pool: a
   page both select is one fetch, read by both rows in the step that fetches
-  it.
+  it;
+* a decode layer whose ensure takes the global path (a pool above 2,048
+  slots), from an empty pool.
 """
 from dataclasses import replace
 
@@ -372,3 +374,37 @@ def test_shared_prefix_pages_fetched_once_and_read_by_both_requests():
             dups += len((set(need[0].tolist()) & set(need[1].tolist())) - {-1})
         compare_state(g, o, f"shared prefix step {s}")
     assert dups > 0, "no page was selected by both requests"
+
+
+def test_decode_through_the_global_ensure_path_from_an_empty_pool():
+    """A pool of 2,300 slots (above the LDS ensure's 2,048) sends the decode
+    layer's ensure down the global first-occurrence path, which also writes
+    the per-entry fetch flags the folded fetch reads: from an empty pool every
+    selected page misses and is read from its mirror row by the attention
+    that fetches it.  Against the oracle, state and pool rows included."""
+    from workload.gpu_run import GpuWorkload
+    wl = replace(get_workload("c2s"), name="edge_global_ensure", num_slots=2300, steps=3)
+    say(f"[edges] global ensure path on {wl.name}")
+    g = GpuWorkload(wl)
+    g.setup()
+    g.upload_queries()
+    o = run.make_tier(wl, materialize=True)
+    run.setup(wl, o)
+    bt, npg = gen.block_tables(wl)
+    q = gen.decode_queries(wl)
+    ctx = gen.context_lengths(wl)
+    bias = gen.page_bias(wl)
+    rs = np.arange(wl.batch + 1)
+    o.set_select_width(wl.batch, wl.topk, wl.max_sel_pages)
+    for s in range(wl.steps):
+        if s == 0:
+            g.tier.reset_residency()
+            o.reset_residency()
+        g.decode_step(s)
+        torch.cuda.synchronize()
+        for layer in range(wl.num_layers):
+            rec = o.decode_layer(layer, q[s, layer], rs, bt, npg, ctx, wl.topk, bias=bias)
+            compare_layer(g, rec, layer, f"global ensure step {s} layer {layer}")
+            if s == 0 and layer == 0:                 # (later layers hit the rows layer 0 fetched)
+                assert len(rec["misses"]) == wl.topk, len(rec["misses"])
+        compare_state(g, o, f"global ensure step {s}")
